@@ -1,0 +1,289 @@
+"""ctypes binding of the C ABI in ``include/dg.h``.
+
+Argument marshalling only: torch tensors supply device memory and the
+stream; every step of the pass runs in the HIP library.  The library must
+have been built (``python -m canvas_denoising_moe_amd.build``); loading fails
+loudly otherwise -- there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_char_p, c_float, c_int32, c_uint64, c_void_p
+from typing import Optional, Sequence
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libdg.so")
+
+DG_OK, DG_EINVAL, DG_ENOMEM, DG_EHIP, DG_ESTATE, DG_EUNSUPPORTED = 0, -1, -2, -3, -4, -5
+DG_F32, DG_BF16 = 0, 1
+STATUS_NAMES = {0: "DG_OK", -1: "DG_EINVAL", -2: "DG_ENOMEM", -3: "DG_EHIP", -4: "DG_ESTATE",
+                -5: "DG_EUNSUPPORTED"}
+
+
+class DGConfig(ctypes.Structure):
+    _fields_ = [
+        ("n_layers", c_int32), ("hidden", c_int32), ("n_heads", c_int32), ("n_kv_heads", c_int32),
+        ("head_dim", c_int32), ("n_experts", c_int32), ("top_k", c_int32), ("n_shared", c_int32),
+        ("expert_ffn", c_int32), ("vocab", c_int32), ("canvas_len", c_int32), ("window", c_int32),
+        ("max_batch", c_int32), ("max_prompt_len", c_int32), ("global_layer_mask", c_uint64),
+        ("rope_theta", c_float), ("prope_frac", c_float), ("rms_eps", c_float), ("dtype", c_int32),
+        ("has_lm_head", c_int32), ("post_ffn_norm", c_int32),
+    ]
+
+
+LAYER_FIELDS = ("wq", "wk", "wv", "wo", "router", "w_gate", "w_up", "w_down", "sh_gate", "sh_up",
+                "sh_down", "norm_in", "norm_pa", "norm_pf", "norm_pf2")
+
+
+class DGLayerWeights(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in LAYER_FIELDS]
+
+
+class DGError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+_SIGS = {
+    "dg_create": (c_int32, [POINTER(DGConfig), c_int32, c_void_p, POINTER(c_void_p)]),
+    "dg_destroy": (c_int32, [c_void_p]),
+    "dg_last_error": (c_char_p, [c_void_p]),
+    "dg_set_layer_weights": (c_int32, [c_void_p, c_int32, POINTER(DGLayerWeights)]),
+    "dg_set_embedding": (c_int32, [c_void_p, c_void_p, c_void_p]),
+    "dg_init_weights": (c_int32, [c_void_p, c_void_p, c_void_p, POINTER(DGLayerWeights)]),
+    "dg_load_prompt_kv": (c_int32, [c_void_p, c_int32, c_int32, POINTER(c_void_p), POINTER(c_void_p)]),
+    "dg_denoise_step": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, POINTER(c_int32), c_void_p, c_void_p]),
+    "dg_generate_block": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
+    "dg_forward_hidden": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p]),
+    "dg_set_trace": (c_int32, [c_void_p, c_void_p]),
+    "dg_k_argmax_conf": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
+    "dg_k_lock_select": (c_int32, [c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                   POINTER(c_int32), c_void_p]),
+    "dg_k_moe_route": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
+                                 c_void_p, c_void_p, c_void_p]),
+    "dg_k_qkv": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "dg_k_canvas_attn": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                   c_int32]),
+    "dg_k_moe_ffn": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "dg_k_lm_head": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p]),
+}
+
+
+def lib():
+    """Load ``libdg.so`` (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library {LIB_PATH} is missing; build it with "
+                               "`python -m canvas_denoising_moe_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def exported_symbols() -> Sequence[str]:
+    return tuple(_SIGS)
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _ptr(t, dtype=None, name="tensor"):
+    """Device address of a contiguous CUDA(HIP) tensor (None -> NULL)."""
+    if t is None:
+        return None
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    return c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, ctx_handle=None):
+    if status != DG_OK:
+        msg = lib().dg_last_error(ctx_handle)
+        raise DGError(status, msg.decode() if msg else "")
+
+
+def make_config(model, max_batch: int, max_prompt_len: int) -> DGConfig:
+    """dg_config from any object with the architecture fields (e.g. a
+    ``ModelConfig``)."""
+    c = DGConfig()
+    for f in ("n_layers", "hidden", "n_heads", "n_kv_heads", "head_dim", "n_experts", "top_k",
+              "n_shared", "expert_ffn", "vocab", "canvas_len", "window"):
+        setattr(c, f, int(getattr(model, f)))
+    c.max_batch = int(max_batch)
+    c.max_prompt_len = int(max_prompt_len)
+    c.global_layer_mask = int(model.global_layer_mask)
+    c.rope_theta = float(model.rope_theta)
+    c.prope_frac = float(model.prope_frac)
+    c.rms_eps = float(model.rms_eps)
+    c.dtype = DG_BF16 if model.dtype == "bf16" else DG_F32
+    c.has_lm_head = int(bool(model.has_lm_head))
+    c.post_ffn_norm = int(bool(model.post_ffn_norm))
+    return c
+
+
+def _wdtype(model):
+    import torch
+    return torch.bfloat16 if model.dtype == "bf16" else torch.float32
+
+
+class Context:
+    """One library context (``dg_ctx``) on one device and stream."""
+
+    def __init__(self, model, max_batch: int = 1, max_prompt_len: int = 0, device: int = 0,
+                 stream=None):
+        import torch
+        self.model = model
+        self.max_batch = max_batch
+        self.device = torch.device("cuda", device)
+        self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
+        self.wdtype = _wdtype(model)
+        cfg = make_config(model, max_batch, max_prompt_len)
+        h = c_void_p()
+        _check(lib().dg_create(ctypes.byref(cfg), device, _stream(self.stream), ctypes.byref(h)), None)
+        self._h = h
+        self._keep = []
+
+    # -- lifetime ------------------------------------------------------------
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().dg_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    @property
+    def handle(self):
+        return self._h
+
+    def _c(self, status):
+        _check(status, self._h)
+
+    # -- weights and prompt ----------------------------------------------------
+    def set_layer_weights(self, layer: int, w: dict):
+        lw = DGLayerWeights()
+        for n in LAYER_FIELDS:
+            setattr(lw, n, _ptr(w[n], self.wdtype, n))
+        self._c(lib().dg_set_layer_weights(self._h, layer, ctypes.byref(lw)))
+
+    def set_embedding(self, embed, norm_final):
+        self._c(lib().dg_set_embedding(self._h, _ptr(embed, self.wdtype, "embed"),
+                                       _ptr(norm_final, self.wdtype, "norm_final")))
+
+    def init_weights(self, embed, norm_final, layers: Sequence[dict]):
+        arr = (DGLayerWeights * len(layers))()
+        for i, w in enumerate(layers):
+            for n in LAYER_FIELDS:
+                setattr(arr[i], n, _ptr(w[n], self.wdtype, n))
+        self._c(lib().dg_init_weights(self._h, _ptr(embed, self.wdtype, "embed"),
+                                      _ptr(norm_final, self.wdtype, "norm_final"), arr))
+
+    def load_prompt_kv(self, slot: int, prompt_len: int, ks: Sequence, vs: Sequence):
+        n = len(ks)
+        karr = (c_void_p * n)(*[_ptr(k, self.wdtype, "k") if k is not None and k.numel() else None for k in ks])
+        varr = (c_void_p * n)(*[_ptr(v, self.wdtype, "v") if v is not None and v.numel() else None for v in vs])
+        self._c(lib().dg_load_prompt_kv(self._h, slot, prompt_len, karr, varr))
+
+    # -- the pass --------------------------------------------------------------
+    def denoise_step(self, tokens, locked, steps_left: Sequence[int], conf=None, pred=None):
+        import torch
+        B = tokens.shape[0]
+        sl = (c_int32 * B)(*[int(s) for s in steps_left])
+        self._c(lib().dg_denoise_step(self._h, B, _ptr(tokens, torch.int32, "tokens"),
+                                      _ptr(locked, torch.uint8, "locked"), sl,
+                                      _ptr(conf, torch.float32, "conf"), _ptr(pred, torch.int32, "pred")))
+
+    def generate_block(self, tokens, locked, n_steps: int):
+        import torch
+        self._c(lib().dg_generate_block(self._h, tokens.shape[0], n_steps, _ptr(tokens, torch.int32, "tokens"),
+                                        _ptr(locked, torch.uint8, "locked")))
+
+    def forward_hidden(self, x_in, x_out):
+        import torch
+        B = x_in.shape[0] // self.model.canvas_len
+        self._c(lib().dg_forward_hidden(self._h, B, _ptr(x_in, torch.float32, "x_in"),
+                                        _ptr(x_out, torch.float32, "x_out")))
+
+    def set_trace(self, route_idx=None):
+        import torch
+        self._keep = [route_idx]
+        self._c(lib().dg_set_trace(self._h, _ptr(route_idx, torch.int32, "route_idx")))
+
+    # -- single kernels ----------------------------------------------------------
+    def k_qkv(self, layer: int, batch: int, a, q, k, v):
+        self._c(lib().dg_k_qkv(self._h, layer, batch, _ptr(a, self.wdtype, "a"), _ptr(q, self.wdtype, "q"),
+                               _ptr(k, self.wdtype, "k"), _ptr(v, self.wdtype, "v")))
+
+    def k_canvas_attn(self, layer: int, batch: int, q, k, v, o, canvas_keys: bool = True):
+        self._c(lib().dg_k_canvas_attn(self._h, layer, batch, _ptr(q, self.wdtype, "q"),
+                                       _ptr(k, self.wdtype, "k"), _ptr(v, self.wdtype, "v"),
+                                       _ptr(o, self.wdtype, "o"), int(bool(canvas_keys))))
+
+    def k_moe_ffn(self, layer: int, batch: int, f, idx, gates, m):
+        import torch
+        self._c(lib().dg_k_moe_ffn(self._h, layer, batch, _ptr(f, self.wdtype, "f"),
+                                   _ptr(idx, torch.int32, "idx"), _ptr(gates, torch.float32, "gates"),
+                                   _ptr(m, torch.float32, "m")))
+
+    def k_lm_head(self, batch: int, h, logits):
+        import torch
+        self._c(lib().dg_k_lm_head(self._h, batch, _ptr(h, self.wdtype, "h"),
+                                   _ptr(logits, torch.float32, "logits")))
+
+
+def k_argmax_conf(logits, pred, conf, stream=None):
+    import torch
+    rows, V = logits.shape
+    _check(lib().dg_k_argmax_conf(_ptr(logits, torch.float32, "logits"), rows, V,
+                                  _ptr(pred, torch.int32, "pred"), _ptr(conf, torch.float32, "conf"),
+                                  _stream(stream)))
+
+
+def k_lock_select(conf, pred, tokens, locked, steps_left: Sequence[int], stream=None):
+    import torch
+    B, N = tokens.shape
+    sl = (c_int32 * max(1, B))(*[int(s) for s in steps_left])
+    _check(lib().dg_k_lock_select(B, N, _ptr(conf, torch.float32, "conf"), _ptr(pred, torch.int32, "pred"),
+                                  _ptr(tokens, torch.int32, "tokens"), _ptr(locked, torch.uint8, "locked"),
+                                  sl, _stream(stream)))
+
+
+def k_moe_route(logits, top_k: int, idx, gates, counts=None, offsets=None, perm=None, stream=None):
+    import torch
+    rows, E = logits.shape
+    _check(lib().dg_k_moe_route(_ptr(logits, torch.float32, "logits"), rows, E, top_k,
+                                _ptr(idx, torch.int32, "idx"), _ptr(gates, torch.float32, "gates"),
+                                _ptr(counts, torch.int32, "counts"), _ptr(offsets, torch.int32, "offsets"),
+                                _ptr(perm, torch.int32, "perm"), _stream(stream)))

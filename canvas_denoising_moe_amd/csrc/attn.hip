@@ -1,0 +1,365 @@
+// canvas_attn: every canvas query attends, in one softmax, to the cached
+// prompt keys visible to its layer and to every canvas key -- bidirectional,
+// no causal mask ([4xFaster] "DiffusionGemma's Technical Architecture"; GQA
+// and the local/global split: [HandsOn] "Detailed Specs").
+//
+// bf16 path (k_attn_mfma): flash-style with 16x16x32 bf16 MFMAs.
+//   * Work unit = (canvas b, KV head g, key split s) x q-tile of 64 query rows.
+//     The query rows of a KV head are its Hq/Hkv query heads x N canvas
+//     positions, so one K/V tile read from LDS feeds every query head sharing
+//     it.  Long prompts are cut into splits of CL keys (a multiple of 64) so
+//     the grid fills the chip; partial (O, m, l) are merged by k_attn_merge in
+//     a fixed order.
+//   * The q-tiles of one (b, g, s) are mapped to one XCD (blocks go
+//     round-robin over the 8 XCDs), so their shared K/V chunk is fetched from
+//     HBM once and re-read from that XCD's L2.
+//   * Scores are computed transposed, S^T = K Q^T, so each lane ends up holding
+//     4+4 keys of one query: exactly the B operand of the P V product
+//     (O^T = V^T P^T) once k indices of A and B are matched.  No cross-lane
+//     shuffle of P is needed; V is kept transposed (V^T) in HBM and LDS.
+//   * Online softmax in base 2 with fp32 state; P is rounded to bf16 for the
+//     MFMA and the normaliser sums the rounded values, so a single key gives
+//     weight exactly 1.
+// fp32 path and odd head sizes (k_attn_simple): one workgroup per query row,
+// keys in chunks of 256 with the same online-softmax recurrence.
+#include "common.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int D>
+__global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int S, int CL, int QT, int xcd_map) {
+  constexpr int KT = 64;            // keys per tile
+  constexpr int KLD = D + 8;        // padded LDS row of K (elements)
+  constexpr int VLD = KT + 8;       // padded LDS row of V^T
+  constexpr int KVEC = KT * D / 8 / 256;  // 16-byte vectors per thread for a K tile
+  constexpr int VVEC = D * KT / 8 / 256;  // same for V^T
+  __shared__ __align__(16) bf16_t Ks[KT * KLD];
+  __shared__ __align__(16) bf16_t Vs[D * VLD];
+
+  int bid = blockIdx.x, unit, qt;
+  if (xcd_map) {
+    const int xcd = bid & 7, slot = bid >> 3;
+    unit = (slot / QT) * 8 + xcd;
+    qt = slot % QT;
+  } else {
+    unit = bid / QT;
+    qt = bid % QT;
+  }
+  const int s = unit % S, bg = unit / S;
+  const int g = bg % a.Hkv, b = bg / a.Hkv;
+  const int group = a.Hq / a.Hkv;
+  const int N = a.N;
+  const int Lw = a.lw[b];
+  const int total = Lw + (a.canvas_keys ? N : 0);
+  const int k0 = s * CL, k1 = min(total, k0 + CL);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lg = lane >> 4, lc = lane & 15;
+  const int grows = group * N;
+  const int qrow = qt * 64 + wave * 16 + lc;
+  const bool qvalid = qrow < grows;
+  const int qh = g * group + (qvalid ? qrow / N : 0);
+  const int qi = qvalid ? qrow % N : 0;
+  const long long row_g = ((long long)b * a.Hq + qh) * N + qi;  // global query row
+
+  const bf16_t* kp = reinterpret_cast<const bf16_t*>(a.kp[b]) + (long long)g * Lw * D;
+  const bf16_t* vp = reinterpret_cast<const bf16_t*>(a.vp[b]) + (long long)g * D * Lw;
+  const bf16_t* kc = reinterpret_cast<const bf16_t*>(a.kc) + ((long long)b * a.Hkv + g) * N * D;
+  const bf16_t* vc = reinterpret_cast<const bf16_t*>(a.vc) + ((long long)b * a.Hkv + g) * D * N;
+
+  // Q^T fragments (B operand of S^T = K Q^T)
+  uint4 qf[D / 32];
+  {
+    const bf16_t* qp = reinterpret_cast<const bf16_t*>(a.q) + row_g * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+      qf[ks] = qvalid ? *reinterpret_cast<const uint4*>(qp + ks * 32 + lg * 8) : make_uint4(0, 0, 0, 0);
+  }
+
+  floatx4 oacc[D / 16];
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) oacc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sc = kLog2e / sqrtf((float)D);
+
+  uint4 kreg[KVEC], vreg[VVEC];
+  auto load_tile = [&](int t0) {
+#pragma unroll
+    for (int it = 0; it < KVEC; ++it) {
+      const int v = tid + it * 256;
+      const int row = v / (D / 8), c8 = v % (D / 8);
+      const int key = t0 + row;
+      uint4 val = make_uint4(0, 0, 0, 0);
+      if (key < k1) {
+        const bf16_t* src = key < Lw ? kp + (long long)key * D : kc + (long long)(key - Lw) * D;
+        val = *reinterpret_cast<const uint4*>(src + c8 * 8);
+      }
+      kreg[it] = val;
+    }
+#pragma unroll
+    for (int it = 0; it < VVEC; ++it) {
+      const int v = tid + it * 256;
+      const int d = v / (KT / 8), c8 = v % (KT / 8);
+      const int key = t0 + c8 * 8;
+      uint4 val = make_uint4(0, 0, 0, 0);
+      const bool in_p = key + 8 <= Lw && (Lw & 7) == 0;
+      const bool in_c = key >= Lw && ((key - Lw) & 7) == 0 && (N & 7) == 0;
+      if (key + 8 <= k1 && (in_p || in_c)) {
+        const bf16_t* src = in_p ? vp + (long long)d * Lw + key : vc + (long long)d * N + (key - Lw);
+        val = *reinterpret_cast<const uint4*>(src);
+      } else {
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int kk = key + j;
+          uint32_t x = 0;
+          if (kk < k1) x = kk < Lw ? vp[(long long)d * Lw + kk] : vc[(long long)d * N + (kk - Lw)];
+          w[j >> 1] |= x << ((j & 1) * 16);
+        }
+        val = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+      vreg[it] = val;
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int it = 0; it < KVEC; ++it) {
+      const int v = tid + it * 256;
+      const int row = v / (D / 8), c8 = v % (D / 8);
+      *reinterpret_cast<uint4*>(&Ks[row * KLD + c8 * 8]) = kreg[it];
+    }
+#pragma unroll
+    for (int it = 0; it < VVEC; ++it) {
+      const int v = tid + it * 256;
+      const int d = v / (KT / 8), c8 = v % (KT / 8);
+      *reinterpret_cast<uint4*>(&Vs[d * VLD + c8 * 8]) = vreg[it];
+    }
+  };
+
+  if (k0 < k1) load_tile(k0);
+  for (int t0 = k0; t0 < k1; t0 += KT) {
+    store_tile();
+    __syncthreads();
+    if (t0 + KT < k1) load_tile(t0 + KT);
+
+    // S^T for 4 blocks of 16 keys: sacc[kb][r] = score(key t0+kb*16+lg*4+r, query lc)
+    floatx4 sacc[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      sacc[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        const uint4 kf = *reinterpret_cast<const uint4*>(&Ks[(kb * 16 + lc) * KLD + ks * 32 + lg * 8]);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, kf),
+                                                            __builtin_bit_cast(bf16x8_v, qf[ks]),
+                                                            sacc[kb], 0, 0, 0);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = t0 + kb * 16 + lg * 4 + r;
+        const float sv = key < k1 ? sacc[kb][r] * sc : -INFINITY;
+        sacc[kb][r] = sv;
+        mx = fmaxf(mx, sv);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const bool none = m_new == -INFINITY;
+    const float alpha = none ? 1.f : exp2f(m_run - m_new);
+    const float mref = none ? 0.f : m_new;
+    // P^T fragments: slot j<4 -> key 32*ks2 + 4*lg + j, slot j>=4 -> key 32*ks2 + 16 + 4*lg + j-4
+    uint32_t pk[2][4];
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bf16_t p = f2bf(exp2f(sacc[kb][r] - mref));
+        ls += bf2f(p);
+        const int j = (kb & 1) * 4 + r;
+        if (j & 1)
+          pk[kb >> 1][j >> 1] |= ((uint32_t)p) << 16;
+        else
+          pk[kb >> 1][j >> 1] = p;
+      }
+    ls += __shfl_xor(ls, 16, 64);
+    ls += __shfl_xor(ls, 32, 64);
+    l_run = l_run * alpha + ls;
+    m_run = m_new;
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) oacc[i] *= alpha;
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      const uint4 pf = make_uint4(pk[ks2][0], pk[ks2][1], pk[ks2][2], pk[ks2][3]);
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const bf16_t* vrow = &Vs[(db * 16 + lc) * VLD + ks2 * 32 + lg * 4];
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+        const uint4 vf = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, vf),
+                                                            __builtin_bit_cast(bf16x8_v, pf),
+                                                            oacc[db], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  if (qvalid) {
+    const long long rows_all = (long long)a.B * a.Hq * N;
+    const long long pr = (long long)s * rows_all + row_g;
+    float* po = a.part_o + pr * D;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+      *reinterpret_cast<float4*>(po + db * 16 + lg * 4) =
+          make_float4(oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]);
+    if (lg == 0) {
+      a.part_m[pr] = m_run;
+      a.part_l[pr] = l_run;
+    }
+  }
+}
+
+// o[(b*N + i), h*D + d] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, splits in order
+template <typename T>
+__global__ void k_attn_merge(AttnArgs a, int S) {
+  const long long rows_all = (long long)a.B * a.Hq * a.N;
+  const long long row = blockIdx.x;
+  const int d = threadIdx.x;
+  if (d >= a.D) return;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, a.part_m[s * rows_all + row]);
+  float num = 0.f, den = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < S; ++s) {
+      const float w = exp2f(a.part_m[s * rows_all + row] - M);
+      num += w * a.part_o[(s * rows_all + row) * a.D + d];
+      den += w * a.part_l[s * rows_all + row];
+    }
+  }
+  const int i = (int)(row % a.N);
+  const long long bh = row / a.N;
+  const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
+  T* o = reinterpret_cast<T*>(a.o);
+  o[((long long)b * a.N + i) * a.Hq * a.D + (long long)h * a.D + d] = from_f<T>(den > 0.f ? num / den : 0.f);
+}
+
+// One query row per workgroup; generic in T and D (<= 256).
+template <typename T>
+__global__ __launch_bounds__(256) void k_attn_simple(AttnArgs a) {
+  __shared__ float qs[256];
+  __shared__ float ps[256];
+  __shared__ float red[8];
+  const long long row = blockIdx.x;  // (b*Hq + h)*N + i
+  const int N = a.N, D = a.D;
+  const int i = (int)(row % N);
+  const long long bh = row / N;
+  const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
+  const int g = h / (a.Hq / a.Hkv);
+  const int Lw = a.lw[b];
+  const int total = Lw + (a.canvas_keys ? N : 0);
+  const int tid = threadIdx.x;
+  const T* q = reinterpret_cast<const T*>(a.q) + row * D;
+  const T* kp = reinterpret_cast<const T*>(a.kp[b]) + (long long)g * Lw * D;
+  const T* vp = reinterpret_cast<const T*>(a.vp[b]) + (long long)g * D * Lw;
+  const T* kc = reinterpret_cast<const T*>(a.kc) + ((long long)b * a.Hkv + g) * N * D;
+  const T* vc = reinterpret_cast<const T*>(a.vc) + ((long long)b * a.Hkv + g) * D * N;
+  if (tid < D) qs[tid] = to_f<T>(q[tid]);
+  __syncthreads();
+  const float scale = 1.0f / sqrtf((float)D);
+  float m = -INFINITY, l = 0.f, o = 0.f;
+  for (int c0 = 0; c0 < total; c0 += 256) {
+    const int key = c0 + tid;
+    float sv = -INFINITY;
+    if (key < total) {
+      const T* kr = key < Lw ? kp + (long long)key * D : kc + (long long)(key - Lw) * D;
+      float acc = 0.f;
+      for (int d = 0; d < D; ++d) acc += qs[d] * to_f<T>(kr[d]);
+      sv = acc * scale;
+    }
+    // block max
+    float mx = wave_max(sv);
+    __syncthreads();
+    if ((tid & 63) == 0) red[tid >> 6] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float m_new = fmaxf(m, mx);
+    const float alpha = m == -INFINITY ? 0.f : expf(m - m_new);
+    const float p = key < total ? expf(sv - m_new) : 0.f;
+    ps[tid] = p;
+    const float psum = block_sum(p, red + 4);
+    l = l * alpha + psum;
+    m = m_new;
+    __syncthreads();
+    if (tid < D) {
+      float acc = 0.f;
+      const int nk = min(256, total - c0);
+      for (int j = 0; j < nk; ++j) {
+        const int kk = c0 + j;
+        const float vv = kk < Lw ? to_f<T>(vp[(long long)tid * Lw + kk]) : to_f<T>(vc[(long long)tid * N + (kk - Lw)]);
+        acc += ps[j] * vv;
+      }
+      o = o * alpha + acc;
+    }
+    __syncthreads();
+  }
+  if (tid < D) {
+    T* out = reinterpret_cast<T*>(a.o);
+    out[((long long)b * N + i) * a.Hq * D + (long long)h * D + tid] = from_f<T>(l > 0.f ? o / l : 0.f);
+  }
+}
+
+}  // namespace
+
+// Split count and length: aim for ~1024 workgroups; splits are whole 64-key tiles.
+static void choose_splits(const AttnArgs& a, int QT, int* S_out, int* CL_out) {
+  int maxtot = 0;
+  for (int b = 0; b < a.B; ++b) maxtot = max(maxtot, a.lw[b] + (a.canvas_keys ? a.N : 0));
+  const long long base = (long long)a.B * a.Hkv * QT;
+  int S = (int)((1024 + base - 1) / base);
+  const int tiles = (maxtot + 63) / 64;
+  if (S > tiles) S = tiles;
+  if (S < 1) S = 1;
+  const long long rows_all = (long long)a.B * a.Hq * a.N;
+  while (S > 1 && (long long)S * rows_all > a.part_cap_rows) --S;
+  int CL = ((maxtot + S - 1) / S + 63) / 64 * 64;
+  if (CL < 64) CL = 64;
+  S = (maxtot + CL - 1) / CL;
+  if (S < 1) S = 1;
+  *S_out = S;
+  *CL_out = CL;
+}
+
+hipError_t launch_attention(int is_bf16, const AttnArgs& a, hipStream_t st) {
+  const long long rows_all = (long long)a.B * a.Hq * a.N;
+  if (rows_all == 0) return hipSuccess;
+  if (is_bf16 && (a.D == 128 || a.D == 64)) {
+    const int QT = (a.Hq / a.Hkv * a.N + 63) / 64;
+    int S, CL;
+    choose_splits(a, QT, &S, &CL);
+    if ((long long)S * rows_all > a.part_cap_rows) return hipErrorInvalidValue;
+    const long long units = (long long)a.B * a.Hkv * S;
+    const int xcd_map = (units % 8) == 0;
+    const dim3 grid((unsigned)(units * QT));
+    if (a.D == 128)
+      hipLaunchKernelGGL(k_attn_mfma<128>, grid, dim3(256), 0, st, a, S, CL, QT, xcd_map);
+    else
+      hipLaunchKernelGGL(k_attn_mfma<64>, grid, dim3(256), 0, st, a, S, CL, QT, xcd_map);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_attn_merge<bf16_t>, dim3((unsigned)rows_all), dim3(a.D), 0, st, a, S);
+    return hipGetLastError();
+  }
+  if (a.D > 256) return hipErrorInvalidValue;
+  if (is_bf16)
+    hipLaunchKernelGGL(k_attn_simple<bf16_t>, dim3((unsigned)rows_all), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_attn_simple<float>, dim3((unsigned)rows_all), dim3(256), 0, st, a);
+  return hipGetLastError();
+}

@@ -1,0 +1,145 @@
+// Shared device helpers and launcher declarations of the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;  // raw bf16 bits
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
+
+#define DG_DEV __device__ __forceinline__
+
+DG_DEV float bf2f(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// float -> bf16, round to nearest even (finite inputs)
+DG_DEV bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+template <typename T> DG_DEV float to_f(T v);
+template <> DG_DEV float to_f<float>(float v) { return v; }
+template <> DG_DEV float to_f<bf16_t>(bf16_t v) { return bf2f(v); }
+
+template <typename T> DG_DEV T from_f(float v);
+template <> DG_DEV float from_f<float>(float v) { return v; }
+template <> DG_DEV bf16_t from_f<bf16_t>(float v) { return f2bf(v); }
+
+// wave64 reductions
+DG_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+DG_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Block-wide sum in a fixed order (deterministic).  `red` holds >= nwaves floats.
+DG_DEV float block_sum(float v, float* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.f;
+  for (int i = 0; i < nw; ++i) s += red[i];
+  return s;
+}
+
+// ----------------------------------------------------------------------------
+// launchers (implemented in the .hip files); all return hipError_t
+// ----------------------------------------------------------------------------
+
+// Weight repack into matrix-core fragment order:
+//   dst[((nb*KB + kb)*64 + lane)*8 + j] = W(k = kb*32 + (lane/16)*8 + j,
+//                                           n = colmap(nb)*16 + lane%16)
+// W(k, n) = src[k*ld + n] when src_kn, else src[n*ld + k].  colmap: 0 = identity,
+// 1 = q/k/v rotary pairing (see gemm.hip), 2 = gate/up interleave with the
+// second source in src2.
+struct PackArgs {
+  const void* src; const void* src2; long long ld; int K, N; int src_kn; int colmap;
+  int head_dim, n_rope_heads;  // colmap 1
+  void* dst;
+};
+hipError_t launch_pack(int is_bf16, const PackArgs& a, hipStream_t s);
+// nbatch matrices: source i at src (and src2) + i*src_bs, destination at dst + i*dst_bs
+hipError_t launch_pack_batched(int is_bf16, const PackArgs& a, int nbatch, long long src_bs,
+                               long long dst_bs, hipStream_t s);
+
+// Generic skinny GEMM on matrix cores; see gemm.hip for the arguments.
+struct GemmArgs {
+  const void* A; long long lda;
+  const int32_t* a_rows;         // logical row -> A row, NULL = identity
+  int a_rows_max;                // rows of A (gathered indices are clamped into range)
+  const void* B; long long b_group_stride;  // elements between groups' packed matrices
+  int K, NB;                     // K % 32 == 0; NB = N / 16
+  int static_row0, static_rows, static_group;  // rows handled by a fixed m-chunk grid
+  const int32_t* group_off; int n_groups;      // data-dependent groups 0..n_groups-1
+};
+enum EpiKind { EPI_STORE_F32 = 0, EPI_GEGLU = 1, EPI_DOWN = 2, EPI_QKV = 3 };
+struct EpiArgs {
+  int kind;
+  void* out; long long ldo;            // STORE_F32 (float), GEGLU (T)
+  const int32_t* slot; const float* gates; int routed_rows; int out_rows;  // DOWN
+  // QKV: output tensors with strides (elements) over (b, head, i, d)
+  void* q; void* k; void* v;
+  long long qs[4], ks[4], vs[4];
+  const float2* rope_cs;               // [batch][N][D/2] (cos, sin)
+  int N, D, Hq, Hkv, n_rot_local, n_rot_global, is_global;
+};
+hipError_t launch_gemm(int is_bf16, const GemmArgs& g, const EpiArgs& e, int mt, hipStream_t s);
+
+// Attention.
+#define DG_MAX_BATCH 64
+struct AttnArgs {
+  const void* q;          // [B][Hq][N][D]
+  const void* kc;         // canvas K [B][Hkv][N][D]
+  const void* vc;         // canvas V^T [B][Hkv][D][N]
+  int B, N, Hq, Hkv, D, canvas_keys;
+  void* o;                // [B*N][Hq*D]
+  float* part_o; float* part_m; float* part_l;  // split partials
+  long long part_cap_rows;  // capacity of the partial buffers in (split, row) pairs
+  const void* kp[DG_MAX_BATCH];  // per canvas: prompt K [Hkv][Lw][D]
+  const void* vp[DG_MAX_BATCH];  // per canvas: prompt V^T [Hkv][D][Lw]
+  int lw[DG_MAX_BATCH];          // per canvas: prompt keys visible to the layer
+};
+hipError_t launch_attention(int is_bf16, const AttnArgs& a, hipStream_t s);
+
+// Routing, combine, norms.
+// logits != NULL: idx/gates are computed (top-k, softmax); logits == NULL: idx is
+// an input.  perm (nullable): rows*k entries t*k+s in expert-sorted order; with
+// a_rows != NULL also the shared expert's rows*k + t entries and a_rows (token of
+// every sorted row).
+hipError_t launch_moe_route(const float* logits, int rows, int E, int k, int32_t* idx, float* gates,
+                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* a_rows,
+                            hipStream_t s);
+// x[t] += delta_norm(sum of terms) ; out[t] = T(RMSNorm(x[t]) * (1 + w_out))
+// mode 0: terms = delta[t] (one row); mode 1: terms = y[t*k + s] for s < k, then y[rows*k + t];
+// mode 2: no delta (only the output norm); w_delta NULL: plain add.
+struct NormArgs {
+  int mode; int rows, H, k; float eps;
+  float* x; const float* delta; const void* w_delta; const void* w_out; void* out;
+};
+hipError_t launch_residual_norm(int is_bf16, const NormArgs& a, hipStream_t s);
+hipError_t launch_embed(int is_bf16, const int32_t* tokens, int rows, int H, int V,
+                        const void* packed_embed, float* x, hipStream_t s);
+hipError_t launch_rope_table(float2* cs, int N, int D, int prompt_len, double theta, hipStream_t s);
+
+// Head: argmax / confidence and the lock step.
+hipError_t launch_argmax_conf(const float* logits, int rows, int V, int32_t* pred, float* conf,
+                              hipStream_t s);
+struct StepsArg { int32_t v[64]; };
+hipError_t launch_lock_select(int B, int N, const float* conf, const int32_t* pred, int32_t* tokens,
+                              uint8_t* locked, StepsArg steps, hipStream_t s);
+
+// Layout helpers.
+hipError_t launch_kv_repack(int is_bf16, const void* src, int L, int Hkv, int D, void* k_dst,
+                            int transpose, hipStream_t s);
+// generic 4-d permute copy: dst[(i0,i1,i2,i3) strides ds] = src[(i0,i1,i2,i3) strides ss]
+hipError_t launch_permute4(int is_bf16, const void* src, void* dst, const int* dims,
+                           const long long* ss, const long long* ds, hipStream_t s);

@@ -1,0 +1,386 @@
+// Skinny GEMMs on CDNA4 matrix cores: y = A @ W with A row-major activations
+// (optionally row-gathered) and W pre-packed into MFMA B-fragment order.
+//
+// Every dense contraction of the pass runs here: the q/k/v projection with its
+// RoPE epilogue, the output projection, the router, the grouped expert GEMMs
+// (gate|up with the GELU-tanh gated product, down with the gate scale) and the
+// tied LM head.  The decoder's GEMMs have few rows (256 canvas positions, ~16
+// per routed expert) and are bound by streaming W from HBM, so the kernel is
+// organised around the weight stream:
+//
+//   * W is packed as [N/16][K/32][64 lanes][8] so the 16x32 B fragment of one
+//     16x16x32 bf16 MFMA is one contiguous 1 KB block: one 16-byte load per
+//     lane, fully coalesced.  Each weight element is read exactly once per
+//     m-chunk.
+//   * A workgroup owns 4 waves x WN n-blocks of output columns and up to MT
+//     m-tiles of 16 rows; the rows' A chunk (128 of K) is staged once in LDS and
+//     shared by the 4 waves, while every wave streams its own W fragments
+//     straight into registers with a one-chunk prefetch.
+//   * Grouped mode (experts): workgroup (group, n-tile) loops over the rows the
+//     router sent to that group (device-side offsets; empty experts exit at
+//     once).  The shared expert's rows, whose count the host knows, are spread
+//     over a fixed m-chunk grid instead.
+//   * For the fixed grid, blocks that share an n-tile are mapped to the same XCD
+//     (blocks are dispatched round-robin over the 8 XCDs) so the re-reads of a
+//     W tile by other m-chunks hit that XCD's L2.
+//
+// fp32 workloads use the same packing and loop with 16x16x4 fp32 MFMAs (8 per
+// 32-wide k-step); lanes feed matching k indices to A and B, so the sum is the
+// plain dot product.
+#include "common.h"
+
+namespace {
+
+template <typename T> struct Frag;
+template <> struct Frag<bf16_t> { uint4 v; };
+template <> struct Frag<float> { float4 a, b; };
+
+template <typename T> DG_DEV Frag<T> ld_frag(const T* p);
+template <> DG_DEV Frag<bf16_t> ld_frag<bf16_t>(const bf16_t* p) {
+  Frag<bf16_t> f;
+  f.v = *reinterpret_cast<const uint4*>(p);
+  return f;
+}
+template <> DG_DEV Frag<float> ld_frag<float>(const float* p) {
+  Frag<float> f;
+  f.a = reinterpret_cast<const float4*>(p)[0];
+  f.b = reinterpret_cast<const float4*>(p)[1];
+  return f;
+}
+template <typename T> DG_DEV Frag<T> zero_frag();
+template <> DG_DEV Frag<bf16_t> zero_frag<bf16_t>() { Frag<bf16_t> f; f.v = make_uint4(0, 0, 0, 0); return f; }
+template <> DG_DEV Frag<float> zero_frag<float>() {
+  Frag<float> f; f.a = make_float4(0, 0, 0, 0); f.b = f.a; return f;
+}
+
+DG_DEV void mma(floatx4& c, const Frag<bf16_t>& a, const Frag<bf16_t>& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, a.v),
+                                               __builtin_bit_cast(bf16x8_v, b.v), c, 0, 0, 0);
+}
+DG_DEV void mma(floatx4& c, const Frag<float>& a, const Frag<float>& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.x, b.a.x, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.y, b.a.y, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.z, b.a.z, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.w, b.a.w, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.x, b.b.x, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.y, b.b.y, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.z, b.b.z, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.w, b.b.w, c, 0, 0, 0);
+}
+
+DG_DEV float gelu_tanh(float z) {
+  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
+  return 0.5f * z * (1.0f + tanhf(k0 * (z + 0.044715f * z * z * z)));
+}
+
+template <typename T> DG_DEV void st(void* base, long long off, float v) {
+  reinterpret_cast<T*>(base)[off] = from_f<T>(v);
+}
+
+// Epilogue for one output row and lane column, WN consecutive n-blocks.
+template <typename T, int WN, int EPI>
+DG_DEV void epilogue(const EpiArgs& e, int row, int nb0, int nb_valid, int c, const float* v) {
+  if constexpr (EPI == EPI_STORE_F32) {
+    float* out = reinterpret_cast<float*>(e.out);
+#pragma unroll
+    for (int w = 0; w < WN; ++w)
+      if (w < nb_valid) out[(long long)row * e.ldo + (nb0 + w) * 16 + c] = v[w];
+  } else if constexpr (EPI == EPI_DOWN) {
+    const int orow = e.slot[row];
+    if ((unsigned)orow >= (unsigned)e.out_rows) return;
+    const float g = row < e.routed_rows ? e.gates[orow] : 1.0f;
+    float* out = reinterpret_cast<float*>(e.out);
+#pragma unroll
+    for (int w = 0; w < WN; ++w)
+      if (w < nb_valid) out[(long long)orow * e.ldo + (nb0 + w) * 16 + c] = v[w] * g;
+  } else if constexpr (EPI == EPI_GEGLU) {
+    // n-block 2p holds gate columns, 2p+1 the up columns of the same outputs
+#pragma unroll
+    for (int p = 0; p < WN / 2; ++p) {
+      const int col = ((nb0 + 2 * p) >> 1) * 16 + c;
+      st<T>(e.out, (long long)row * e.ldo + col, gelu_tanh(v[2 * p]) * v[2 * p + 1]);
+    }
+  } else if constexpr (EPI == EPI_QKV) {
+    const int b = row / e.N, i = row - b * e.N;
+    const int bph = e.D >> 4;  // 16-column blocks per head
+#pragma unroll
+    for (int p = 0; p < WN / 2; ++p) {
+      const int nb = nb0 + 2 * p;
+      const int hs = nb / bph, w0 = nb - hs * bph;
+      float x1 = v[2 * p], x2 = v[2 * p + 1];
+      if (hs < e.Hq + e.Hkv) {
+        // rotary pair (d, d + D/2) sits in the two n-blocks of this wave
+        const int d = (w0 >> 1) * 16 + c;
+        const int n_rot = e.is_global ? e.n_rot_global : e.n_rot_local;
+        if (d < n_rot) {
+          const float2 cs = e.rope_cs[((long long)row) * (e.D >> 1) + d];
+          const float y1 = x1 * cs.x - x2 * cs.y;
+          const float y2 = x2 * cs.x + x1 * cs.y;
+          x1 = y1; x2 = y2;
+        }
+        if (hs < e.Hq) {
+          const long long o = b * e.qs[0] + hs * e.qs[1] + i * e.qs[2];
+          st<T>(e.q, o + d * e.qs[3], x1);
+          st<T>(e.q, o + (d + (e.D >> 1)) * e.qs[3], x2);
+        } else {
+          const long long o = b * e.ks[0] + (hs - e.Hq) * e.ks[1] + i * e.ks[2];
+          st<T>(e.k, o + d * e.ks[3], x1);
+          st<T>(e.k, o + (d + (e.D >> 1)) * e.ks[3], x2);
+        }
+      } else {
+        const int h = hs - e.Hq - e.Hkv;
+        const int d = w0 * 16 + c;
+        const long long o = b * e.vs[0] + h * e.vs[1] + i * e.vs[2];
+        st<T>(e.v, o + d * e.vs[3], x1);
+        st<T>(e.v, o + (d + 16) * e.vs[3], x2);
+      }
+    }
+  }
+}
+
+template <typename T, int MT, int WN, int EPI>
+__global__ __launch_bounds__(256) void k_gemm(GemmArgs g, EpiArgs e) {
+  constexpr int KC = 4;                  // k-steps (of 32) per staged chunk
+  constexpr int KCH = KC * 32;
+  constexpr int ROWS = MT * 16;
+  constexpr int VEC = 16 / sizeof(T);    // elements per 16-byte vector
+  constexpr int LDS_LD = KCH + VEC;      // padded LDS row
+  constexpr int VPR = KCH / VEC;         // vectors per row and chunk
+  constexpr int VPT = ROWS * VPR / 256;  // vectors per thread
+  static_assert(VPT * 256 == ROWS * VPR, "A chunk must split evenly over 256 threads");
+  __shared__ __align__(16) T As[ROWS * LDS_LD];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tiles = (g.NB + 4 * WN - 1) / (4 * WN);
+  const int KB = g.K >> 5;
+  const int NKC = (KB + KC - 1) / KC;
+
+  // ---- block -> (group, n-tile, rows)
+  int bid = blockIdx.x, group, tile, rs, re;
+  bool dynamic_rows;
+  const int smc = (g.static_rows + ROWS - 1) / ROWS;
+  const int n_static = tiles * smc;
+  if (bid < n_static) {
+    int mc;
+    if ((tiles & 7) == 0 && smc > 1) {
+      const int xcd = bid & 7, slot = bid >> 3;
+      tile = (slot / smc) * 8 + xcd;
+      mc = slot % smc;
+    } else {
+      tile = bid / smc;
+      mc = bid % smc;
+    }
+    group = g.static_group;
+    rs = g.static_row0 + mc * ROWS;
+    re = min(g.static_row0 + g.static_rows, rs + ROWS);
+    dynamic_rows = false;
+  } else {
+    bid -= n_static;
+    group = bid / tiles;
+    tile = bid - group * tiles;
+    rs = g.group_off[group];
+    re = g.group_off[group + 1];
+    dynamic_rows = true;
+  }
+  if (rs >= re) return;  // block-uniform: no rows for this expert
+
+  const T* __restrict__ A = reinterpret_cast<const T*>(g.A);
+  const T* __restrict__ Bg = reinterpret_cast<const T*>(g.B) + (long long)group * g.b_group_stride;
+  const int nb0 = tile * 4 * WN + wave * WN;
+  const int nb_valid = g.NB - nb0;  // wave-uniform; <= 0 means this wave has no columns
+  const int c = lane & 15, rg = (lane >> 4) * 4;
+
+  for (int row0 = rs; row0 < re; row0 += ROWS) {
+    const int row_end = min(re, row0 + ROWS);
+    const int act_mt = (row_end - row0 + 15) >> 4;
+    floatx4 acc[MT][WN];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int w = 0; w < WN; ++w) acc[m][w] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    uint4 areg[VPT];
+    auto loadA = [&](int kc) {
+#pragma unroll
+      for (int v = 0; v < VPT; ++v) {
+        const int idx = tid + v * 256;
+        const int rr = idx / VPR, cv = idx - rr * VPR;
+        const int r = row0 + rr, k0 = kc * KCH + cv * VEC;
+        uint4 val = make_uint4(0, 0, 0, 0);
+        if (r < row_end && k0 < g.K) {
+          long long ar = r;
+          if (g.a_rows) {
+            ar = g.a_rows[r];
+            ar = ar < 0 ? 0 : (ar >= g.a_rows_max ? g.a_rows_max - 1 : ar);
+          }
+          val = *reinterpret_cast<const uint4*>(A + ar * g.lda + k0);
+        }
+        areg[v] = val;
+      }
+    };
+    auto storeA = [&]() {
+#pragma unroll
+      for (int v = 0; v < VPT; ++v) {
+        const int idx = tid + v * 256;
+        const int rr = idx / VPR, cv = idx - rr * VPR;
+        *reinterpret_cast<uint4*>(&As[rr * LDS_LD + cv * VEC]) = areg[v];
+      }
+    };
+    Frag<T> bcur[KC][WN], bnext[KC][WN];
+    auto loadB = [&](int kc, Frag<T> (&bf)[KC][WN]) {
+#pragma unroll
+      for (int ks = 0; ks < KC; ++ks) {
+        const int kb = kc * KC + ks;
+#pragma unroll
+        for (int w = 0; w < WN; ++w) {
+          if (kb < KB && w < nb_valid)
+            bf[ks][w] = ld_frag<T>(Bg + ((long long)(nb0 + w) * KB + kb) * 512 + lane * 8);
+          else
+            bf[ks][w] = zero_frag<T>();
+        }
+      }
+    };
+
+    loadA(0);
+    loadB(0, bcur);
+    storeA();
+    __syncthreads();
+    for (int kc = 0; kc < NKC; ++kc) {
+      const bool more = kc + 1 < NKC;
+      if (more) {
+        loadA(kc + 1);
+        loadB(kc + 1, bnext);
+      }
+      const int nks = min(KC, KB - kc * KC);
+      if (nb_valid > 0) {
+#pragma unroll
+        for (int ks = 0; ks < KC; ++ks) {
+          if (ks < nks) {
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+              if (m < act_mt) {
+                const Frag<T> a = ld_frag<T>(&As[(m * 16 + c) * LDS_LD + ks * 32 + (lane >> 4) * 8]);
+#pragma unroll
+                for (int w = 0; w < WN; ++w) mma(acc[m][w], a, bcur[ks][w]);
+              }
+            }
+          }
+        }
+      }
+      __syncthreads();
+      if (more) {
+        storeA();
+#pragma unroll
+        for (int ks = 0; ks < KC; ++ks)
+#pragma unroll
+          for (int w = 0; w < WN; ++w) bcur[ks][w] = bnext[ks][w];
+      }
+      __syncthreads();
+    }
+
+    if (nb_valid > 0) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m < act_mt) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = row0 + m * 16 + rg + r;
+            if (row < row_end) {
+              float v[WN];
+#pragma unroll
+              for (int w = 0; w < WN; ++w) v[w] = acc[m][w][r];
+              epilogue<T, WN, EPI>(e, row, nb0, nb_valid, c, v);
+            }
+          }
+        }
+      }
+    }
+    if (!dynamic_rows) break;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// weight repack
+// ----------------------------------------------------------------------------
+template <typename T>
+__global__ void k_pack(PackArgs a, int nbatch, long long src_bs, long long dst_bs) {
+  const int KB = a.K >> 5;
+  const long long per = (long long)a.N * a.K;
+  const long long total = per * nbatch;
+  const T* src = reinterpret_cast<const T*>(a.src);
+  const T* src2 = reinterpret_cast<const T*>(a.src2);
+  T* dst = reinterpret_cast<T*>(a.dst);
+  for (long long idx = blockIdx.x * (long long)blockDim.x + threadIdx.x; idx < total;
+       idx += (long long)gridDim.x * blockDim.x) {
+    const long long bi = idx / per, o = idx - bi * per;
+    const int j = (int)(o & 7), lane = (int)((o >> 3) & 63);
+    const long long kbnb = o >> 9;
+    const int kb = (int)(kbnb % KB), nb = (int)(kbnb / KB);
+    const int k = kb * 32 + (lane >> 4) * 8 + j;
+    const T* s = src + bi * src_bs;
+    int nblk = nb;
+    if (a.colmap == 1) {
+      const int bph = a.head_dim >> 4, hs = nb / bph, w = nb - hs * bph;
+      nblk = hs * bph + ((w & 1) ? (w >> 1) + (bph >> 1) : (w >> 1));
+    } else if (a.colmap == 2) {
+      nblk = nb >> 1;
+      if (nb & 1) s = src2 + bi * src_bs;
+    }
+    const long long n = (long long)nblk * 16 + (lane & 15);
+    dst[bi * dst_bs + o] = a.src_kn ? s[(long long)k * a.ld + n] : s[n * a.ld + k];
+  }
+}
+
+template <typename T, int MT, int WN, int EPI>
+hipError_t run_gemm(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
+  constexpr int ROWS = MT * 16;
+  const int tiles = (g.NB + 4 * WN - 1) / (4 * WN);
+  const int smc = (g.static_rows + ROWS - 1) / ROWS;
+  const long long blocks = (long long)tiles * smc + (long long)tiles * g.n_groups;
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL((k_gemm<T, MT, WN, EPI>), dim3((unsigned)blocks), dim3(256), 0, s, g, e);
+  return hipGetLastError();
+}
+
+template <typename T, int EPI>
+hipError_t run_gemm_mt(const GemmArgs& g, const EpiArgs& e, int mt, hipStream_t s) {
+  // 128-row chunks only for bf16 (the fp32 chunk would exceed 64 KB of LDS)
+  if constexpr (sizeof(T) == 2) {
+    if (mt >= 8) return run_gemm<T, 8, 2, EPI>(g, e, s);
+  }
+  return run_gemm<T, 4, 2, EPI>(g, e, s);
+}
+
+template <typename T>
+hipError_t run_gemm_t(const GemmArgs& g, const EpiArgs& e, int mt, hipStream_t s) {
+  switch (e.kind) {
+    case EPI_STORE_F32: return run_gemm_mt<T, EPI_STORE_F32>(g, e, mt, s);
+    case EPI_GEGLU: return run_gemm_mt<T, EPI_GEGLU>(g, e, mt, s);
+    case EPI_DOWN: return run_gemm_mt<T, EPI_DOWN>(g, e, mt, s);
+    case EPI_QKV: return run_gemm_mt<T, EPI_QKV>(g, e, mt, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_gemm(int is_bf16, const GemmArgs& g, const EpiArgs& e, int mt, hipStream_t s) {
+  return is_bf16 ? run_gemm_t<bf16_t>(g, e, mt, s) : run_gemm_t<float>(g, e, mt, s);
+}
+
+hipError_t launch_pack(int is_bf16, const PackArgs& a, hipStream_t s) {
+  return launch_pack_batched(is_bf16, a, 1, 0, 0, s);
+}
+
+hipError_t launch_pack_batched(int is_bf16, const PackArgs& a, int nbatch, long long src_bs,
+                               long long dst_bs, hipStream_t s) {
+  const long long total = (long long)a.N * a.K * nbatch;
+  if (total <= 0) return hipSuccess;
+  const long long want = (total + 255) / 256;
+  const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
+  if (is_bf16)
+    hipLaunchKernelGGL(k_pack<bf16_t>, dim3(blocks), dim3(256), 0, s, a, nbatch, src_bs, dst_bs);
+  else
+    hipLaunchKernelGGL(k_pack<float>, dim3(blocks), dim3(256), 0, s, a, nbatch, src_bs, dst_bs);
+  return hipGetLastError();
+}

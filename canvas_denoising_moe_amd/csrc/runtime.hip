@@ -1,0 +1,694 @@
+// Host runtime behind the C ABI in include/dg.h: owns the packed weights,
+// the prompt KV copies and the workspaces, validates every call before it
+// enqueues anything, and sequences the kernels of a denoise pass on the
+// caller's stream.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "common.h"
+#include "dg.h"
+
+namespace {
+
+std::string g_create_error;
+
+struct LayerW {
+  void* qkv = nullptr;   // packed [(Hq+2Hkv)D/16][H/32][64][8]
+  void* wo = nullptr;    // packed [H/16][HqD/32][64][8]
+  void* router = nullptr;
+  void* gu = nullptr;    // (E+1) experts, packed gate|up interleave [2F/16][H/32][64][8]
+  void* down = nullptr;  // (E+1) experts, packed [H/16][F/32][64][8]
+  void* norm[4] = {nullptr, nullptr, nullptr, nullptr};  // in, pa, pf, pf2
+  bool set = false;
+};
+
+struct SlotKV {
+  int prompt_len = -1;
+  std::vector<void*> k, v;       // per layer: K [Hkv][len][D], V^T [Hkv][D][len]
+  std::vector<long long> cap;    // allocated positions per layer
+  std::vector<int> len;
+};
+
+}  // namespace
+
+struct dg_ctx {
+  dg_config c{};
+  int dev = 0;
+  hipStream_t st = nullptr;
+  int bf16 = 0;
+  size_t es = 4;
+  std::vector<LayerW> L;
+  void* embed = nullptr;
+  void* norm_final = nullptr;
+  bool embed_set = false;
+  std::vector<SlotKV> slots;
+  float2* rope = nullptr;  // [max_batch][N][D/2]
+  // workspaces
+  float *x = nullptr, *ao = nullptr, *rl = nullptr, *gates = nullptr, *y = nullptr, *logits = nullptr,
+        *conf = nullptr, *part_o = nullptr, *part_m = nullptr, *part_l = nullptr;
+  void *a = nullptr, *f = nullptr, *q = nullptr, *kc = nullptr, *vc = nullptr, *o = nullptr, *u = nullptr;
+  int32_t *idx = nullptr, *offsets = nullptr, *perm = nullptr, *arows = nullptr, *pred = nullptr;
+  long long part_cap = 0;
+  int32_t* trace = nullptr;
+  std::string err;
+  std::vector<void*> owned;
+};
+
+namespace {
+
+dg_status fail(dg_ctx* ctx, dg_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  if (ctx) ctx->err = buf; else g_create_error = buf;
+  return s;
+}
+
+#define HIPX(expr)                                                                       \
+  do {                                                                                   \
+    hipError_t _e = (expr);                                                              \
+    if (_e != hipSuccess) return fail(ctx, DG_EHIP, "%s: %s", #expr, hipGetErrorString(_e)); \
+  } while (0)
+
+dg_status dalloc(dg_ctx* ctx, void** p, size_t bytes) {
+  *p = nullptr;
+  if (bytes == 0) return DG_OK;
+  hipError_t e = hipMalloc(p, bytes);
+  if (e != hipSuccess) {
+    *p = nullptr;
+    (void)hipGetLastError();
+    return fail(ctx, DG_ENOMEM, "hipMalloc(%zu bytes) failed: %s", bytes, hipGetErrorString(e));
+  }
+  ctx->owned.push_back(*p);
+  return DG_OK;
+}
+
+void dfree(dg_ctx* ctx, void* p) {
+  if (!p) return;
+  for (auto& q : ctx->owned)
+    if (q == p) { q = nullptr; break; }
+  (void)hipFree(p);
+}
+
+#define TRY(expr)                      \
+  do {                                 \
+    dg_status _s = (expr);             \
+    if (_s != DG_OK) return _s;        \
+  } while (0)
+
+template <typename P> dg_status dalloc_t(dg_ctx* ctx, P** p, size_t bytes) {
+  void* v = nullptr;
+  dg_status s = dalloc(ctx, &v, bytes);
+  *p = reinterpret_cast<P*>(v);
+  return s;
+}
+
+bool is_global(const dg_config& c, int l) { return (c.global_layer_mask >> l) & 1ull; }
+int kv_len(const dg_config& c, int l, int prompt_len) {
+  return is_global(c, l) ? prompt_len : (prompt_len < c.window ? prompt_len : c.window);
+}
+
+dg_status check_config(const dg_config* c) {
+  dg_ctx* ctx = nullptr;
+  if (!c) return fail(ctx, DG_EINVAL, "config is NULL");
+  if (c->n_layers < 1 || c->n_layers > 64) return fail(ctx, DG_EINVAL, "n_layers must be in [1, 64]");
+  if (c->hidden <= 0 || c->hidden % 32 || c->hidden > 16384)
+    return fail(ctx, DG_EUNSUPPORTED, "hidden must be a positive multiple of 32 (<= 16384)");
+  if (c->n_heads <= 0 || c->n_kv_heads <= 0 || c->n_heads % c->n_kv_heads)
+    return fail(ctx, DG_EINVAL, "n_heads must be a positive multiple of n_kv_heads");
+  if (c->head_dim <= 0 || c->head_dim % 32 || c->head_dim > 256)
+    return fail(ctx, DG_EUNSUPPORTED, "head_dim must be a multiple of 32 in [32, 256]");
+  if (c->n_experts <= 0 || c->n_experts % 16 || c->n_experts > 256)
+    return fail(ctx, DG_EUNSUPPORTED, "n_experts must be a multiple of 16 in [16, 256]");
+  if (c->top_k < 1 || c->top_k > 8 || c->top_k > c->n_experts)
+    return fail(ctx, DG_EINVAL, "top_k must be in [1, min(8, n_experts)]");
+  if (c->n_shared != 1) return fail(ctx, DG_EUNSUPPORTED, "exactly one shared expert is supported");
+  if (c->expert_ffn <= 0 || c->expert_ffn % 32)
+    return fail(ctx, DG_EUNSUPPORTED, "expert_ffn must be a positive multiple of 32");
+  if (c->has_lm_head && (c->vocab <= 0 || c->vocab % 16))
+    return fail(ctx, DG_EUNSUPPORTED, "vocab must be a positive multiple of 16");
+  if (c->canvas_len <= 0 || c->canvas_len % 16 || c->canvas_len > 4096)
+    return fail(ctx, DG_EUNSUPPORTED, "canvas_len must be a multiple of 16 in [16, 4096]");
+  if (c->max_batch < 1 || c->max_batch > DG_MAX_BATCH)
+    return fail(ctx, DG_EINVAL, "max_batch must be in [1, 64]");
+  const long long M = (long long)c->max_batch * c->canvas_len;
+  if (M > 4096) return fail(ctx, DG_EUNSUPPORTED, "max_batch * canvas_len must be <= 4096");
+  if ((long long)c->n_experts * ((M + 31) / 32) > 16384)
+    return fail(ctx, DG_EUNSUPPORTED, "n_experts * ceil(max_batch*canvas_len/32) must be <= 16384");
+  if (c->window < 0 || c->max_prompt_len < 0) return fail(ctx, DG_EINVAL, "window and max_prompt_len must be >= 0");
+  if (c->dtype != DG_F32 && c->dtype != DG_BF16) return fail(ctx, DG_EINVAL, "dtype must be DG_F32 or DG_BF16");
+  if (!(c->rope_theta > 0.f) || !(c->prope_frac >= 0.f && c->prope_frac <= 1.f) || !(c->rms_eps >= 0.f))
+    return fail(ctx, DG_EINVAL, "rope_theta > 0, prope_frac in [0, 1] and rms_eps >= 0 required");
+  return DG_OK;
+}
+
+dg_status enter(dg_ctx* ctx) {
+  if (!ctx) return fail(nullptr, DG_EINVAL, "context is NULL");
+  ctx->err.clear();
+  HIPX(hipSetDevice(ctx->dev));
+  // surface asynchronous faults of earlier work without blocking
+  HIPX(hipGetLastError());
+  return DG_OK;
+}
+
+dg_status alloc_workspaces(dg_ctx* ctx) {
+  const dg_config& c = ctx->c;
+  const size_t M = (size_t)c.max_batch * c.canvas_len;
+  const size_t H = c.hidden, D = c.head_dim, E = c.n_experts, K = c.top_k, F = c.expert_ffn;
+  const size_t es = ctx->es;
+  const size_t rows_r = M * K + M;
+  TRY(dalloc_t(ctx, &ctx->x, M * H * 4));
+  TRY(dalloc_t(ctx, &ctx->ao, M * H * 4));
+  TRY(dalloc(ctx, &ctx->a, M * H * es));
+  TRY(dalloc(ctx, &ctx->f, M * H * es));
+  TRY(dalloc(ctx, &ctx->q, M * c.n_heads * D * es));
+  TRY(dalloc(ctx, &ctx->kc, M * c.n_kv_heads * D * es));
+  TRY(dalloc(ctx, &ctx->vc, M * c.n_kv_heads * D * es));
+  TRY(dalloc(ctx, &ctx->o, M * c.n_heads * D * es));
+  TRY(dalloc_t(ctx, &ctx->rl, M * E * 4));
+  TRY(dalloc_t(ctx, &ctx->idx, M * K * 4));
+  TRY(dalloc_t(ctx, &ctx->gates, M * K * 4));
+  TRY(dalloc_t(ctx, &ctx->offsets, (E + 2) * 4));
+  TRY(dalloc_t(ctx, &ctx->perm, rows_r * 4));
+  TRY(dalloc_t(ctx, &ctx->arows, rows_r * 4));
+  TRY(dalloc(ctx, &ctx->u, rows_r * F * es));
+  TRY(dalloc_t(ctx, &ctx->y, rows_r * H * 4));
+  if (c.has_lm_head) TRY(dalloc_t(ctx, &ctx->logits, M * (size_t)c.vocab * 4));
+  TRY(dalloc_t(ctx, &ctx->pred, M * 4));
+  TRY(dalloc_t(ctx, &ctx->conf, M * 4));
+  TRY(dalloc_t(ctx, &ctx->rope, (size_t)c.max_batch * c.canvas_len * (D / 2) * sizeof(float2)));
+  // attention split partials: up to 64 splits of every query row
+  const long long qrows = (long long)M * c.n_heads;
+  ctx->part_cap = qrows * 64;
+  TRY(dalloc_t(ctx, &ctx->part_o, (size_t)ctx->part_cap * D * 4));
+  TRY(dalloc_t(ctx, &ctx->part_m, (size_t)ctx->part_cap * 4));
+  TRY(dalloc_t(ctx, &ctx->part_l, (size_t)ctx->part_cap * 4));
+  return DG_OK;
+}
+
+bool weights_ready(const dg_ctx* ctx) {
+  for (const auto& l : ctx->L)
+    if (!l.set) return false;
+  return !ctx->c.has_lm_head || ctx->embed_set;
+}
+
+dg_status check_slots(dg_ctx* ctx, int batch) {
+  for (int b = 0; b < batch; ++b)
+    if (ctx->slots[b].prompt_len < 0)
+      return fail(ctx, DG_ESTATE, "prompt KV of slot %d is not loaded", b);
+  return DG_OK;
+}
+
+// ---------------------------------------------------------------------------
+// pass building blocks
+// ---------------------------------------------------------------------------
+
+dg_status enqueue_qkv(dg_ctx* ctx, int l, int B, const void* a, void* q, void* k, void* v,
+                      const long long* qs, const long long* ks, const long long* vs) {
+  const dg_config& c = ctx->c;
+  const int H = c.hidden, D = c.head_dim;
+  GemmArgs g{};
+  g.A = a; g.lda = H; g.B = ctx->L[l].qkv; g.K = H;
+  g.NB = (c.n_heads + 2 * c.n_kv_heads) * D / 16;
+  g.static_rows = B * c.canvas_len;
+  EpiArgs e{};
+  e.kind = EPI_QKV;
+  e.q = q; e.k = k; e.v = v;
+  for (int i = 0; i < 4; ++i) { e.qs[i] = qs[i]; e.ks[i] = ks[i]; e.vs[i] = vs[i]; }
+  e.rope_cs = ctx->rope;
+  e.N = c.canvas_len; e.D = D; e.Hq = c.n_heads; e.Hkv = c.n_kv_heads;
+  e.n_rot_local = D / 2;
+  e.n_rot_global = (int)(c.prope_frac * (float)(D / 2));
+  e.is_global = is_global(c, l);
+  HIPX(launch_gemm(ctx->bf16, g, e, 4, ctx->st));
+  return DG_OK;
+}
+
+dg_status enqueue_attention(dg_ctx* ctx, int l, int B, void* o, int canvas_keys) {
+  const dg_config& c = ctx->c;
+  AttnArgs aa{};
+  aa.q = ctx->q; aa.kc = ctx->kc; aa.vc = ctx->vc;
+  aa.B = B; aa.N = c.canvas_len; aa.Hq = c.n_heads; aa.Hkv = c.n_kv_heads; aa.D = c.head_dim;
+  aa.canvas_keys = canvas_keys;
+  aa.o = o;
+  aa.part_o = ctx->part_o; aa.part_m = ctx->part_m; aa.part_l = ctx->part_l;
+  aa.part_cap_rows = ctx->part_cap;
+  for (int b = 0; b < B; ++b) {
+    aa.kp[b] = ctx->slots[b].k[l];
+    aa.vp[b] = ctx->slots[b].v[l];
+    aa.lw[b] = ctx->slots[b].len[l];
+  }
+  HIPX(launch_attention(ctx->bf16, aa, ctx->st));
+  return DG_OK;
+}
+
+// m-chunk height for the grouped expert GEMMs: 128 rows once experts average
+// more than 48 rows, 64 otherwise
+int expert_mt(const dg_config& c, int M) { return (long long)M * c.top_k > 48LL * c.n_experts ? 8 : 4; }
+
+// routed + shared expert FFNs of layer l on f (routing already in idx/gates/offsets/perm/arows);
+// leaves y [M*k + M, H]
+dg_status enqueue_experts(dg_ctx* ctx, int l, int M, const void* f) {
+  const dg_config& c = ctx->c;
+  const int H = c.hidden, F = c.expert_ffn, E = c.n_experts, K = c.top_k;
+  const int mt = expert_mt(c, M);
+  GemmArgs g{};
+  g.A = f; g.lda = H; g.a_rows = ctx->arows; g.a_rows_max = M;
+  g.B = ctx->L[l].gu; g.b_group_stride = 2LL * F * H;
+  g.K = H; g.NB = 2 * F / 16;
+  g.static_row0 = M * K; g.static_rows = M; g.static_group = E;
+  g.group_off = ctx->offsets; g.n_groups = E;
+  EpiArgs e{};
+  e.kind = EPI_GEGLU; e.out = ctx->u; e.ldo = F;
+  HIPX(launch_gemm(ctx->bf16, g, e, mt, ctx->st));
+
+  GemmArgs d{};
+  d.A = ctx->u; d.lda = F; d.a_rows = nullptr;
+  d.B = ctx->L[l].down; d.b_group_stride = (long long)F * H;
+  d.K = F; d.NB = H / 16;
+  d.static_row0 = M * K; d.static_rows = M; d.static_group = E;
+  d.group_off = ctx->offsets; d.n_groups = E;
+  EpiArgs ed{};
+  ed.kind = EPI_DOWN; ed.out = ctx->y; ed.ldo = H;
+  ed.slot = ctx->perm; ed.gates = ctx->gates; ed.routed_rows = M * K; ed.out_rows = M * K + M;
+  HIPX(launch_gemm(ctx->bf16, d, ed, mt, ctx->st));
+  return DG_OK;
+}
+
+dg_status enqueue_dense(dg_ctx* ctx, const void* A, int lda, const void* Bp, int K, int N, int M, float* out,
+                        int ldo) {
+  GemmArgs g{};
+  g.A = A; g.lda = lda; g.B = Bp; g.K = K; g.NB = N / 16; g.static_rows = M;
+  EpiArgs e{};
+  e.kind = EPI_STORE_F32; e.out = out; e.ldo = ldo;
+  HIPX(launch_gemm(ctx->bf16, g, e, 4, ctx->st));
+  return DG_OK;
+}
+
+// Decoder layers on ctx->x, with ctx->a holding the normalised input of the
+// first layer.  The last layer leaves RMSNorm(x)(1 + w_last_out) in ctx->a when
+// w_last_out is given (the final norm before the LM head).
+dg_status enqueue_layers(dg_ctx* ctx, int B, const void* w_last_out) {
+  const dg_config& c = ctx->c;
+  const int N = c.canvas_len, M = B * N, H = c.hidden, D = c.head_dim;
+  const int Hq = c.n_heads, Hkv = c.n_kv_heads, E = c.n_experts, K = c.top_k;
+  const long long qs[4] = {(long long)Hq * N * D, (long long)N * D, D, 1};
+  const long long ks[4] = {(long long)Hkv * N * D, (long long)N * D, D, 1};
+  const long long vs[4] = {(long long)Hkv * D * N, (long long)D * N, 1, N};
+  for (int l = 0; l < c.n_layers; ++l) {
+    const LayerW& W = ctx->L[l];
+    TRY(enqueue_qkv(ctx, l, B, ctx->a, ctx->q, ctx->kc, ctx->vc, qs, ks, vs));
+    TRY(enqueue_attention(ctx, l, B, ctx->o, 1));
+    TRY(enqueue_dense(ctx, ctx->o, Hq * D, W.wo, Hq * D, H, M, ctx->ao, H));
+    NormArgs na{};
+    na.mode = 0; na.rows = M; na.H = H; na.k = K; na.eps = c.rms_eps;
+    na.x = ctx->x; na.delta = ctx->ao; na.w_delta = W.norm[1]; na.w_out = W.norm[2]; na.out = ctx->f;
+    HIPX(launch_residual_norm(ctx->bf16, na, ctx->st));
+    TRY(enqueue_dense(ctx, ctx->f, H, W.router, H, E, M, ctx->rl, E));
+    HIPX(launch_moe_route(ctx->rl, M, E, K, ctx->idx, ctx->gates, nullptr, ctx->offsets, ctx->perm,
+                          ctx->arows, ctx->st));
+    if (ctx->trace)
+      HIPX(hipMemcpyAsync(ctx->trace + (size_t)l * M * K, ctx->idx, (size_t)M * K * 4,
+                          hipMemcpyDeviceToDevice, ctx->st));
+    TRY(enqueue_experts(ctx, l, M, ctx->f));
+    NormArgs nc{};
+    nc.mode = 1; nc.rows = M; nc.H = H; nc.k = K; nc.eps = c.rms_eps;
+    nc.x = ctx->x; nc.delta = ctx->y; nc.w_delta = c.post_ffn_norm ? W.norm[3] : nullptr;
+    nc.w_out = (l + 1 < c.n_layers) ? ctx->L[l + 1].norm[0] : w_last_out;
+    nc.out = ctx->a;
+    HIPX(launch_residual_norm(ctx->bf16, nc, ctx->st));
+  }
+  return DG_OK;
+}
+
+dg_status enqueue_pass(dg_ctx* ctx, int B, int32_t* tokens, uint8_t* locked, const StepsArg& steps) {
+  const dg_config& c = ctx->c;
+  const int N = c.canvas_len, M = B * N, H = c.hidden;
+  HIPX(launch_embed(ctx->bf16, tokens, M, H, c.vocab, ctx->embed, ctx->x, ctx->st));
+  NormArgs n0{};
+  n0.mode = 2; n0.rows = M; n0.H = H; n0.k = c.top_k; n0.eps = c.rms_eps;
+  n0.x = ctx->x; n0.w_out = ctx->L[0].norm[0]; n0.out = ctx->a;
+  HIPX(launch_residual_norm(ctx->bf16, n0, ctx->st));
+  TRY(enqueue_layers(ctx, B, ctx->norm_final));
+  TRY(enqueue_dense(ctx, ctx->a, H, ctx->embed, H, c.vocab, M, ctx->logits, c.vocab));
+  HIPX(launch_argmax_conf(ctx->logits, M, c.vocab, ctx->pred, ctx->conf, ctx->st));
+  HIPX(launch_lock_select(B, N, ctx->conf, ctx->pred, tokens, locked, steps, ctx->st));
+  return DG_OK;
+}
+
+size_t bytes_of(const dg_ctx* ctx, long long n) { return (size_t)n * ctx->es; }
+
+}  // namespace
+
+// ============================================================================
+// C ABI
+// ============================================================================
+
+extern "C" {
+
+dg_status dg_create(const dg_config* cfg, int32_t device, void* hip_stream, dg_ctx** out) {
+  g_create_error.clear();
+  if (!out) return fail(nullptr, DG_EINVAL, "out is NULL");
+  *out = nullptr;
+  dg_status s = check_config(cfg);
+  if (s != DG_OK) return s;
+  int ndev = 0;
+  hipError_t he = hipGetDeviceCount(&ndev);
+  if (he != hipSuccess || ndev <= 0) return fail(nullptr, DG_EHIP, "no HIP device available");
+  if (device < 0 || device >= ndev) return fail(nullptr, DG_EINVAL, "device %d out of range", device);
+  he = hipSetDevice(device);
+  if (he != hipSuccess) return fail(nullptr, DG_EHIP, "hipSetDevice: %s", hipGetErrorString(he));
+  dg_ctx* ctx = new dg_ctx();
+  ctx->c = *cfg;
+  ctx->dev = device;
+  ctx->st = reinterpret_cast<hipStream_t>(hip_stream);
+  ctx->bf16 = cfg->dtype == DG_BF16;
+  ctx->es = ctx->bf16 ? 2 : 4;
+  ctx->L.resize(cfg->n_layers);
+  ctx->slots.resize(cfg->max_batch);
+  s = alloc_workspaces(ctx);
+  if (s != DG_OK) {
+    g_create_error = ctx->err;
+    dg_destroy(ctx);
+    return s;
+  }
+  *out = ctx;
+  return DG_OK;
+}
+
+dg_status dg_destroy(dg_ctx* ctx) {
+  if (!ctx) return DG_OK;
+  (void)hipSetDevice(ctx->dev);
+  (void)hipStreamSynchronize(ctx->st);
+  for (void* p : ctx->owned)
+    if (p) (void)hipFree(p);
+  delete ctx;
+  return DG_OK;
+}
+
+const char* dg_last_error(const dg_ctx* ctx) { return ctx ? ctx->err.c_str() : g_create_error.c_str(); }
+
+dg_status dg_set_layer_weights(dg_ctx* ctx, int32_t layer, const dg_layer_weights* w) {
+  TRY(enter(ctx));
+  const dg_config& c = ctx->c;
+  if (layer < 0 || layer >= c.n_layers) return fail(ctx, DG_EINVAL, "layer %d out of range", layer);
+  if (!w) return fail(ctx, DG_EINVAL, "weights are NULL");
+  const void* ptrs[15] = {w->wq, w->wk, w->wv, w->wo, w->router, w->w_gate, w->w_up, w->w_down,
+                          w->sh_gate, w->sh_up, w->sh_down, w->norm_in, w->norm_pa, w->norm_pf, w->norm_pf2};
+  for (int i = 0; i < 15; ++i)
+    if (!ptrs[i]) return fail(ctx, DG_EINVAL, "layer %d: weight pointer %d is NULL", layer, i);
+  const long long H = c.hidden, D = c.head_dim, E = c.n_experts, F = c.expert_ffn;
+  const long long qd = c.n_heads * D, kvd = c.n_kv_heads * D;
+  LayerW& L = ctx->L[layer];
+  if (!L.qkv) {
+    TRY(dalloc(ctx, &L.qkv, bytes_of(ctx, (qd + 2 * kvd) * H)));
+    TRY(dalloc(ctx, &L.wo, bytes_of(ctx, qd * H)));
+    TRY(dalloc(ctx, &L.router, bytes_of(ctx, H * E)));
+    TRY(dalloc(ctx, &L.gu, bytes_of(ctx, (E + 1) * 2 * F * H)));
+    TRY(dalloc(ctx, &L.down, bytes_of(ctx, (E + 1) * F * H)));
+    for (int i = 0; i < 4; ++i) TRY(dalloc(ctx, &L.norm[i], bytes_of(ctx, H)));
+  }
+  const int KB = (int)(H / 32);
+  char* qkv = reinterpret_cast<char*>(L.qkv);
+  PackArgs p{};
+  // q and k with the rotary pairing, v plain; K = H for all three
+  p = PackArgs{w->wq, nullptr, qd, (int)H, (int)qd, 1, 1, (int)D, c.n_heads, qkv};
+  HIPX(launch_pack(ctx->bf16, p, ctx->st));
+  p = PackArgs{w->wk, nullptr, kvd, (int)H, (int)kvd, 1, 1, (int)D, c.n_kv_heads,
+               qkv + bytes_of(ctx, (qd / 16) * KB * 512)};
+  HIPX(launch_pack(ctx->bf16, p, ctx->st));
+  p = PackArgs{w->wv, nullptr, kvd, (int)H, (int)kvd, 1, 0, (int)D, 0,
+               qkv + bytes_of(ctx, ((qd + kvd) / 16) * KB * 512)};
+  HIPX(launch_pack(ctx->bf16, p, ctx->st));
+  p = PackArgs{w->wo, nullptr, H, (int)qd, (int)H, 1, 0, 0, 0, L.wo};
+  HIPX(launch_pack(ctx->bf16, p, ctx->st));
+  p = PackArgs{w->router, nullptr, E, (int)H, (int)E, 1, 0, 0, 0, L.router};
+  HIPX(launch_pack(ctx->bf16, p, ctx->st));
+  // routed experts 0..E-1 then the shared expert at index E
+  p = PackArgs{w->w_gate, w->w_up, F, (int)H, (int)(2 * F), 1, 2, 0, 0, L.gu};
+  HIPX(launch_pack_batched(ctx->bf16, p, (int)E, H * F, 2 * F * H, ctx->st));
+  p = PackArgs{w->sh_gate, w->sh_up, F, (int)H, (int)(2 * F), 1, 2, 0, 0,
+               reinterpret_cast<char*>(L.gu) + bytes_of(ctx, E * 2 * F * H)};
+  HIPX(launch_pack(ctx->bf16, p, ctx->st));
+  p = PackArgs{w->w_down, nullptr, H, (int)F, (int)H, 1, 0, 0, 0, L.down};
+  HIPX(launch_pack_batched(ctx->bf16, p, (int)E, F * H, F * H, ctx->st));
+  p = PackArgs{w->sh_down, nullptr, H, (int)F, (int)H, 1, 0, 0, 0,
+               reinterpret_cast<char*>(L.down) + bytes_of(ctx, E * F * H)};
+  HIPX(launch_pack(ctx->bf16, p, ctx->st));
+  const void* norms[4] = {w->norm_in, w->norm_pa, w->norm_pf, w->norm_pf2};
+  for (int i = 0; i < 4; ++i)
+    HIPX(hipMemcpyAsync(L.norm[i], norms[i], bytes_of(ctx, H), hipMemcpyDeviceToDevice, ctx->st));
+  L.set = true;
+  return DG_OK;
+}
+
+dg_status dg_set_embedding(dg_ctx* ctx, const void* embed, const void* norm_final) {
+  TRY(enter(ctx));
+  const dg_config& c = ctx->c;
+  if (!c.has_lm_head) return fail(ctx, DG_ESTATE, "context has no LM head");
+  if (!embed || !norm_final) return fail(ctx, DG_EINVAL, "embed and norm_final are required");
+  const long long H = c.hidden, V = c.vocab;
+  if (!ctx->embed) {
+    TRY(dalloc(ctx, &ctx->embed, bytes_of(ctx, V * H)));
+    TRY(dalloc(ctx, &ctx->norm_final, bytes_of(ctx, H)));
+  }
+  // the LM head contracts over H: W(k = h, n = v) = embed[v][h]
+  PackArgs p{embed, nullptr, H, (int)H, (int)V, 0, 0, 0, 0, ctx->embed};
+  HIPX(launch_pack(ctx->bf16, p, ctx->st));
+  HIPX(hipMemcpyAsync(ctx->norm_final, norm_final, bytes_of(ctx, H), hipMemcpyDeviceToDevice, ctx->st));
+  ctx->embed_set = true;
+  return DG_OK;
+}
+
+dg_status dg_init_weights(dg_ctx* ctx, const void* embed, const void* norm_final, const dg_layer_weights* layers) {
+  TRY(enter(ctx));
+  if (!layers) return fail(ctx, DG_EINVAL, "layers is NULL");
+  if (ctx->c.has_lm_head) TRY(dg_set_embedding(ctx, embed, norm_final));
+  for (int l = 0; l < ctx->c.n_layers; ++l) TRY(dg_set_layer_weights(ctx, l, &layers[l]));
+  return DG_OK;
+}
+
+dg_status dg_load_prompt_kv(dg_ctx* ctx, int32_t slot, int32_t prompt_len, const void* const* k,
+                            const void* const* v) {
+  TRY(enter(ctx));
+  const dg_config& c = ctx->c;
+  if (slot < 0 || slot >= c.max_batch) return fail(ctx, DG_EINVAL, "slot %d out of range", slot);
+  if (prompt_len < 0 || prompt_len > c.max_prompt_len)
+    return fail(ctx, DG_EINVAL, "prompt_len %d outside [0, max_prompt_len=%d]", prompt_len, c.max_prompt_len);
+  if (!k || !v) return fail(ctx, DG_EINVAL, "k and v arrays are required");
+  for (int l = 0; l < c.n_layers; ++l)
+    if (kv_len(c, l, prompt_len) > 0 && (!k[l] || !v[l]))
+      return fail(ctx, DG_EINVAL, "layer %d: K/V pointer is NULL", l);
+  SlotKV& S = ctx->slots[slot];
+  if (S.k.empty()) {
+    S.k.assign(c.n_layers, nullptr);
+    S.v.assign(c.n_layers, nullptr);
+    S.cap.assign(c.n_layers, 0);
+    S.len.assign(c.n_layers, 0);
+  }
+  const int Hkv = c.n_kv_heads, D = c.head_dim;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const int len = kv_len(c, l, prompt_len);
+    if (len > S.cap[l]) {
+      HIPX(hipStreamSynchronize(ctx->st));
+      dfree(ctx, S.k[l]);
+      dfree(ctx, S.v[l]);
+      S.k[l] = S.v[l] = nullptr;
+      S.cap[l] = 0;
+      TRY(dalloc(ctx, &S.k[l], bytes_of(ctx, (long long)len * Hkv * D)));
+      TRY(dalloc(ctx, &S.v[l], bytes_of(ctx, (long long)len * Hkv * D)));
+      S.cap[l] = len;
+    }
+    S.len[l] = len;
+    if (len > 0) {
+      HIPX(launch_kv_repack(ctx->bf16, k[l], len, Hkv, D, S.k[l], 0, ctx->st));
+      HIPX(launch_kv_repack(ctx->bf16, v[l], len, Hkv, D, S.v[l], 1, ctx->st));
+    }
+  }
+  HIPX(launch_rope_table(ctx->rope + (size_t)slot * c.canvas_len * (D / 2), c.canvas_len, D, prompt_len,
+                         (double)c.rope_theta, ctx->st));
+  S.prompt_len = prompt_len;
+  return DG_OK;
+}
+
+dg_status dg_denoise_step(dg_ctx* ctx, int32_t batch, int32_t* tokens, uint8_t* locked,
+                          const int32_t* steps_left_host, float* conf_out, int32_t* pred_out) {
+  TRY(enter(ctx));
+  const dg_config& c = ctx->c;
+  if (!c.has_lm_head) return fail(ctx, DG_ESTATE, "context has no LM head");
+  if (batch < 1 || batch > c.max_batch) return fail(ctx, DG_EINVAL, "batch %d outside [1, %d]", batch, c.max_batch);
+  if (!tokens || !locked || !steps_left_host) return fail(ctx, DG_EINVAL, "tokens, locked and steps_left are required");
+  if (!weights_ready(ctx)) return fail(ctx, DG_ESTATE, "weights are not loaded");
+  TRY(check_slots(ctx, batch));
+  StepsArg steps{};
+  for (int b = 0; b < batch; ++b) {
+    if (steps_left_host[b] < 1) return fail(ctx, DG_EINVAL, "steps_left[%d] = %d < 1", b, steps_left_host[b]);
+    steps.v[b] = steps_left_host[b];
+  }
+  TRY(enqueue_pass(ctx, batch, tokens, locked, steps));
+  const size_t M = (size_t)batch * c.canvas_len;
+  if (conf_out) HIPX(hipMemcpyAsync(conf_out, ctx->conf, M * 4, hipMemcpyDeviceToDevice, ctx->st));
+  if (pred_out) HIPX(hipMemcpyAsync(pred_out, ctx->pred, M * 4, hipMemcpyDeviceToDevice, ctx->st));
+  return DG_OK;
+}
+
+dg_status dg_generate_block(dg_ctx* ctx, int32_t batch, int32_t n_steps, int32_t* tokens, uint8_t* locked) {
+  TRY(enter(ctx));
+  const dg_config& c = ctx->c;
+  if (!c.has_lm_head) return fail(ctx, DG_ESTATE, "context has no LM head");
+  if (batch < 1 || batch > c.max_batch) return fail(ctx, DG_EINVAL, "batch %d outside [1, %d]", batch, c.max_batch);
+  if (n_steps < 1) return fail(ctx, DG_EINVAL, "n_steps must be >= 1");
+  if (!tokens || !locked) return fail(ctx, DG_EINVAL, "tokens and locked are required");
+  if (!weights_ready(ctx)) return fail(ctx, DG_ESTATE, "weights are not loaded");
+  TRY(check_slots(ctx, batch));
+  for (int t = 0; t < n_steps; ++t) {
+    StepsArg steps{};
+    for (int b = 0; b < batch; ++b) steps.v[b] = n_steps - t;
+    TRY(enqueue_pass(ctx, batch, tokens, locked, steps));
+  }
+  return DG_OK;
+}
+
+dg_status dg_forward_hidden(dg_ctx* ctx, int32_t batch, const float* x_in, float* x_out) {
+  TRY(enter(ctx));
+  const dg_config& c = ctx->c;
+  if (batch < 1 || batch > c.max_batch) return fail(ctx, DG_EINVAL, "batch %d outside [1, %d]", batch, c.max_batch);
+  if (!x_in || !x_out) return fail(ctx, DG_EINVAL, "x_in and x_out are required");
+  for (const auto& l : ctx->L)
+    if (!l.set) return fail(ctx, DG_ESTATE, "layer weights are not loaded");
+  TRY(check_slots(ctx, batch));
+  const int M = batch * c.canvas_len, H = c.hidden;
+  HIPX(hipMemcpyAsync(ctx->x, x_in, (size_t)M * H * 4, hipMemcpyDeviceToDevice, ctx->st));
+  NormArgs n0{};
+  n0.mode = 2; n0.rows = M; n0.H = H; n0.k = c.top_k; n0.eps = c.rms_eps;
+  n0.x = ctx->x; n0.w_out = ctx->L[0].norm[0]; n0.out = ctx->a;
+  HIPX(launch_residual_norm(ctx->bf16, n0, ctx->st));
+  TRY(enqueue_layers(ctx, batch, nullptr));
+  HIPX(hipMemcpyAsync(x_out, ctx->x, (size_t)M * H * 4, hipMemcpyDeviceToDevice, ctx->st));
+  return DG_OK;
+}
+
+dg_status dg_set_trace(dg_ctx* ctx, int32_t* route_idx) {
+  TRY(enter(ctx));
+  ctx->trace = route_idx;
+  return DG_OK;
+}
+
+// ---- single kernels --------------------------------------------------------
+
+dg_status dg_k_argmax_conf(const float* logits, int32_t rows, int32_t vocab, int32_t* pred, float* conf,
+                           void* stream) {
+  dg_ctx* ctx = nullptr;
+  if (rows < 0 || vocab <= 0 || vocab % 4) return fail(ctx, DG_EINVAL, "rows >= 0 and vocab a positive multiple of 4 required");
+  if (rows == 0) return DG_OK;  // nothing to do; pointers may be NULL
+  if (!logits || !pred || !conf) return fail(ctx, DG_EINVAL, "logits, pred and conf are required");
+  HIPX(launch_argmax_conf(logits, rows, vocab, pred, conf, reinterpret_cast<hipStream_t>(stream)));
+  return DG_OK;
+}
+
+dg_status dg_k_lock_select(int32_t batch, int32_t n, const float* conf, const int32_t* pred, int32_t* tokens,
+                           uint8_t* locked, const int32_t* steps_left_host, void* stream) {
+  dg_ctx* ctx = nullptr;
+  if (!conf || !pred || !tokens || !locked || !steps_left_host)
+    return fail(ctx, DG_EINVAL, "conf, pred, tokens, locked and steps_left are required");
+  if (batch < 0 || batch > DG_MAX_BATCH || n < 1 || n > 4096)
+    return fail(ctx, DG_EINVAL, "batch must be in [0, 64] and n in [1, 4096]");
+  StepsArg steps{};
+  for (int b = 0; b < batch; ++b) {
+    if (steps_left_host[b] < 1) return fail(ctx, DG_EINVAL, "steps_left[%d] < 1", b);
+    steps.v[b] = steps_left_host[b];
+  }
+  HIPX(launch_lock_select(batch, n, conf, pred, tokens, locked, steps, reinterpret_cast<hipStream_t>(stream)));
+  return DG_OK;
+}
+
+dg_status dg_k_moe_route(const float* logits, int32_t rows, int32_t n_experts, int32_t top_k, int32_t* idx,
+                         float* gates, int32_t* counts, int32_t* offsets, int32_t* perm, void* stream) {
+  dg_ctx* ctx = nullptr;
+  if (!logits || !idx || !gates) return fail(ctx, DG_EINVAL, "logits, idx and gates are required");
+  if (rows < 1 || rows > 4096 || n_experts < 1 || n_experts > 256 || top_k < 1 || top_k > 8 ||
+      top_k > n_experts)
+    return fail(ctx, DG_EINVAL, "rows in [1, 4096], E in [1, 256], k in [1, min(8, E)] required");
+  if ((long long)n_experts * ((rows + 31) / 32) > 16384)
+    return fail(ctx, DG_EINVAL, "E * ceil(rows / 32) must be <= 16384");
+  HIPX(launch_moe_route(logits, rows, n_experts, top_k, idx, gates, counts, offsets, perm, nullptr,
+                        reinterpret_cast<hipStream_t>(stream)));
+  return DG_OK;
+}
+
+dg_status dg_k_qkv(dg_ctx* ctx, int32_t layer, int32_t batch, const void* a, void* q, void* k, void* v) {
+  TRY(enter(ctx));
+  const dg_config& c = ctx->c;
+  if (layer < 0 || layer >= c.n_layers || !ctx->L[layer].set) return fail(ctx, DG_ESTATE, "layer %d not loaded", layer);
+  if (batch < 1 || batch > c.max_batch) return fail(ctx, DG_EINVAL, "batch out of range");
+  if (!a || !q || !k || !v) return fail(ctx, DG_EINVAL, "a, q, k, v are required");
+  TRY(check_slots(ctx, batch));
+  const long long N = c.canvas_len, D = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads;
+  const long long qs[4] = {N * Hq * D, D, Hq * D, 1};
+  const long long ks[4] = {N * Hkv * D, D, Hkv * D, 1};
+  return enqueue_qkv(ctx, layer, batch, a, q, k, v, qs, ks, ks);
+}
+
+dg_status dg_k_canvas_attn(dg_ctx* ctx, int32_t layer, int32_t batch, const void* q, const void* k, const void* v,
+                           void* o, int32_t canvas_keys) {
+  TRY(enter(ctx));
+  const dg_config& c = ctx->c;
+  if (layer < 0 || layer >= c.n_layers) return fail(ctx, DG_EINVAL, "layer out of range");
+  if (batch < 1 || batch > c.max_batch) return fail(ctx, DG_EINVAL, "batch out of range");
+  if (!q || !k || !v || !o) return fail(ctx, DG_EINVAL, "q, k, v, o are required");
+  TRY(check_slots(ctx, batch));
+  const int N = c.canvas_len, D = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads;
+  {
+    const int n[4] = {batch, Hq, N, D};
+    const long long ss[4] = {(long long)N * Hq * D, D, (long long)Hq * D, 1};
+    const long long ds[4] = {(long long)Hq * N * D, (long long)N * D, D, 1};
+    HIPX(launch_permute4(ctx->bf16, q, ctx->q, n, ss, ds, ctx->st));
+  }
+  {
+    const int n[4] = {batch, Hkv, N, D};
+    const long long ss[4] = {(long long)N * Hkv * D, D, (long long)Hkv * D, 1};
+    const long long dk[4] = {(long long)Hkv * N * D, (long long)N * D, D, 1};
+    const long long dv[4] = {(long long)Hkv * D * N, (long long)D * N, 1, N};
+    HIPX(launch_permute4(ctx->bf16, k, ctx->kc, n, ss, dk, ctx->st));
+    HIPX(launch_permute4(ctx->bf16, v, ctx->vc, n, ss, dv, ctx->st));
+  }
+  return enqueue_attention(ctx, layer, batch, o, canvas_keys ? 1 : 0);
+}
+
+dg_status dg_k_moe_ffn(dg_ctx* ctx, int32_t layer, int32_t batch, const void* f, const int32_t* idx,
+                       const float* gates, float* m) {
+  TRY(enter(ctx));
+  const dg_config& c = ctx->c;
+  if (layer < 0 || layer >= c.n_layers || !ctx->L[layer].set) return fail(ctx, DG_ESTATE, "layer %d not loaded", layer);
+  if (batch < 1 || batch > c.max_batch) return fail(ctx, DG_EINVAL, "batch out of range");
+  if (!f || !idx || !gates || !m) return fail(ctx, DG_EINVAL, "f, idx, gates, m are required");
+  const int M = batch * c.canvas_len, K = c.top_k, H = c.hidden;
+  HIPX(hipMemcpyAsync(ctx->idx, idx, (size_t)M * K * 4, hipMemcpyDeviceToDevice, ctx->st));
+  HIPX(hipMemcpyAsync(ctx->gates, gates, (size_t)M * K * 4, hipMemcpyDeviceToDevice, ctx->st));
+  HIPX(launch_moe_route(nullptr, M, c.n_experts, K, ctx->idx, ctx->gates, nullptr, ctx->offsets, ctx->perm,
+                        ctx->arows, ctx->st));
+  TRY(enqueue_experts(ctx, layer, M, f));
+  HIPX(hipMemsetAsync(m, 0, (size_t)M * H * 4, ctx->st));
+  NormArgs nc{};
+  nc.mode = 1; nc.rows = M; nc.H = H; nc.k = K; nc.eps = c.rms_eps;
+  nc.x = m; nc.delta = ctx->y; nc.w_delta = nullptr; nc.w_out = nullptr;
+  HIPX(launch_residual_norm(ctx->bf16, nc, ctx->st));
+  return DG_OK;
+}
+
+dg_status dg_k_lm_head(dg_ctx* ctx, int32_t batch, const void* h, float* logits) {
+  TRY(enter(ctx));
+  const dg_config& c = ctx->c;
+  if (!c.has_lm_head || !ctx->embed_set) return fail(ctx, DG_ESTATE, "embedding not loaded");
+  if (batch < 1 || batch > c.max_batch) return fail(ctx, DG_EINVAL, "batch out of range");
+  if (!h || !logits) return fail(ctx, DG_EINVAL, "h and logits are required");
+  return enqueue_dense(ctx, h, c.hidden, ctx->embed, c.hidden, c.vocab, batch * c.canvas_len, logits, c.vocab);
+}
+
+}  // extern "C"

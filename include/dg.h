@@ -1,0 +1,230 @@
+/*
+ * dg.h -- C ABI of the MI355X (gfx950) canvas-denoising library.
+ *
+ * The library runs the hot path of DiffusionGemma-style text diffusion: a
+ * canvas of placeholder tokens is refined over a fixed number of parallel
+ * denoise passes; each pass runs a decoder stack over every canvas position
+ * at once and locks the most confident predictions, which stay fixed as
+ * context for the following passes.  Sources (page title, section):
+ *
+ *   [4xFaster]     "DiffusionGemma: The Diffusion Era Begins with 4x Faster
+ *                  Text Generation" -- "What is Diffusion and Why is it
+ *                  Coming to Text Generation Now?" (canvas of random
+ *                  placeholder tokens; locked tokens serve as context) and
+ *                  "DiffusionGemma's Technical Architecture" (canvas 256,
+ *                  128 experts with 8 active + 1 shared, sliding window 1024,
+ *                  encoder KV cache read by the decoder through
+ *                  cross-attention, bidirectional attention over the canvas).
+ *   [HandsOn]      "Hands-On with Diffusion Gemma: Another Gemma with a
+ *                  Diffusion Mechanism" -- "Detailed Specs" (local/global
+ *                  layer pattern, GELU-tanh gated MLP, norm layers, tied
+ *                  embedding and LM head, RoPE and p-RoPE, KV cache bridge).
+ *   [ParadigmShift] "DiffusionGemma: Exploring the Paradigm Shift in
+ *                  Non-Autoregressive Language Modeling" -- "Analysis of
+ *                  Implications" (uncertain tokens are re-noised).
+ *   [Experimental] "DiffusionGemma: Google's Experimental Diffusion LLM" --
+ *                  "How Text Diffusion Actually Works" (a small fixed number
+ *                  of passes per block).
+ *
+ * Conventions for every call:
+ *   - All device pointers are plain HIP device addresses on the context's
+ *     device; host pointers are marked "host".  No call takes ownership of a
+ *     caller buffer.
+ *   - Work is enqueued asynchronously on the stream given to dg_create (0 =
+ *     the null stream); the caller synchronises before reading outputs.
+ *   - Arguments are validated before anything is enqueued; on an error
+ *     nothing is enqueued, output buffers are untouched and the status is
+ *     returned.  A HIP error reported by the runtime (including an
+ *     asynchronous fault of an earlier call) is returned as DG_EHIP.
+ *   - dg_last_error() gives a message for the context's last error.
+ *   - A context is not thread-safe: one host thread at a time.
+ *   - bf16 values are raw 16-bit patterns (upper half of an IEEE float32);
+ *     "T" below is float for DG_F32 contexts and bf16 for DG_BF16 contexts.
+ *   - Weight matrices use the math layout y = x @ W with W row-major
+ *     [in, out].
+ */
+#ifndef DG_H
+#define DG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dg_status {
+  DG_OK = 0,
+  DG_EINVAL = -1,       /* bad argument (null pointer, size out of range) */
+  DG_ENOMEM = -2,       /* device allocation failed */
+  DG_EHIP = -3,         /* HIP runtime error */
+  DG_ESTATE = -4,       /* call not valid in the context's state */
+  DG_EUNSUPPORTED = -5  /* shape or dtype this build does not handle */
+} dg_status;
+
+typedef enum dg_dtype { DG_F32 = 0, DG_BF16 = 1 } dg_dtype;
+
+/* Architecture and capacity of a context. */
+typedef struct dg_config {
+  int32_t n_layers;       /* decoder layers (<= 64) */
+  int32_t hidden;         /* H, multiple of 32 */
+  int32_t n_heads;        /* query heads Hq */
+  int32_t n_kv_heads;     /* KV heads Hkv; Hq % Hkv == 0 (grouped-query attention) */
+  int32_t head_dim;       /* D, multiple of 32, <= 256 */
+  int32_t n_experts;      /* routed experts E, multiple of 16, <= 256 */
+  int32_t top_k;          /* active routed experts per token, 1..8 */
+  int32_t n_shared;       /* always-on shared experts; must be 1 */
+  int32_t expert_ffn;     /* F, multiple of 32 */
+  int32_t vocab;          /* V, multiple of 16 (0 allowed when has_lm_head == 0) */
+  int32_t canvas_len;     /* N, canvas slots per canvas, multiple of 16 */
+  int32_t window;         /* sliding window of local layers (prompt positions) */
+  int32_t max_batch;      /* canvases per call, 1..64, max_batch*canvas_len <= 4096 */
+  int32_t max_prompt_len; /* largest prompt KV length of any slot */
+  uint64_t global_layer_mask; /* bit l set: layer l is global (GQA over the whole
+                                 prompt, p-RoPE); clear: sliding window, RoPE */
+  float rope_theta;       /* RoPE base */
+  float prope_frac;       /* fraction of rotary pairs p-RoPE rotates on global layers */
+  float rms_eps;          /* RMSNorm epsilon */
+  int32_t dtype;          /* dg_dtype of weights, KV and stored activations */
+  int32_t has_lm_head;    /* 0: decoder layers only (dg_forward_hidden) */
+  int32_t post_ffn_norm;  /* 1: normalise the MoE output before the residual add */
+} dg_config;
+
+/* One decoder layer's weights (caller-owned device pointers, dtype T).
+ * Shapes: wq [H, Hq*D]; wk, wv [H, Hkv*D]; wo [Hq*D, H]; router [H, E];
+ * w_gate, w_up [E, H, F]; w_down [E, F, H]; sh_gate, sh_up [H, F];
+ * sh_down [F, H]; norm_in, norm_pa, norm_pf, norm_pf2 [H] (used as 1 + w). */
+typedef struct dg_layer_weights {
+  const void *wq, *wk, *wv, *wo, *router;
+  const void *w_gate, *w_up, *w_down;
+  const void *sh_gate, *sh_up, *sh_down;
+  const void *norm_in, *norm_pa, *norm_pf, *norm_pf2;
+} dg_layer_weights;
+
+typedef struct dg_ctx dg_ctx;
+
+/* Create a context on `device` (its current HIP device is set on every call)
+ * enqueuing on `hip_stream` (a hipStream_t, may be NULL).  Allocates the
+ * workspaces for max_batch canvases.  *out is NULL on failure. */
+dg_status dg_create(const dg_config* cfg, int32_t device, void* hip_stream, dg_ctx** out);
+
+/* Synchronise the context's stream and free everything the context owns.
+ * NULL is accepted. */
+dg_status dg_destroy(dg_ctx* ctx);
+
+/* Message of the last error of `ctx` (NULL: the last dg_create failure).
+ * The string stays valid until the next call on the context. */
+const char* dg_last_error(const dg_ctx* ctx);
+
+/* Copy one layer's weights into library-owned storage, repacked into the
+ * layout of the matrix-core kernels.  The caller may free its buffers once
+ * the stream has passed this call. */
+dg_status dg_set_layer_weights(dg_ctx* ctx, int32_t layer, const dg_layer_weights* w);
+
+/* Copy the embedding [V, H] (also the tied LM head, [HandsOn] "Detailed
+ * Specs", weight sharing) and the final norm weight [H]. */
+dg_status dg_set_embedding(dg_ctx* ctx, const void* embed, const void* norm_final);
+
+/* All weights at once: `layers` is a host array of n_layers entries; embed
+ * and norm_final may be NULL when has_lm_head == 0. */
+dg_status dg_init_weights(dg_ctx* ctx, const void* embed, const void* norm_final,
+                          const dg_layer_weights* layers);
+
+/* Load the cached prompt KV of canvas slot `slot` (0 <= slot < max_batch),
+ * the encoder's KV cache read by the decoder ([4xFaster] "DiffusionGemma's
+ * Technical Architecture").  k[l], v[l] (host arrays of n_layers device
+ * pointers) are [len_l, Hkv, D] of dtype T with len_l = prompt_len on global
+ * layers and min(prompt_len, window) -- the last positions -- on local
+ * layers.  K is already position-encoded.  The canvas of this slot sits at
+ * positions prompt_len + i.  0 <= prompt_len <= max_prompt_len. */
+dg_status dg_load_prompt_kv(dg_ctx* ctx, int32_t slot, int32_t prompt_len,
+                            const void* const* k, const void* const* v);
+
+/* One denoise pass over canvases 0..batch-1: embed, decoder stack, final
+ * norm, tied LM head, per-position argmax and confidence (softmax
+ * probability of the argmax), then per canvas lock the
+ * ceil(remaining / steps_left[b]) unlocked positions of highest confidence
+ * (ties to the lower position): they take their predicted token and become
+ * locked; the others keep their placeholder ([4xFaster] "What is
+ * Diffusion...", [ParadigmShift] "Analysis of Implications").
+ *   tokens  int32 [batch, N] device, in/out
+ *   locked  uint8 [batch, N] device, in/out (1 = locked)
+ *   steps_left_host  int32 [batch] host, each >= 1
+ *   conf_out float [batch, N] device or NULL; pred_out int32 [batch, N] or NULL
+ * Requires all weights and the prompt KV of slots 0..batch-1. */
+dg_status dg_denoise_step(dg_ctx* ctx, int32_t batch, int32_t* tokens, uint8_t* locked,
+                          const int32_t* steps_left_host, float* conf_out, int32_t* pred_out);
+
+/* n_steps passes, pass t with steps_left = n_steps - t for every canvas, so
+ * every position is locked at the end ([Experimental] "How Text Diffusion
+ * Actually Works").  No host synchronisation inside. */
+dg_status dg_generate_block(dg_ctx* ctx, int32_t batch, int32_t n_steps, int32_t* tokens,
+                            uint8_t* locked);
+
+/* Decoder layers only on a given residual stream: x_in, x_out float
+ * [batch*N, H] device (may alias).  Prompt KV of slots 0..batch-1 required. */
+dg_status dg_forward_hidden(dg_ctx* ctx, int32_t batch, const float* x_in, float* x_out);
+
+/* Record every pass's expert choice: route_idx int32 [n_layers, batch*N,
+ * top_k] device (slot order: logit descending, index ascending), written by
+ * each following dg_denoise_step / dg_forward_hidden (a block overwrites it
+ * per pass).  NULL switches recording off. */
+dg_status dg_set_trace(dg_ctx* ctx, int32_t* route_idx);
+
+/* ---- single-kernel entry points (same kernels as the pass) ---------------- */
+
+/* Per-row argmax (lowest index among equal maxima) and confidence
+ * 1 / sum_v exp(l_v - l_max) of float logits [rows, vocab] ([HandsOn]
+ * "Detailed Specs": the probability distribution judges which tokens are
+ * final).  pred int32 [rows], conf float [rows] (rows == 0: nothing is done
+ * and the pointers may be NULL).  vocab % 4 == 0.  `stream` may be NULL. */
+dg_status dg_k_argmax_conf(const float* logits, int32_t rows, int32_t vocab, int32_t* pred,
+                           float* conf, void* stream);
+
+/* Lock-and-remask step alone (see dg_denoise_step) on given conf/pred
+ * [batch, n]; steps_left_host host [batch] (>= 1); batch <= 64, n <= 4096. */
+dg_status dg_k_lock_select(int32_t batch, int32_t n, const float* conf, const int32_t* pred,
+                           int32_t* tokens, uint8_t* locked, const int32_t* steps_left_host,
+                           void* stream);
+
+/* Top-k routing on float router logits [rows, E] ([4xFaster] "DiffusionGemma's
+ * Technical Architecture": 8 of 128 experts active): idx int32 [rows, k]
+ * ordered (logit desc, expert asc); gates float [rows, k] = softmax over the
+ * k kept logits; counts int32 [E]; offsets int32 [E + 2] (expert e's rows
+ * are [offsets[e], offsets[e+1]), offsets[E] = rows*k, offsets[E+1] =
+ * rows*k + rows for the shared expert); perm int32 [rows*k] = t*k + s of
+ * each routed row, tokens ascending within an expert.  Any of counts,
+ * offsets, perm may be NULL.  rows <= 4096, E <= 256, k <= 8,
+ * E * ceil(rows / 32) <= 16384. */
+dg_status dg_k_moe_route(const float* logits, int32_t rows, int32_t n_experts, int32_t top_k,
+                         int32_t* idx, float* gates, int32_t* counts, int32_t* offsets,
+                         int32_t* perm, void* stream);
+
+/* q/k/v projections with RoPE (p-RoPE on global layers) of layer `layer`:
+ * a T [batch*N, H] -> q T [batch, N, Hq, D], k, v T [batch, N, Hkv, D],
+ * positions prompt_len(slot b) + i. */
+dg_status dg_k_qkv(dg_ctx* ctx, int32_t layer, int32_t batch, const void* a, void* q, void* k,
+                   void* v);
+
+/* Attention of layer `layer` for canvases 0..batch-1: one softmax over the
+ * keys [prompt KV visible to the layer ; canvas keys] (canvas keys left out
+ * when canvas_keys == 0), grouped-query heads, no causal mask.  q T [batch,
+ * N, Hq, D], k, v T [batch, N, Hkv, D] -> o T [batch, N, Hq*D]. */
+dg_status dg_k_canvas_attn(dg_ctx* ctx, int32_t layer, int32_t batch, const void* q,
+                           const void* k, const void* v, void* o, int32_t canvas_keys);
+
+/* Routed MoE of layer `layer` with given routing: f T [batch*N, H], idx
+ * int32 [batch*N, k], gates float [batch*N, k] -> m float [batch*N, H] =
+ * sum_s gates[t,s] * FFN_idx[t,s](f_t) + FFN_shared(f_t), with
+ * FFN(z) = (gelu_tanh(z Wg) * (z Wu)) Wd and the gated activation stored as
+ * T ([HandsOn] "Detailed Specs": GELU-tanh gated MLP). */
+dg_status dg_k_moe_ffn(dg_ctx* ctx, int32_t layer, int32_t batch, const void* f,
+                       const int32_t* idx, const float* gates, float* m);
+
+/* Tied LM head: h T [batch*N, H] -> logits float [batch*N, V] = h @ embed^T. */
+dg_status dg_k_lm_head(dg_ctx* ctx, int32_t batch, const void* h, float* logits);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DG_H */

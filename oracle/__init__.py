@@ -32,7 +32,7 @@ are pinned only through those per-step pins: the pages print no worked
 example of a pass.
 """
 from .model import (  # noqa: F401
-    OracleWeights, argmax_conf, attention_heads, bf16_bits_to_f64, bf16_round,
+    OracleWeights, argmax_conf, attention_heads, canvas_attention, qkv_rope, Shadow, forward_hidden, bf16_bits_to_f64, bf16_round,
     denoise_pass, expert_ffn, gelu_tanh, generate_block, layer_forward, lm_logits,
     lock_count, lock_select, moe_block, rmsnorm, rope, route, softmax_attention,
 )

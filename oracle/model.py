@@ -352,6 +352,50 @@ def _shadow_route(sh: Shadow, layer: int):
 # --------------------------------------------------------------------------
 
 
+def qkv_rope(a: np.ndarray, lw: Dict[str, np.ndarray], cfg, layer: int,
+             prompt_lens: Sequence[int], rnd: Callable[[np.ndarray], np.ndarray]):
+    """q/k/v projections of the normalised input ``a [B*N, H]`` with RoPE at
+    canvas positions ``prompt_len + i`` (p-RoPE on global layers), rounded to
+    the storage format.  Returns ``q [B, N, Hq, D]``, ``k, v [B, N, Hkv, D]``."""
+    N = cfg.canvas_len
+    B = len(prompt_lens)
+    D, Hq, Hkv = cfg.head_dim, cfg.n_heads, cfg.n_kv_heads
+    n_rot = int(cfg.prope_frac * (D // 2)) if cfg.is_global(layer) else D // 2
+    q = a @ lw["wq"]
+    k = a @ lw["wk"]
+    v = a @ lw["wv"]
+    qs, ks, vs = [], [], []
+    for b in range(B):
+        rows = slice(b * N, (b + 1) * N)
+        pos = prompt_lens[b] + np.arange(N)
+        qs.append(rnd(rope(q[rows].reshape(N, Hq, D), pos, cfg.rope_theta, n_rot)))
+        ks.append(rnd(rope(k[rows].reshape(N, Hkv, D), pos, cfg.rope_theta, n_rot)))
+        vs.append(rnd(v[rows].reshape(N, Hkv, D)))
+    return np.stack(qs), np.stack(ks), np.stack(vs)
+
+
+def canvas_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                     prompt_kv: Sequence[Tuple[np.ndarray, np.ndarray]],
+                     rnd: Callable[[np.ndarray], np.ndarray], canvas_keys: bool = True) -> np.ndarray:
+    """One softmax per canvas query over the keys [prompt KV ; all canvas
+    positions]: the canvas attends to itself bidirectionally and to the
+    cached prompt context ([4xFaster] "DiffusionGemma's Technical
+    Architecture").  ``q [B, N, Hq, D]``; ``k, v [B, N, Hkv, D]``;
+    ``prompt_kv[b] = (K, V)`` each ``[len, Hkv, D]``.  Returns ``o [B*N, Hq*D]``
+    rounded to the storage format."""
+    B, N, Hq, D = q.shape
+    o = np.empty((B * N, Hq * D))
+    for b in range(B):
+        Kp, Vp = prompt_kv[b]
+        if canvas_keys:
+            keys = np.concatenate([Kp, k[b]], axis=0)
+            vals = np.concatenate([Vp, v[b]], axis=0)
+        else:
+            keys, vals = Kp, Vp
+        o[b * N:(b + 1) * N] = rnd(attention_heads(q[b], keys, vals)).reshape(N, Hq * D)
+    return o
+
+
 def layer_forward(x: np.ndarray, lw: Dict[str, np.ndarray], cfg, layer: int,
                   prompt_kv: Sequence[Tuple[np.ndarray, np.ndarray]],
                   prompt_lens: Sequence[int], rnd: Callable[[np.ndarray], np.ndarray],
@@ -368,42 +412,19 @@ def layer_forward(x: np.ndarray, lw: Dict[str, np.ndarray], cfg, layer: int,
       1. a = RMSNorm(x) (input_layernorm), stored as bf16 in bf16 workloads;
       2. q, k, v = a @ Wq, a @ Wk, a @ Wv; RoPE at canvas positions
          ``prompt_len + i`` (p-RoPE on global layers);
-      3. one softmax over the keys [prompt KV ; all canvas positions]: the
-         canvas attends to itself bidirectionally and to the cached prompt
-         context ([4xFaster] "DiffusionGemma's Technical Architecture":
-         bidirectional attention over the canvas plus cross-attention into the
-         encoder's KV cache, with q/k/v/o shared between encoder and decoder,
-         [HandsOn] "Detailed Specs");
+      3. one softmax over the keys [prompt KV ; all canvas positions]
+         (bidirectional canvas attention plus the encoder's cached context,
+         with q/k/v/o shared between encoder and decoder, [HandsOn] "Detailed
+         Specs");
       4. x += RMSNorm(o @ Wo) (post_attention_layernorm);
       5. f = RMSNorm(x) (pre_feedforward_layernorm);
       6. m = routed top-k MoE + shared expert;
       7. x += RMSNorm(m) (post-FFN norm; plain x += m when disabled).
     """
-    N = cfg.canvas_len
-    B = len(prompt_lens)
-    D, Hq, Hkv = cfg.head_dim, cfg.n_heads, cfg.n_kv_heads
-    g_layer = cfg.is_global(layer)
-    n_rot = int(cfg.prope_frac * (D // 2)) if g_layer else D // 2
     eps = cfg.rms_eps
-
     a = rnd(rmsnorm(x, lw["norm_in"], eps))
-    q = a @ lw["wq"]
-    k = a @ lw["wk"]
-    v = a @ lw["wv"]
-    o = np.empty((B * N, Hq * D))
-    for b in range(B):
-        rows = slice(b * N, (b + 1) * N)
-        pos = prompt_lens[b] + np.arange(N)
-        qb = rnd(rope(q[rows].reshape(N, Hq, D), pos, cfg.rope_theta, n_rot))
-        kb = rnd(rope(k[rows].reshape(N, Hkv, D), pos, cfg.rope_theta, n_rot))
-        vb = rnd(v[rows].reshape(N, Hkv, D))
-        Kp, Vp = prompt_kv[b]
-        if canvas_keys:
-            keys = np.concatenate([Kp, kb], axis=0)
-            vals = np.concatenate([Vp, vb], axis=0)
-        else:
-            keys, vals = Kp, Vp
-        o[rows] = rnd(attention_heads(qb, keys, vals)).reshape(N, Hq * D)
+    q, k, v = qkv_rope(a, lw, cfg, layer, prompt_lens, rnd)
+    o = canvas_attention(q, k, v, prompt_kv, rnd, canvas_keys)
     x = x + rmsnorm(o @ lw["wo"], lw["norm_pa"], eps)
     f = rnd(rmsnorm(x, lw["norm_pf"], eps))
     m, r, idx, gates = moe_block(f, lw, cfg.top_k, rnd, route_override)
