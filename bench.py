@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Throughput of the canvas denoise pass on one MI355X.
+
+A step is one denoise pass of the whole hot path (embed, 30 decoder layers
+with canvas attention + prompt-KV attention and the routed MoE, final norm,
+tied LM head, argmax/confidence, lock-and-remask) over one batch of seeded
+synthetic input: random-init bf16 weights (N(0, 0.02)), N(0, 1) prompt KV and
+a uniformly drawn canvas.  Steps walk through the block's pass schedule
+(steps_left = T, T-1, ..., 1) and restart it with a fresh canvas every T
+passes, so every lock count of a block is exercised.
+
+Prints one JSON line: canvas tokens/s per pass as ``value``, the resolved
+tokens/s of whole blocks, the roofline of the dominant kernel (the grouped
+gate|up expert GEMM, timed with HIP events on the library's stream) and the
+CPU oracle's rate on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+
+METRIC = "canvas tokens/sec per denoise pass; resolved tok/s (30-layer bf16, 1 MI355X)"
+
+
+def algorithmic(w, touched):
+    """Algorithmic HBM bytes and flops of one pass and of one gate|up launch.
+
+    ``touched[l]`` is the number of routed experts that received a token in
+    layer l (weights of untouched experts need not be read)."""
+    m = w.model
+    M = w.batch * m.canvas_len
+    H, D, F, E, K, V = m.hidden, m.head_dim, m.expert_ffn, m.n_experts, m.top_k, m.vocab
+    qd, kvd = m.n_heads * D, m.n_kv_heads * D
+    es = 2 if m.dtype == "bf16" else 4
+    byts = flops = 0.0
+    gu_bytes = []
+    for l in range(m.n_layers):
+        Lw = m.kv_len(l, w.prompt_len)
+        attn_w = (H * (qd + 2 * kvd) + qd * H + H * E) * es
+        ex = (touched[l] + 1) * 3 * H * F * es
+        kv = w.batch * Lw * kvd * 2 * es
+        norms = 4 * H * es
+        byts += attn_w + ex + kv + norms
+        gu_bytes.append((touched[l] + 1) * 2 * H * F * es + M * H * es + (M * K + M) * F * es)
+        flops += 2.0 * M * (H * (qd + 2 * kvd) + qd * H + H * E + (K + 1) * 3 * H * F)
+        flops += 4.0 * M * m.n_heads * D * (Lw + m.canvas_len)
+    if m.has_lm_head:
+        byts += V * H * es + H * es + M * H * es
+        flops += 2.0 * M * H * V
+    gu_flops = 2.0 * (M * K + M) * H * 2 * F
+    return byts, flops, sum(gu_bytes) / len(gu_bytes), gu_flops
+
+
+def cpu_baseline(w, max_rows_head: int = 64):
+    """The oracle (float64 numpy) timed on a bounded sample of the workload:
+    the first group of layers up to and including the first global layer
+    (five sliding-window layers and one global layer in the 30-layer stack),
+    run in sequence over the whole canvas, and the LM head + argmax for
+    ``max_rows_head`` positions; the pass time is extrapolated to the full
+    stack and canvas (weight generation is not timed)."""
+    import numpy as np
+    from oracle import model as om
+    from oracle.inputs import prompt_kv_fn, weights_for
+    from synth import gen
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    m = w.model
+    M = w.batch * m.canvas_len
+    W = weights_for(w)
+    kvf = prompt_kv_fn(w)
+    tok, _ = gen.canvas(w)
+    x = W.embed_rows(tok.reshape(-1).astype(np.int64))
+    g_layer = next(l for l in range(m.n_layers) if m.is_global(l))
+    group = list(range(g_layer + 1))
+    t_layers = 0.0
+    for l in group:
+        lw = W.layer(l)
+        kv = [kvf(l, b) for b in range(w.batch)]
+        t0 = time.perf_counter()
+        x, _ = om.layer_forward(x, lw, m, l, kv, [w.prompt_len] * w.batch, om.bf16_round)
+        t_layers += time.perf_counter() - t0
+        del lw
+    E = W.embed()
+    rows = min(max_rows_head, M)
+    h = om.bf16_round(om.rmsnorm(x[:rows], W.norm_final(), m.rms_eps))
+    t0 = time.perf_counter()
+    om.argmax_conf(om.lm_logits(h, E))
+    t_head = time.perf_counter() - t0
+    est = t_layers * m.n_layers / len(group) + t_head * M / rows
+    sample = (f"oracle float64 on {cores} BLAS threads: layers 0-{g_layer} ({len(group) - 1} sliding-window "
+              f"+ 1 global) over all {M} canvas positions in {t_layers:.2f} s and the LM head + argmax "
+              f"for {rows} positions in {t_head:.2f} s; pass time extrapolated to {m.n_layers} layers "
+              f"and {M} positions = {est:.1f} s")
+    return {"value": M / est, "unit": "canvas tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": sample}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=24)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--workload", default="C3", help="C1..C5 (default C3: the 30-layer bf16 stack)")
+    ap.add_argument("--blocks", type=int, default=2, help="whole blocks timed for resolved tok/s")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path: independent canvases shard with no exchange, see the design notes.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import canvas_denoising_moe_amd as dg
+    from canvas_denoising_moe_amd import binding as bd
+    from synth import BY_ID, gen, upload
+
+    w = BY_ID[args.workload]
+    m = w.model
+    B, N, T = w.batch, m.canvas_len, w.n_steps
+    M = B * N
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    t0 = time.perf_counter()
+    ctx = dg.Context(m, max_batch=B, max_prompt_len=w.prompt_len, device=0)
+    upload.load_context(ctx, w)
+    torch.cuda.synchronize()
+    init_s = time.perf_counter() - t0
+    print(f"[bench] {w.name}: weights and prompt KV loaded in {init_s:.1f} s", file=sys.stderr, flush=True)
+
+    tok0, lk0 = gen.canvas(w)
+    tok0_d = torch.from_numpy(tok0).to(dev)
+    lk0_d = torch.from_numpy(lk0).to(dev)
+    tokens = tok0_d.clone()
+    locked = lk0_d.clone()
+
+    # routing of one pass: experts that received tokens per layer
+    trace = torch.empty((m.n_layers, M, m.top_k), dtype=torch.int32, device=dev)
+    ctx.set_trace(trace)
+    ctx.denoise_step(tokens, locked, [T] * B)
+    torch.cuda.synchronize()
+    ctx.set_trace(None)
+    tr = trace.cpu().numpy()
+    touched = [int(np.unique(tr[l]).size) for l in range(m.n_layers)]
+
+    def step(i):
+        s = i % T
+        if s == 0:
+            tokens.copy_(tok0_d)
+            locked.copy_(lk0_d)
+        ctx.denoise_step(tokens, locked, [T - s] * B)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    ctx.profile(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ctx.profile(False)
+    prof = {k: ctx.profile_read(k) for k in (bd.PROF_GATE_UP, bd.PROF_DOWN, bd.PROF_ATTN,
+                                              bd.PROF_LM_HEAD, bd.PROF_PASS)}
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = M / (ms_per_step / 1e3)
+
+    # whole blocks (resolved tokens / block time), inputs restored outside the timing
+    block_ms = []
+    for _ in range(args.blocks):
+        tokens.copy_(tok0_d)
+        locked.copy_(lk0_d)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ctx.generate_block(tokens, locked, T)
+        torch.cuda.synchronize()
+        block_ms.append((time.perf_counter() - t0) * 1e3)
+        assert bool(locked.all()), "block left unlocked positions"
+    newly = int(M - lk0.sum())
+    block_med = float(np.median(block_ms))
+    resolved = newly / (block_med / 1e3)
+
+    byts, flops, gu_bytes, gu_flops = algorithmic(w, touched)
+    n_gu, ms_gu = prof[bd.PROF_GATE_UP]
+    gu_avg_s = ms_gu / n_gu / 1e3
+    achieved = gu_bytes / gu_avg_s / 1e9
+    pass_n, pass_ms = prof[bd.PROF_PASS]
+    pass_avg_ms = pass_ms / pass_n
+    kern = {}
+    for name, k in (("gate_up", bd.PROF_GATE_UP), ("down", bd.PROF_DOWN), ("attention", bd.PROF_ATTN),
+                    ("lm_head", bd.PROF_LM_HEAD)):
+        n, ms = prof[k]
+        kern[name] = {"launches": n, "avg_us": round(ms / n * 1e3, 2), "share_of_pass": round(ms / pass_ms, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "canvas tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if m.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded random-init weights N(0,0.02), prompt KV N(0,1), uniform canvas)",
+        "config": {"workload": w.name, "batch": B, "canvas_len": N, "layers": m.n_layers,
+                   "prompt_len": w.prompt_len, "passes_per_block": T, "experts": m.n_experts,
+                   "top_k": m.top_k, "vocab": m.vocab, "hidden": m.hidden},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "moe_grouped_gemm gate|up", "bytes_per_launch": int(gu_bytes),
+                     "avg_launch_us": round(gu_avg_s * 1e6, 2)},
+        "cpu_baseline": cpu,
+        "resolved_tok_s": round(resolved, 1),
+        "block_ms": round(block_med, 3),
+        "pass_ms_events": round(pass_avg_ms, 4),
+        "pass_roofline": {"bytes": int(byts), "flops": int(flops),
+                          "hbm_frac": round(byts / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "mfma_frac": round(flops / (ms_per_step / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+        "kernels": kern,
+        "experts_touched_min": min(touched),
+        "init_s": round(init_s, 1),
+    }
+    ctx.close()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

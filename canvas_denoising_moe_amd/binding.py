@@ -69,7 +69,11 @@ _SIGS = {
                                    c_int32]),
     "dg_k_moe_ffn": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
     "dg_k_lm_head": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p]),
+    "dg_profile": (c_int32, [c_void_p, c_int32]),
+    "dg_profile_read": (c_int32, [c_void_p, c_int32, POINTER(c_int32), POINTER(ctypes.c_double)]),
 }
+
+PROF_GATE_UP, PROF_DOWN, PROF_ATTN, PROF_LM_HEAD, PROF_PASS = range(5)
 
 
 def lib():
@@ -240,6 +244,17 @@ class Context:
         import torch
         self._keep = [route_idx]
         self._c(lib().dg_set_trace(self._h, _ptr(route_idx, torch.int32, "route_idx")))
+
+    # -- kernel timing -------------------------------------------------------------
+    def profile(self, enable: bool):
+        self._c(lib().dg_profile(self._h, int(bool(enable))))
+
+    def profile_read(self, kernel: int):
+        """(launches, total milliseconds) recorded for a kernel class."""
+        n = c_int32()
+        ms = ctypes.c_double()
+        self._c(lib().dg_profile_read(self._h, kernel, ctypes.byref(n), ctypes.byref(ms)))
+        return n.value, ms.value
 
     # -- single kernels ----------------------------------------------------------
     def k_qkv(self, layer: int, batch: int, a, q, k, v):

@@ -56,6 +56,11 @@ struct dg_ctx {
   int32_t* trace = nullptr;
   std::string err;
   std::vector<void*> owned;
+  // kernel timing: event pairs per kernel class (pool reused after a reset)
+  bool prof = false;
+  std::vector<hipEvent_t> ev_pool;
+  size_t ev_used = 0;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> prof_rec[DG_PROF_COUNT];
 };
 
 namespace {
@@ -107,6 +112,28 @@ template <typename P> dg_status dalloc_t(dg_ctx* ctx, P** p, size_t bytes) {
   dg_status s = dalloc(ctx, &v, bytes);
   *p = reinterpret_cast<P*>(v);
   return s;
+}
+
+// ---- kernel timing (events on the context's stream) ------------------------
+hipEvent_t next_event(dg_ctx* ctx) {
+  if (ctx->ev_used == ctx->ev_pool.size()) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    ctx->ev_pool.push_back(e);
+  }
+  return ctx->ev_pool[ctx->ev_used++];
+}
+hipEvent_t prof_start(dg_ctx* ctx) {
+  if (!ctx->prof) return nullptr;
+  hipEvent_t e = next_event(ctx);
+  if (e && hipEventRecord(e, ctx->st) != hipSuccess) return nullptr;
+  return e;
+}
+void prof_stop(dg_ctx* ctx, int kind, hipEvent_t s) {
+  if (!s) return;
+  hipEvent_t e = next_event(ctx);
+  if (!e || hipEventRecord(e, ctx->st) != hipSuccess) return;
+  ctx->prof_rec[kind].push_back({s, e});
 }
 
 bool is_global(const dg_config& c, int l) { return (c.global_layer_mask >> l) & 1ull; }
@@ -244,7 +271,9 @@ dg_status enqueue_attention(dg_ctx* ctx, int l, int B, void* o, int canvas_keys)
     aa.vp[b] = ctx->slots[b].v[l];
     aa.lw[b] = ctx->slots[b].len[l];
   }
+  hipEvent_t ev = prof_start(ctx);
   HIPX(launch_attention(ctx->bf16, aa, ctx->st));
+  prof_stop(ctx, DG_PROF_ATTN, ev);
   return DG_OK;
 }
 
@@ -266,7 +295,9 @@ dg_status enqueue_experts(dg_ctx* ctx, int l, int M, const void* f) {
   g.group_off = ctx->offsets; g.n_groups = E;
   EpiArgs e{};
   e.kind = EPI_GEGLU; e.out = ctx->u; e.ldo = F;
+  hipEvent_t ev = prof_start(ctx);
   HIPX(launch_gemm(ctx->bf16, g, e, mt, ctx->st));
+  prof_stop(ctx, DG_PROF_GATE_UP, ev);
 
   GemmArgs d{};
   d.A = ctx->u; d.lda = F; d.a_rows = nullptr;
@@ -277,7 +308,9 @@ dg_status enqueue_experts(dg_ctx* ctx, int l, int M, const void* f) {
   EpiArgs ed{};
   ed.kind = EPI_DOWN; ed.out = ctx->y; ed.ldo = H;
   ed.slot = ctx->perm; ed.gates = ctx->gates; ed.routed_rows = M * K; ed.out_rows = M * K + M;
+  ev = prof_start(ctx);
   HIPX(launch_gemm(ctx->bf16, d, ed, mt, ctx->st));
+  prof_stop(ctx, DG_PROF_DOWN, ev);
   return DG_OK;
 }
 
@@ -336,7 +369,9 @@ dg_status enqueue_pass(dg_ctx* ctx, int B, int32_t* tokens, uint8_t* locked, con
   n0.x = ctx->x; n0.w_out = ctx->L[0].norm[0]; n0.out = ctx->a;
   HIPX(launch_residual_norm(ctx->bf16, n0, ctx->st));
   TRY(enqueue_layers(ctx, B, ctx->norm_final));
+  hipEvent_t ev = prof_start(ctx);
   TRY(enqueue_dense(ctx, ctx->a, H, ctx->embed, H, c.vocab, M, ctx->logits, c.vocab));
+  prof_stop(ctx, DG_PROF_LM_HEAD, ev);
   HIPX(launch_argmax_conf(ctx->logits, M, c.vocab, ctx->pred, ctx->conf, ctx->st));
   HIPX(launch_lock_select(B, N, ctx->conf, ctx->pred, tokens, locked, steps, ctx->st));
   return DG_OK;
@@ -386,6 +421,7 @@ dg_status dg_destroy(dg_ctx* ctx) {
   if (!ctx) return DG_OK;
   (void)hipSetDevice(ctx->dev);
   (void)hipStreamSynchronize(ctx->st);
+  for (hipEvent_t e : ctx->ev_pool) (void)hipEventDestroy(e);
   for (void* p : ctx->owned)
     if (p) (void)hipFree(p);
   delete ctx;
@@ -531,7 +567,9 @@ dg_status dg_denoise_step(dg_ctx* ctx, int32_t batch, int32_t* tokens, uint8_t* 
     if (steps_left_host[b] < 1) return fail(ctx, DG_EINVAL, "steps_left[%d] = %d < 1", b, steps_left_host[b]);
     steps.v[b] = steps_left_host[b];
   }
+  hipEvent_t evp = prof_start(ctx);
   TRY(enqueue_pass(ctx, batch, tokens, locked, steps));
+  prof_stop(ctx, DG_PROF_PASS, evp);
   const size_t M = (size_t)batch * c.canvas_len;
   if (conf_out) HIPX(hipMemcpyAsync(conf_out, ctx->conf, M * 4, hipMemcpyDeviceToDevice, ctx->st));
   if (pred_out) HIPX(hipMemcpyAsync(pred_out, ctx->pred, M * 4, hipMemcpyDeviceToDevice, ctx->st));
@@ -550,7 +588,9 @@ dg_status dg_generate_block(dg_ctx* ctx, int32_t batch, int32_t n_steps, int32_t
   for (int t = 0; t < n_steps; ++t) {
     StepsArg steps{};
     for (int b = 0; b < batch; ++b) steps.v[b] = n_steps - t;
+    hipEvent_t evp = prof_start(ctx);
     TRY(enqueue_pass(ctx, batch, tokens, locked, steps));
+    prof_stop(ctx, DG_PROF_PASS, evp);
   }
   return DG_OK;
 }
@@ -689,6 +729,33 @@ dg_status dg_k_lm_head(dg_ctx* ctx, int32_t batch, const void* h, float* logits)
   if (batch < 1 || batch > c.max_batch) return fail(ctx, DG_EINVAL, "batch out of range");
   if (!h || !logits) return fail(ctx, DG_EINVAL, "h and logits are required");
   return enqueue_dense(ctx, h, c.hidden, ctx->embed, c.hidden, c.vocab, batch * c.canvas_len, logits, c.vocab);
+}
+
+dg_status dg_profile(dg_ctx* ctx, int32_t enable) {
+  TRY(enter(ctx));
+  if (enable) {
+    HIPX(hipStreamSynchronize(ctx->st));  // recorded events are done before reuse
+    for (auto& r : ctx->prof_rec) r.clear();
+    ctx->ev_used = 0;
+  }
+  ctx->prof = enable != 0;
+  return DG_OK;
+}
+
+dg_status dg_profile_read(dg_ctx* ctx, int32_t kernel, int32_t* launches, double* total_ms) {
+  TRY(enter(ctx));
+  if (kernel < 0 || kernel >= DG_PROF_COUNT || !launches || !total_ms)
+    return fail(ctx, DG_EINVAL, "bad kernel id or NULL output");
+  HIPX(hipStreamSynchronize(ctx->st));
+  double tot = 0.0;
+  for (const auto& pr : ctx->prof_rec[kernel]) {
+    float ms = 0.f;
+    HIPX(hipEventElapsedTime(&ms, pr.first, pr.second));
+    tot += ms;
+  }
+  *launches = (int32_t)ctx->prof_rec[kernel].size();
+  *total_ms = tot;
+  return DG_OK;
 }
 
 }  // extern "C"
