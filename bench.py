@@ -139,7 +139,7 @@ def main():
 
     t0 = time.perf_counter()
     ctx = dg.Context(m, max_batch=B, max_prompt_len=w.prompt_len, device=0)
-    upload.load_context(ctx, w)
+    upload.load_context(ctx, w, progress=True)
     torch.cuda.synchronize()
     init_s = time.perf_counter() - t0
     print(f"[bench] {w.name}: weights and prompt KV loaded in {init_s:.1f} s", file=sys.stderr, flush=True)

@@ -94,6 +94,23 @@ struct EpiArgs {
 };
 hipError_t launch_gemm(int is_bf16, const GemmArgs& g, const EpiArgs& e, int mt, hipStream_t s);
 
+// Streaming GEMM over work entries of <= 16 rows (see gemm.hip).  Dense entries
+// cover rows [dense_row0, dense_row0 + dense_rows) of group dense_group in steps
+// of 16; work entries {group, first row, end row, -} come from the router.
+// Needs 16 * K * sizeof(T) bytes of LDS (K <= 4096 for bf16, 2048 for fp32).
+struct StreamArgs {
+  const void* A; long long lda;
+  const int32_t* a_rows; int a_rows_max;
+  const void* B; long long b_group_stride;
+  int K, NB;
+  int n_dense, dense_row0, dense_rows, dense_group;
+  const int4* work; const int32_t* work_count; int work_cap;
+  // split-K (fp32-store epilogue only): K/32 % ksplit == 0; split s writes its
+  // partial sums at out + s * split_stride
+  int ksplit; long long split_stride;
+};
+hipError_t launch_stream(int is_bf16, const StreamArgs& g, const EpiArgs& e, hipStream_t s);
+
 // Attention.
 #define DG_MAX_BATCH 64
 struct AttnArgs {
@@ -111,13 +128,24 @@ struct AttnArgs {
 hipError_t launch_attention(int is_bf16, const AttnArgs& a, hipStream_t s);
 
 // Routing, combine, norms.
-// logits != NULL: idx/gates are computed (top-k, softmax); logits == NULL: idx is
-// an input.  perm (nullable): rows*k entries t*k+s in expert-sorted order; with
-// a_rows != NULL also the shared expert's rows*k + t entries and a_rows (token of
-// every sorted row).
-hipError_t launch_moe_route(const float* logits, int rows, int E, int k, int32_t* idx, float* gates,
-                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* a_rows,
-                            hipStream_t s);
+// MoE routing (route.hip).  ROUTE_LOGITS: top-k + gates of the router logits
+// (sum of logit_parts split-K partials); ROUTE_GIVEN: idx/gates are inputs.  Both
+// then build counts/offsets/perm/a_rows/work.  bm (E * ceil(rows/32) words) and
+// done must be zero before the first launch; the kernel leaves them zero again.
+enum RouteMode { ROUTE_LOGITS = 1, ROUTE_GIVEN = 2 };
+struct RouteArgs {
+  int mode;
+  int rows, E, k;
+  const float* logits; int logit_parts; long long part_stride;
+  float* r_out;
+  int32_t* idx; float* gates;
+  int32_t* counts; int32_t* offsets; int32_t* perm; int32_t* a_rows;
+  int4* work; int32_t* work_count;
+  uint32_t* bm; int32_t* done;
+  int with_shared;
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
 // x[t] += delta_norm(sum of terms) ; out[t] = T(RMSNorm(x[t]) * (1 + w_out))
 // mode 0: terms = delta[t] (one row); mode 1: terms = y[t*k + s] for s < k, then y[rows*k + t];
 // mode 2: no delta (only the output norm); w_delta NULL: plain add.

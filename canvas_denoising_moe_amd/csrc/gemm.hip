@@ -47,6 +47,14 @@ template <> DG_DEV Frag<float> ld_frag<float>(const float* p) {
   f.b = reinterpret_cast<const float4*>(p)[1];
   return f;
 }
+template <typename T> DG_DEV void st_frag(T* p, const Frag<T>& f);
+template <> DG_DEV void st_frag<bf16_t>(bf16_t* p, const Frag<bf16_t>& f) {
+  *reinterpret_cast<uint4*>(p) = f.v;
+}
+template <> DG_DEV void st_frag<float>(float* p, const Frag<float>& f) {
+  reinterpret_cast<float4*>(p)[0] = f.a;
+  reinterpret_cast<float4*>(p)[1] = f.b;
+}
 template <typename T> DG_DEV Frag<T> zero_frag();
 template <> DG_DEV Frag<bf16_t> zero_frag<bf16_t>() { Frag<bf16_t> f; f.v = make_uint4(0, 0, 0, 0); return f; }
 template <> DG_DEV Frag<float> zero_frag<float>() {
@@ -79,9 +87,10 @@ template <typename T> DG_DEV void st(void* base, long long off, float v) {
 
 // Epilogue for one output row and lane column, WN consecutive n-blocks.
 template <typename T, int WN, int EPI>
-DG_DEV void epilogue(const EpiArgs& e, int row, int nb0, int nb_valid, int c, const float* v) {
+DG_DEV void epilogue(const EpiArgs& e, int row, int nb0, int nb_valid, int c, const float* v,
+                     long long split_off = 0) {
   if constexpr (EPI == EPI_STORE_F32) {
-    float* out = reinterpret_cast<float*>(e.out);
+    float* out = reinterpret_cast<float*>(e.out) + split_off;
 #pragma unroll
     for (int w = 0; w < WN; ++w)
       if (w < nb_valid) out[(long long)row * e.ldo + (nb0 + w) * 16 + c] = v[w];
@@ -300,6 +309,171 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g, EpiArgs e) {
 }
 
 // ----------------------------------------------------------------------------
+// Streaming GEMM: one workgroup per (work entry of <= 16 rows, n-tile).
+//
+// The entry's A rows (<= 16) are staged once, over the whole of K, into LDS in
+// MFMA A-fragment order ([K/32][64 lanes][8]: every lane later reads its own
+// 16 contiguous bytes, no bank conflicts).  After a single barrier each wave
+// streams the W fragments of its WN n-blocks through an R-deep register ring:
+// the load of k-step kb+R is issued as soon as k-step kb is consumed, so every
+// wave keeps R*WN KB of weights in flight for the whole of K and no barrier
+// ever drains the pipeline.  Entries come either from a dense row range (16
+// rows each) or from the router's work list (expert, first row, end row), in
+// which heavy experts are split into several 16-row entries that run in
+// parallel.  Blocks are ordered tile-major over (tile, entry) and every XCD
+// takes a contiguous slice, so the entries of one expert run back to back on
+// one XCD and share that expert's W tile through its L2.
+// ----------------------------------------------------------------------------
+template <typename T, int WN, int EPI, int R>
+__global__ __launch_bounds__(256) void k_stream(StreamArgs g, EpiArgs e) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  T* As = reinterpret_cast<T*>(smem_raw);  // [KB][64][8]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tiles = (g.NB + 4 * WN - 1) / (4 * WN);
+  const int J = g.n_dense + g.work_cap;
+  const int ksplit = g.ksplit > 1 ? g.ksplit : 1;
+  const long long P = (long long)tiles * J * ksplit;
+  const long long Q = (P + 7) >> 3;
+  const long long p = (long long)(blockIdx.x & 7) * Q + (blockIdx.x >> 3);
+  if (p >= P) return;
+  const int ks = (int)(p % ksplit);
+  const long long pp = p / ksplit;
+  const int tile = (int)(pp / J), j = (int)(pp - (long long)tile * J);
+  int group, rs, re;
+  if (j < g.n_dense) {
+    group = g.dense_group;
+    rs = g.dense_row0 + j * 16;
+    re = min(g.dense_row0 + g.dense_rows, rs + 16);
+  } else {
+    const int w = j - g.n_dense;
+    if (w >= *g.work_count) return;
+    const int4 en = g.work[w];
+    group = en.x; rs = en.y; re = en.z;
+  }
+  if (rs >= re) return;
+  const int KBall = g.K >> 5;
+  const int KB = KBall / ksplit;  // k-steps of this split
+  const int kbase = ks * KB;
+
+  // ---- weight prefetch first: the HBM stream is the long pole
+  const T* __restrict__ Bg = reinterpret_cast<const T*>(g.B) + (long long)group * g.b_group_stride;
+  const int nb0 = tile * 4 * WN + wave * WN;
+  const int nbv = g.NB - nb0;  // wave-uniform count of valid n-blocks
+  const T* bptr[WN];
+#pragma unroll
+  for (int w = 0; w < WN; ++w) bptr[w] = Bg + ((long long)(nb0 + w) * KBall + kbase) * 512 + lane * 8;
+  Frag<T> b[R][WN];
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int w = 0; w < WN; ++w)
+      b[i][w] = (i < KB && w < nbv) ? ld_frag<T>(bptr[w] + (long long)i * 512) : zero_frag<T>();
+
+  // ---- stage A rows [rs, re) into fragment order, loads batched ahead of the stores
+  {
+    const T* __restrict__ A = reinterpret_cast<const T*>(g.A);
+    const int k8s = KB * 4;  // 8-element groups per row within the split
+    const int groups8 = 16 * k8s;
+    A += kbase * 32;
+    constexpr int U = 8;
+    for (int base = tid; base < groups8; base += 256 * U) {
+      Frag<T> v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int q = base + u * 256;
+        v[u] = zero_frag<T>();
+        if (q < groups8) {
+          const int r = q / k8s, k8 = q - r * k8s;  // consecutive threads read along a row
+          const int row = rs + r;
+          if (row < re) {
+            long long ar = row;
+            if (g.a_rows) {
+              ar = g.a_rows[row];
+              ar = ar < 0 ? 0 : (ar >= g.a_rows_max ? g.a_rows_max - 1 : ar);
+            }
+            v[u] = ld_frag<T>(A + ar * g.lda + k8 * 8);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int q = base + u * 256;
+        if (q < groups8) {
+          const int r = q / k8s, k8 = q - r * k8s;
+          st_frag<T>(As + ((k8 >> 2) * 64 + r + 16 * (k8 & 3)) * 8, v[u]);
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  floatx4 acc[WN];
+#pragma unroll
+  for (int w = 0; w < WN; ++w) acc[w] = floatx4{0.f, 0.f, 0.f, 0.f};
+  if (nbv > 0) {
+    for (int kb0 = 0; kb0 < KB; kb0 += R) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int kb = kb0 + i;
+        if (kb < KB) {
+          const Frag<T> a = ld_frag<T>(As + (kb * 64 + lane) * 8);
+#pragma unroll
+          for (int w = 0; w < WN; ++w) mma(acc[w], a, b[i][w]);
+          const int kn = kb + R;
+          if (kn < KB) {
+#pragma unroll
+            for (int w = 0; w < WN; ++w)
+              if (w < nbv) b[i][w] = ld_frag<T>(bptr[w] + (long long)kn * 512);
+          }
+        }
+      }
+    }
+    const int c = lane & 15, rg = (lane >> 4) * 4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = rs + rg + r;
+      if (row < re) {
+        float v[WN];
+#pragma unroll
+        for (int w = 0; w < WN; ++w) v[w] = acc[w][r];
+        epilogue<T, WN, EPI>(e, row, nb0, nbv, c, v, ks * g.split_stride);
+      }
+    }
+  }
+}
+
+template <typename T, int WN, int EPI, int R>
+hipError_t run_stream(const StreamArgs& g, const EpiArgs& e, hipStream_t s) {
+  const int tiles = (g.NB + 4 * WN - 1) / (4 * WN);
+  const int ksplit = g.ksplit > 1 ? g.ksplit : 1;
+  if (((g.K >> 5) % ksplit) != 0 || (ksplit > 1 && EPI != EPI_STORE_F32)) return hipErrorInvalidValue;
+  const long long P = (long long)tiles * (g.n_dense + g.work_cap) * ksplit;
+  if (P <= 0) return hipSuccess;
+  const long long blocks = ((P + 7) >> 3) << 3;
+  const size_t lds = (size_t)16 * (g.K / ksplit) * sizeof(T);
+  static bool attr_set = false;  // one attribute call per instantiation
+  if (!attr_set) {
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_stream<T, WN, EPI, R>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (err != hipSuccess) return err;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((k_stream<T, WN, EPI, R>), dim3((unsigned)blocks), dim3(256), lds, s, g, e);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t run_stream_t(const StreamArgs& g, const EpiArgs& e, hipStream_t s) {
+  switch (e.kind) {
+    case EPI_STORE_F32: return run_stream<T, 2, EPI_STORE_F32, 8>(g, e, s);
+    case EPI_GEGLU: return run_stream<T, 2, EPI_GEGLU, 8>(g, e, s);
+    case EPI_DOWN: return run_stream<T, 2, EPI_DOWN, 8>(g, e, s);
+    case EPI_QKV: return run_stream<T, 2, EPI_QKV, 8>(g, e, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// ----------------------------------------------------------------------------
 // weight repack
 // ----------------------------------------------------------------------------
 template <typename T>
@@ -366,6 +540,10 @@ hipError_t run_gemm_t(const GemmArgs& g, const EpiArgs& e, int mt, hipStream_t s
 
 hipError_t launch_gemm(int is_bf16, const GemmArgs& g, const EpiArgs& e, int mt, hipStream_t s) {
   return is_bf16 ? run_gemm_t<bf16_t>(g, e, mt, s) : run_gemm_t<float>(g, e, mt, s);
+}
+
+hipError_t launch_stream(int is_bf16, const StreamArgs& g, const EpiArgs& e, hipStream_t s) {
+  return is_bf16 ? run_stream_t<bf16_t>(g, e, s) : run_stream_t<float>(g, e, s);
 }
 
 hipError_t launch_pack(int is_bf16, const PackArgs& a, hipStream_t s) {

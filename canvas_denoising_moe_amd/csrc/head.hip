@@ -33,18 +33,32 @@ __global__ __launch_bounds__(256) void k_argmax_conf(const float* __restrict__ l
   const float4* r4 = reinterpret_cast<const float4*>(logits + row * V);
   const int tid = threadIdx.x;
   MaxState st{-INFINITY, 0x7fffffff, 0.f};
-  for (int c4 = tid; c4 < (V >> 2); c4 += blockDim.x) {
-    const float4 v = r4[c4];
-    const float vals[4] = {v.x, v.y, v.z, v.w};
+  const int n4 = V >> 2, nt = blockDim.x;
+  constexpr int U = 8;  // loads in flight per thread
+  for (int base = tid; base < n4; base += nt * U) {
+    float4 v[U];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float x = vals[j];
-      if (x > st.m) {
-        st.s = (st.s > 0.f ? st.s * expf(st.m - x) : 0.f) + 1.0f;
-        st.m = x;
-        st.i = c4 * 4 + j;
-      } else {
-        st.s += expf(x - st.m);
+    for (int u = 0; u < U; ++u) {
+      const int c4 = base + u * nt;
+      v[u] = c4 < n4 ? r4[c4] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    }
+    // columns are visited in increasing order, so a later equal maximum never replaces
+    // an earlier one
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c4 = base + u * nt;
+      if (c4 >= n4) break;
+      const float vals[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x = vals[j];
+        if (x > st.m) {
+          st.s = (st.s > 0.f ? st.s * expf(st.m - x) : 0.f) + 1.0f;
+          st.m = x;
+          st.i = c4 * 4 + j;
+        } else {
+          st.s += expf(x - st.m);
+        }
       }
     }
   }

@@ -1,162 +1,133 @@
-// Router top-k with the token -> expert scatter, the residual / RMSNorm
+// The residual / RMSNorm
 // kernels (the norm sandwich of [HandsOn] "Detailed Specs", fused with the
 // residual adds and the MoE combine), the embedding gather and the RoPE table.
 #include "common.h"
 
 namespace {
 
-// One workgroup routes every token: top-k of E logits per token (logit
-// descending, ties to the lower expert index), softmax over the kept logits,
-// then a deterministic counting sort of the (token, slot) pairs by expert with
-// tokens ascending inside an expert.  Membership bits per (expert, token) are
-// set with atomicOr (order-independent), so counts, offsets and ranks do not
-// depend on thread timing.
-__global__ __launch_bounds__(1024) void k_moe_route(const float* __restrict__ logits, int rows, int E,
-                                                    int k, int32_t* idx, float* gates, int32_t* counts,
-                                                    int32_t* offsets, int32_t* perm, int32_t* a_rows) {
-  extern __shared__ uint32_t sm[];
-  const int W = (rows + 31) >> 5;
-  uint32_t* bm = sm;                                 // [E][W]
-  int* offs = reinterpret_cast<int*>(sm + E * W);    // [E + 2]
-  const int tid = threadIdx.x, nt = blockDim.x;
-  for (int i = tid; i < E * W; i += nt) bm[i] = 0u;
-  __syncthreads();
-
-  for (int t = tid; t < rows; t += nt) {
-    if (!logits) {  // routing given: only the scatter
-      for (int s = 0; s < k; ++s) {
-        int e = idx[(long long)t * k + s];
-        e = e < 0 ? 0 : (e >= E ? E - 1 : e);  // out-of-range ids must not leave LDS
-        atomicOr(&bm[e * W + (t >> 5)], 1u << (t & 31));
-      }
-      continue;
-    }
-    const float* r = logits + (long long)t * E;
-    float bv[8];
-    int be[8];
-#pragma unroll
-    for (int s = 0; s < 8; ++s) { bv[s] = -INFINITY; be[s] = -1; }
-    for (int e = 0; e < E; ++e) {
-      const float v = r[e];
-      // first slot that v beats (an empty slot, or a strictly smaller logit);
-      // equal logits keep the earlier (lower) expert in front
-      int p = k;
-#pragma unroll
-      for (int s = 7; s >= 0; --s)
-        if (s < k && (be[s] < 0 || bv[s] < v)) p = s;
-      if (p < k) {
-#pragma unroll
-        for (int s = 7; s > 0; --s)
-          if (s < k && s > p) { bv[s] = bv[s - 1]; be[s] = be[s - 1]; }
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-          if (s == p) { bv[s] = v; be[s] = e; }
-      }
-    }
-    float ex[8], sum = 0.f;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      ex[s] = s < k ? expf(bv[s] - bv[0]) : 0.f;
-      sum += ex[s];
-    }
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      if (s < k) {
-        idx[(long long)t * k + s] = be[s];
-        gates[(long long)t * k + s] = ex[s] / sum;
-        atomicOr(&bm[be[s] * W + (t >> 5)], 1u << (t & 31));
-      }
-    }
-  }
-  __threadfence_block();
-  __syncthreads();
-  if (tid < E) {
-    int c = 0;
-    for (int w = 0; w < W; ++w) c += __popc(bm[tid * W + w]);
-    offs[tid] = c;
-    if (counts) counts[tid] = c;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int acc = 0;
-    for (int e = 0; e < E; ++e) {
-      const int c = offs[e];
-      offs[e] = acc;
-      acc += c;
-    }
-    offs[E] = acc;  // == rows * k
-    offs[E + 1] = acc + rows;
-  }
-  __syncthreads();
-  if (offsets)
-    for (int e = tid; e < E + 2; e += nt) offsets[e] = offs[e];
-  for (int p = tid; p < rows * k; p += nt) {
-    const int t = p / k;
-    int e = idx[p];
-    e = e < 0 ? 0 : (e >= E ? E - 1 : e);
-    const uint32_t* row = bm + e * W;
-    const int wt = t >> 5;
-    int rank = __popc(row[wt] & ((1u << (t & 31)) - 1u));
-    for (int w = 0; w < wt; ++w) rank += __popc(row[w]);
-    const int pos = offs[e] + rank;
-    if (perm) perm[pos] = p;
-    if (a_rows) a_rows[pos] = t;
-  }
-  if (a_rows && perm) {
-    const int base = rows * k;
-    for (int t = tid; t < rows; t += nt) {
-      perm[base + t] = base + t;
-      a_rows[base + t] = t;
-    }
-  }
+template <typename T> DG_DEV float4 load4(const T* p);
+template <> DG_DEV float4 load4<float>(const float* p) { return *reinterpret_cast<const float4*>(p); }
+template <> DG_DEV float4 load4<bf16_t>(const bf16_t* p) {
+  const uint2 q = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(q.x << 16), __uint_as_float(q.x & 0xffff0000u),
+                     __uint_as_float(q.y << 16), __uint_as_float(q.y & 0xffff0000u));
 }
+template <typename T> DG_DEV void store4(T* p, float4 v);
+template <> DG_DEV void store4<float>(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+template <> DG_DEV void store4<bf16_t>(bf16_t* p, float4 v) {
+  *reinterpret_cast<uint2*>(p) = make_uint2((uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16),
+                                            (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16));
+}
+DG_DEV float4 f4add(float4 a, float4 b) { return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w); }
+DG_DEV float f4dot(float4 a) { return a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w; }
 
 // x[t] += RMSNorm(delta_t) * (1 + w_delta)   (plain add without w_delta)
 // out[t] = T(RMSNorm(x[t]) * (1 + w_out))      (skipped without w_out)
 // delta_t: mode 0 one row of `delta`; mode 1 the MoE combine
 //   sum_{s<k} y[t*k + s] (slot order) + y[rows*k + t]; mode 2 nothing.
-template <typename T>
+// One workgroup per token; thread i owns float4 columns i, i + 256, ... (NV of
+// them, H <= 1024 * NV).  Every term of the row (up to k + 1 MoE outputs) is
+// loaded before any arithmetic, so a token's whole working set is in flight at
+// once; sums of squares are fixed-order block reductions.
+template <typename T, int NV>
 __global__ __launch_bounds__(256) void k_residual_norm(NormArgs a) {
-  extern __shared__ float buf[];  // [H]
   __shared__ float red[8];
-  const int t = blockIdx.x, tid = threadIdx.x, H = a.H;
-  float* x = a.x + (long long)t * H;
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int H = a.H, n4 = H >> 2;
+  float4* x4 = reinterpret_cast<float4*>(a.x + (long long)t * H);
+  const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 xv[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c4 = tid + 256 * i;
+    xv[i] = c4 < n4 ? x4[c4] : z4;
+  }
   if (a.mode != 2) {
-    float ss = 0.f;
-    for (int c = tid; c < H; c += blockDim.x) {
-      float d;
-      if (a.mode == 0) {
-        d = a.delta[(long long)t * H + c];
-      } else {
-        d = 0.f;
-        for (int s = 0; s < a.k; ++s) d += a.delta[((long long)t * a.k + s) * H + c];
-        d += a.delta[((long long)a.rows * a.k + t) * H + c];
+    const float4* d4 = reinterpret_cast<const float4*>(a.delta);
+    float4 dv[NV];
+    if (a.mode == 0) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int c4 = tid + 256 * i;
+        dv[i] = c4 < n4 ? d4[(long long)t * n4 + c4] : z4;
       }
-      buf[c] = d;
-      ss += d * d;
-    }
-    if (a.w_delta) {
-      const float tot = block_sum(ss, red);
-      const float sc = rsqrtf(tot / H + a.eps);
-      const T* w = reinterpret_cast<const T*>(a.w_delta);
-      for (int c = tid; c < H; c += blockDim.x) x[c] += buf[c] * sc * (1.0f + to_f<T>(w[c]));
     } else {
-      for (int c = tid; c < H; c += blockDim.x) x[c] += buf[c];
+      // routed terms y[t*k + s] (slot order), then the shared expert's y[rows*k + t]
+      float4 tv[8][NV], sv[NV];
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+          const int c4 = tid + 256 * i;
+          tv[s][i] = (s < a.k && c4 < n4) ? d4[((long long)t * a.k + s) * n4 + c4] : z4;
+        }
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int c4 = tid + 256 * i;
+        sv[i] = c4 < n4 ? d4[((long long)a.rows * a.k + t) * n4 + c4] : z4;
+      }
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        float4 d = z4;
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          if (s < a.k) d = f4add(d, tv[s][i]);
+        dv[i] = f4add(d, sv[i]);
+      }
     }
-    __syncthreads();
+    const T* w = reinterpret_cast<const T*>(a.w_delta);
+    float sc = 1.0f;
+    if (w) {
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) ss += f4dot(dv[i]);
+      sc = rsqrtf(block_sum(ss, red) / H + a.eps);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c4 = tid + 256 * i;
+      if (c4 < n4) {
+        float4 d = dv[i];
+        if (w) {
+          const float4 g = load4<T>(w + 4 * c4);
+          d = make_float4(d.x * sc * (1.f + g.x), d.y * sc * (1.f + g.y), d.z * sc * (1.f + g.z),
+                          d.w * sc * (1.f + g.w));
+        }
+        xv[i] = f4add(xv[i], d);
+        x4[c4] = xv[i];
+      }
+    }
   }
   if (a.w_out) {
     float ss = 0.f;
-    for (int c = tid; c < H; c += blockDim.x) {
-      const float v = x[c];
-      ss += v * v;
-    }
-    const float tot = block_sum(ss, red + 4);
-    const float sc = rsqrtf(tot / H + a.eps);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) ss += f4dot(xv[i]);  // columns past H hold zeros
+    const float sc = rsqrtf(block_sum(ss, red + 4) / H + a.eps);
     const T* w = reinterpret_cast<const T*>(a.w_out);
     T* out = reinterpret_cast<T*>(a.out) + (long long)t * H;
-    for (int c = tid; c < H; c += blockDim.x) out[c] = from_f<T>(x[c] * sc * (1.0f + to_f<T>(w[c])));
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c4 = tid + 256 * i;
+      if (c4 < n4) {
+        const float4 g = load4<T>(w + 4 * c4);
+        const float4 v = xv[i];
+        store4<T>(out + 4 * c4, make_float4(v.x * sc * (1.f + g.x), v.y * sc * (1.f + g.y),
+                                            v.z * sc * (1.f + g.z), v.w * sc * (1.f + g.w)));
+      }
+    }
   }
+}
+
+template <typename T>
+hipError_t run_residual_norm(const NormArgs& a, hipStream_t s) {
+  const int n4 = a.H >> 2;
+  if (n4 <= 256)
+    hipLaunchKernelGGL((k_residual_norm<T, 1>), dim3(a.rows), dim3(256), 0, s, a);
+  else if (n4 <= 512)
+    hipLaunchKernelGGL((k_residual_norm<T, 2>), dim3(a.rows), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_residual_norm<T, 4>), dim3(a.rows), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 // x[t, h] = E[token_t, h] read from the fragment-packed embedding
@@ -194,24 +165,10 @@ __global__ void k_rope_table(float2* cs, int N, int D, int prompt_len, double th
 
 }  // namespace
 
-hipError_t launch_moe_route(const float* logits, int rows, int E, int k, int32_t* idx, float* gates,
-                            int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* a_rows,
-                            hipStream_t s) {
-  const int W = (rows + 31) / 32;
-  const size_t lds = (size_t)E * W * 4 + (size_t)(E + 2) * 4;
-  hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(1024), lds, s, logits, rows, E, k, idx, gates, counts,
-                     offsets, perm, a_rows);
-  return hipGetLastError();
-}
-
 hipError_t launch_residual_norm(int is_bf16, const NormArgs& a, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
-  const size_t lds = (size_t)a.H * 4;
-  if (is_bf16)
-    hipLaunchKernelGGL(k_residual_norm<bf16_t>, dim3(a.rows), dim3(256), lds, s, a);
-  else
-    hipLaunchKernelGGL(k_residual_norm<float>, dim3(a.rows), dim3(256), lds, s, a);
-  return hipGetLastError();
+  if (a.H > 4096 || (a.H & 3) || a.k > 8) return hipErrorInvalidValue;
+  return is_bf16 ? run_residual_norm<bf16_t>(a, s) : run_residual_norm<float>(a, s);
 }
 
 hipError_t launch_embed(int is_bf16, const int32_t* tokens, int rows, int H, int V, const void* pe,

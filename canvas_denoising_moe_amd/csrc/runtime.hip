@@ -19,8 +19,8 @@ std::string g_create_error;
 struct LayerW {
   void* qkv = nullptr;   // packed [(Hq+2Hkv)D/16][H/32][64][8]
   void* wo = nullptr;    // packed [H/16][HqD/32][64][8]
-  void* router = nullptr;
-  void* gu = nullptr;    // (E+1) experts, packed gate|up interleave [2F/16][H/32][64][8]
+  void* router = nullptr;    // packed [E/16][H/32][64][8]
+  void* gu = nullptr;   // (E+1) experts, packed gate|up interleave [2F/16][H/32][64][8]
   void* down = nullptr;  // (E+1) experts, packed [H/16][F/32][64][8]
   void* norm[4] = {nullptr, nullptr, nullptr, nullptr};  // in, pa, pf, pf2
   bool set = false;
@@ -54,6 +54,12 @@ struct dg_ctx {
   int32_t *idx = nullptr, *offsets = nullptr, *perm = nullptr, *arows = nullptr, *pred = nullptr;
   long long part_cap = 0;
   int32_t* trace = nullptr;
+  // router scatter state: membership bitmap and ticket (kept zero between launches),
+  // expert work list
+  uint32_t* bm = nullptr;
+  int32_t* done = nullptr;
+  int4* work = nullptr;
+  int32_t* work_count = nullptr;
   std::string err;
   std::vector<void*> owned;
   // kernel timing: event pairs per kernel class (pool reused after a reset)
@@ -136,7 +142,43 @@ void prof_stop(dg_ctx* ctx, int kind, hipEvent_t s) {
   ctx->prof_rec[kind].push_back({s, e});
 }
 
+// Scratch of the context-free routing entry point: membership bitmap for up to
+// 256 experts x 4096 rows and the completion ticket, per device, allocated on
+// first use and kept zero between launches by the kernel itself.
+dg_status route_scratch(uint32_t** bm, int32_t** done) {
+  static uint32_t* s_bm[DG_MAX_BATCH] = {};
+  static int32_t* s_done[DG_MAX_BATCH] = {};
+  dg_ctx* ctx = nullptr;
+  int dev = 0;
+  HIPX(hipGetDevice(&dev));
+  if (dev < 0 || dev >= DG_MAX_BATCH) return fail(ctx, DG_EUNSUPPORTED, "device index %d too large", dev);
+  if (!s_bm[dev]) {
+    const size_t words = 256 * (4096 / 32);
+    void* p = nullptr;
+    HIPX(hipMalloc(&p, words * 4 + 256));
+    HIPX(hipMemset(p, 0, words * 4 + 256));
+    HIPX(hipDeviceSynchronize());
+    s_bm[dev] = reinterpret_cast<uint32_t*>(p);
+    s_done[dev] = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(p) + words * 4);
+  }
+  *bm = s_bm[dev];
+  *done = s_done[dev];
+  return DG_OK;
+}
+
 bool is_global(const dg_config& c, int l) { return (c.global_layer_mask >> l) & 1ull; }
+
+// capacity of the expert work list for M tokens: every routed expert adds at
+// most one partial 16-row entry beyond M*k/16, the shared expert M/16
+int work_cap(const dg_config& c, int M) {
+  return c.n_experts + (M * c.top_k + 15) / 16 + (M + 15) / 16;
+}
+
+// split-K factor of the router GEMM: its weights are small (H x E), so the K
+// range is cut into kRouterSplit slices to spread the stream over many
+// workgroups; the routing kernel adds the partial logits in slice order
+constexpr int kRouterSplit = 8;
+int router_split(const dg_config& c) { return ((c.hidden / 32) % kRouterSplit) == 0 ? kRouterSplit : 1; }
 int kv_len(const dg_config& c, int l, int prompt_len) {
   return is_global(c, l) ? prompt_len : (prompt_len < c.window ? prompt_len : c.window);
 }
@@ -145,8 +187,11 @@ dg_status check_config(const dg_config* c) {
   dg_ctx* ctx = nullptr;
   if (!c) return fail(ctx, DG_EINVAL, "config is NULL");
   if (c->n_layers < 1 || c->n_layers > 64) return fail(ctx, DG_EINVAL, "n_layers must be in [1, 64]");
-  if (c->hidden <= 0 || c->hidden % 32 || c->hidden > 16384)
-    return fail(ctx, DG_EUNSUPPORTED, "hidden must be a positive multiple of 32 (<= 16384)");
+  // the streaming GEMMs stage 16 rows x K in LDS: K <= 4096 (bf16) / 2048 (fp32)
+  const int kmax = c->dtype == DG_F32 ? 2048 : 4096;
+  if (c->hidden <= 0 || c->hidden % 32 || c->hidden > kmax)
+    return fail(ctx, DG_EUNSUPPORTED, "hidden must be a positive multiple of 32 (<= %d)", kmax);
+  if (c->expert_ffn > kmax) return fail(ctx, DG_EUNSUPPORTED, "expert_ffn must be <= %d", kmax);
   if (c->n_heads <= 0 || c->n_kv_heads <= 0 || c->n_heads % c->n_kv_heads)
     return fail(ctx, DG_EINVAL, "n_heads must be a positive multiple of n_kv_heads");
   if (c->head_dim <= 0 || c->head_dim % 32 || c->head_dim > 256)
@@ -198,7 +243,7 @@ dg_status alloc_workspaces(dg_ctx* ctx) {
   TRY(dalloc(ctx, &ctx->kc, M * c.n_kv_heads * D * es));
   TRY(dalloc(ctx, &ctx->vc, M * c.n_kv_heads * D * es));
   TRY(dalloc(ctx, &ctx->o, M * c.n_heads * D * es));
-  TRY(dalloc_t(ctx, &ctx->rl, M * E * 4));
+  TRY(dalloc_t(ctx, &ctx->rl, (size_t)kRouterSplit * M * E * 4));
   TRY(dalloc_t(ctx, &ctx->idx, M * K * 4));
   TRY(dalloc_t(ctx, &ctx->gates, M * K * 4));
   TRY(dalloc_t(ctx, &ctx->offsets, (E + 2) * 4));
@@ -216,6 +261,15 @@ dg_status alloc_workspaces(dg_ctx* ctx) {
   TRY(dalloc_t(ctx, &ctx->part_o, (size_t)ctx->part_cap * D * 4));
   TRY(dalloc_t(ctx, &ctx->part_m, (size_t)ctx->part_cap * 4));
   TRY(dalloc_t(ctx, &ctx->part_l, (size_t)ctx->part_cap * 4));
+  const size_t bm_words = E * ((M + 31) / 32);
+  TRY(dalloc_t(ctx, &ctx->bm, bm_words * 4));
+  TRY(dalloc_t(ctx, &ctx->done, 4));
+  TRY(dalloc_t(ctx, &ctx->work, (size_t)work_cap(c, (int)M) * sizeof(int4)));
+  TRY(dalloc_t(ctx, &ctx->work_count, 4));
+  HIPX(hipMemset(ctx->bm, 0, bm_words * 4));
+  HIPX(hipMemset(ctx->done, 0, 4));
+  HIPX(hipMemset(ctx->work_count, 0, 4));
+  HIPX(hipDeviceSynchronize());
   return DG_OK;
 }
 
@@ -240,10 +294,11 @@ dg_status enqueue_qkv(dg_ctx* ctx, int l, int B, const void* a, void* q, void* k
                       const long long* qs, const long long* ks, const long long* vs) {
   const dg_config& c = ctx->c;
   const int H = c.hidden, D = c.head_dim;
-  GemmArgs g{};
+  const int M = B * c.canvas_len;
+  StreamArgs g{};
   g.A = a; g.lda = H; g.B = ctx->L[l].qkv; g.K = H;
   g.NB = (c.n_heads + 2 * c.n_kv_heads) * D / 16;
-  g.static_rows = B * c.canvas_len;
+  g.n_dense = (M + 15) / 16; g.dense_rows = M;
   EpiArgs e{};
   e.kind = EPI_QKV;
   e.q = q; e.k = k; e.v = v;
@@ -253,7 +308,7 @@ dg_status enqueue_qkv(dg_ctx* ctx, int l, int B, const void* a, void* q, void* k
   e.n_rot_local = D / 2;
   e.n_rot_global = (int)(c.prope_frac * (float)(D / 2));
   e.is_global = is_global(c, l);
-  HIPX(launch_gemm(ctx->bf16, g, e, 4, ctx->st));
+  HIPX(launch_stream(ctx->bf16, g, e, ctx->st));
   return DG_OK;
 }
 
@@ -277,50 +332,79 @@ dg_status enqueue_attention(dg_ctx* ctx, int l, int B, void* o, int canvas_keys)
   return DG_OK;
 }
 
-// m-chunk height for the grouped expert GEMMs: 128 rows once experts average
-// more than 48 rows, 64 otherwise
-int expert_mt(const dg_config& c, int M) { return (long long)M * c.top_k > 48LL * c.n_experts ? 8 : 4; }
+// Routing of layer l.  ROUTE_LOGITS: router logits of ctx->f (split-K partials in
+// ctx->rl), then top-k and the scatter; ROUTE_GIVEN: ctx->idx/gates are given.
+dg_status enqueue_route(dg_ctx* ctx, int l, int M, int mode) {
+  const dg_config& c = ctx->c;
+  const int E = c.n_experts, H = c.hidden;
+  RouteArgs r{};
+  r.mode = mode; r.rows = M; r.E = E; r.k = c.top_k;
+  if (mode == ROUTE_LOGITS) {
+    EpiArgs e{};
+    e.kind = EPI_STORE_F32; e.out = ctx->rl; e.ldo = E;
+    StreamArgs g{};
+    g.A = ctx->f; g.lda = H; g.B = ctx->L[l].router; g.K = H; g.NB = E / 16;
+    g.n_dense = (M + 15) / 16; g.dense_rows = M;
+    g.ksplit = router_split(c); g.split_stride = (long long)M * E;
+    HIPX(launch_stream(ctx->bf16, g, e, ctx->st));
+    r.logits = ctx->rl; r.logit_parts = g.ksplit; r.part_stride = g.split_stride;
+  }
+  r.idx = ctx->idx; r.gates = ctx->gates;
+  r.offsets = ctx->offsets; r.perm = ctx->perm; r.a_rows = ctx->arows;
+  r.work = ctx->work; r.work_count = ctx->work_count;
+  r.bm = ctx->bm; r.done = ctx->done;
+  r.with_shared = 1;
+  HIPX(launch_route(r, ctx->st));
+  return DG_OK;
+}
 
-// routed + shared expert FFNs of layer l on f (routing already in idx/gates/offsets/perm/arows);
-// leaves y [M*k + M, H]
+// routed + shared expert FFNs of layer l on f (routing already in idx/gates/perm/arows/work);
+// leaves y [M*k + M, H]: row t*k + s holds gate[t,s] * FFN_e(f_t), row M*k + t the shared FFN
 dg_status enqueue_experts(dg_ctx* ctx, int l, int M, const void* f) {
   const dg_config& c = ctx->c;
-  const int H = c.hidden, F = c.expert_ffn, E = c.n_experts, K = c.top_k;
-  const int mt = expert_mt(c, M);
-  GemmArgs g{};
+  const int H = c.hidden, F = c.expert_ffn, K = c.top_k;
+  StreamArgs g{};
   g.A = f; g.lda = H; g.a_rows = ctx->arows; g.a_rows_max = M;
   g.B = ctx->L[l].gu; g.b_group_stride = 2LL * F * H;
   g.K = H; g.NB = 2 * F / 16;
-  g.static_row0 = M * K; g.static_rows = M; g.static_group = E;
-  g.group_off = ctx->offsets; g.n_groups = E;
+  g.work = ctx->work; g.work_count = ctx->work_count; g.work_cap = work_cap(c, M);
   EpiArgs e{};
   e.kind = EPI_GEGLU; e.out = ctx->u; e.ldo = F;
   hipEvent_t ev = prof_start(ctx);
-  HIPX(launch_gemm(ctx->bf16, g, e, mt, ctx->st));
+  HIPX(launch_stream(ctx->bf16, g, e, ctx->st));
   prof_stop(ctx, DG_PROF_GATE_UP, ev);
 
-  GemmArgs d{};
+  StreamArgs d{};
   d.A = ctx->u; d.lda = F; d.a_rows = nullptr;
   d.B = ctx->L[l].down; d.b_group_stride = (long long)F * H;
   d.K = F; d.NB = H / 16;
-  d.static_row0 = M * K; d.static_rows = M; d.static_group = E;
-  d.group_off = ctx->offsets; d.n_groups = E;
+  d.work = ctx->work; d.work_count = ctx->work_count; d.work_cap = work_cap(c, M);
   EpiArgs ed{};
   ed.kind = EPI_DOWN; ed.out = ctx->y; ed.ldo = H;
   ed.slot = ctx->perm; ed.gates = ctx->gates; ed.routed_rows = M * K; ed.out_rows = M * K + M;
   ev = prof_start(ctx);
-  HIPX(launch_gemm(ctx->bf16, d, ed, mt, ctx->st));
+  HIPX(launch_stream(ctx->bf16, d, ed, ctx->st));
   prof_stop(ctx, DG_PROF_DOWN, ev);
   return DG_OK;
 }
 
+// Dense y = A @ W into fp32.  Small weights (the output projection) stream per
+// 16-row tile and re-read W from L2; the LM head's 1 GB embedding is read once
+// per 64-row chunk by the chunked kernel instead.
 dg_status enqueue_dense(dg_ctx* ctx, const void* A, int lda, const void* Bp, int K, int N, int M, float* out,
-                        int ldo) {
-  GemmArgs g{};
-  g.A = A; g.lda = lda; g.B = Bp; g.K = K; g.NB = N / 16; g.static_rows = M;
+                        int ldo, bool streaming = true) {
   EpiArgs e{};
   e.kind = EPI_STORE_F32; e.out = out; e.ldo = ldo;
-  HIPX(launch_gemm(ctx->bf16, g, e, 4, ctx->st));
+  if (streaming) {
+    StreamArgs g{};
+    g.A = A; g.lda = lda; g.B = Bp; g.K = K; g.NB = N / 16;
+    g.n_dense = (M + 15) / 16; g.dense_rows = M;
+    HIPX(launch_stream(ctx->bf16, g, e, ctx->st));
+  } else {
+    GemmArgs g{};
+    g.A = A; g.lda = lda; g.B = Bp; g.K = K; g.NB = N / 16; g.static_rows = M;
+    HIPX(launch_gemm(ctx->bf16, g, e, 4, ctx->st));
+  }
   return DG_OK;
 }
 
@@ -339,13 +423,12 @@ dg_status enqueue_layers(dg_ctx* ctx, int B, const void* w_last_out) {
     TRY(enqueue_qkv(ctx, l, B, ctx->a, ctx->q, ctx->kc, ctx->vc, qs, ks, vs));
     TRY(enqueue_attention(ctx, l, B, ctx->o, 1));
     TRY(enqueue_dense(ctx, ctx->o, Hq * D, W.wo, Hq * D, H, M, ctx->ao, H));
+    // x += RMSNorm(o Wo)(1 + w_pa); f = RMSNorm(x)(1 + w_pf)
     NormArgs na{};
     na.mode = 0; na.rows = M; na.H = H; na.k = K; na.eps = c.rms_eps;
     na.x = ctx->x; na.delta = ctx->ao; na.w_delta = W.norm[1]; na.w_out = W.norm[2]; na.out = ctx->f;
     HIPX(launch_residual_norm(ctx->bf16, na, ctx->st));
-    TRY(enqueue_dense(ctx, ctx->f, H, W.router, H, E, M, ctx->rl, E));
-    HIPX(launch_moe_route(ctx->rl, M, E, K, ctx->idx, ctx->gates, nullptr, ctx->offsets, ctx->perm,
-                          ctx->arows, ctx->st));
+    TRY(enqueue_route(ctx, l, M, ROUTE_LOGITS));
     if (ctx->trace)
       HIPX(hipMemcpyAsync(ctx->trace + (size_t)l * M * K, ctx->idx, (size_t)M * K * 4,
                           hipMemcpyDeviceToDevice, ctx->st));
@@ -370,7 +453,7 @@ dg_status enqueue_pass(dg_ctx* ctx, int B, int32_t* tokens, uint8_t* locked, con
   HIPX(launch_residual_norm(ctx->bf16, n0, ctx->st));
   TRY(enqueue_layers(ctx, B, ctx->norm_final));
   hipEvent_t ev = prof_start(ctx);
-  TRY(enqueue_dense(ctx, ctx->a, H, ctx->embed, H, c.vocab, M, ctx->logits, c.vocab));
+  TRY(enqueue_dense(ctx, ctx->a, H, ctx->embed, H, c.vocab, M, ctx->logits, c.vocab, false));
   prof_stop(ctx, DG_PROF_LM_HEAD, ev);
   HIPX(launch_argmax_conf(ctx->logits, M, c.vocab, ctx->pred, ctx->conf, ctx->st));
   HIPX(launch_lock_select(B, N, ctx->conf, ctx->pred, tokens, locked, steps, ctx->st));
@@ -657,8 +740,16 @@ dg_status dg_k_moe_route(const float* logits, int32_t rows, int32_t n_experts, i
     return fail(ctx, DG_EINVAL, "rows in [1, 4096], E in [1, 256], k in [1, min(8, E)] required");
   if ((long long)n_experts * ((rows + 31) / 32) > 16384)
     return fail(ctx, DG_EINVAL, "E * ceil(rows / 32) must be <= 16384");
-  HIPX(launch_moe_route(logits, rows, n_experts, top_k, idx, gates, counts, offsets, perm, nullptr,
-                        reinterpret_cast<hipStream_t>(stream)));
+  uint32_t* bm = nullptr;
+  int32_t* done = nullptr;
+  TRY(route_scratch(&bm, &done));
+  RouteArgs r{};
+  r.mode = ROUTE_LOGITS; r.rows = rows; r.E = n_experts; r.k = top_k;
+  r.logits = logits; r.logit_parts = 1;
+  r.idx = idx; r.gates = gates;
+  r.counts = counts; r.offsets = offsets; r.perm = perm;
+  r.bm = bm; r.done = done;
+  HIPX(launch_route(r, reinterpret_cast<hipStream_t>(stream)));
   return DG_OK;
 }
 
@@ -711,8 +802,7 @@ dg_status dg_k_moe_ffn(dg_ctx* ctx, int32_t layer, int32_t batch, const void* f,
   const int M = batch * c.canvas_len, K = c.top_k, H = c.hidden;
   HIPX(hipMemcpyAsync(ctx->idx, idx, (size_t)M * K * 4, hipMemcpyDeviceToDevice, ctx->st));
   HIPX(hipMemcpyAsync(ctx->gates, gates, (size_t)M * K * 4, hipMemcpyDeviceToDevice, ctx->st));
-  HIPX(launch_moe_route(nullptr, M, c.n_experts, K, ctx->idx, ctx->gates, nullptr, ctx->offsets, ctx->perm,
-                        ctx->arows, ctx->st));
+  TRY(enqueue_route(ctx, layer, M, ROUTE_GIVEN));
   TRY(enqueue_experts(ctx, layer, M, f));
   HIPX(hipMemsetAsync(m, 0, (size_t)M * H * 4, ctx->st));
   NormArgs nc{};
@@ -728,7 +818,8 @@ dg_status dg_k_lm_head(dg_ctx* ctx, int32_t batch, const void* h, float* logits)
   if (!c.has_lm_head || !ctx->embed_set) return fail(ctx, DG_ESTATE, "embedding not loaded");
   if (batch < 1 || batch > c.max_batch) return fail(ctx, DG_EINVAL, "batch out of range");
   if (!h || !logits) return fail(ctx, DG_EINVAL, "h and logits are required");
-  return enqueue_dense(ctx, h, c.hidden, ctx->embed, c.hidden, c.vocab, batch * c.canvas_len, logits, c.vocab);
+  return enqueue_dense(ctx, h, c.hidden, ctx->embed, c.hidden, c.vocab, batch * c.canvas_len, logits, c.vocab,
+                       false);
 }
 
 dg_status dg_profile(dg_ctx* ctx, int32_t enable) {

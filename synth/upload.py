@@ -32,11 +32,19 @@ def prompt_kv_to_device(w: Workload, canvas: int, device="cuda"):
     return ks, vs
 
 
-def load_context(ctx, w: Workload, device="cuda", layers=None):
+def load_context(ctx, w: Workload, device="cuda", layers=None, progress: bool = False):
     """Upload every weight and prompt KV of workload ``w`` into ``ctx`` (one
     layer at a time so the caller-side staging stays one layer large)."""
+    import sys
+    import time
+
     import torch
     m = w.model
+    t0 = time.perf_counter()
+
+    def note(msg):
+        if progress:
+            print(f"[load {time.perf_counter() - t0:6.1f}s] {msg}", file=sys.stderr, flush=True)
     if m.has_lm_head:
         e = to_device(gen.embed(w), m.dtype, device)
         nf = to_device(gen.norm_final(w), m.dtype, device)
@@ -48,6 +56,7 @@ def load_context(ctx, w: Workload, device="cuda", layers=None):
         ctx.set_layer_weights(l, lw)
         torch.cuda.synchronize()
         del lw
+        note(f"layer {l} weights")
     for b in range(w.batch):
         ks, vs = prompt_kv_to_device(w, b, device)
         ctx.load_prompt_kv(b, w.prompt_len, ks, vs)
