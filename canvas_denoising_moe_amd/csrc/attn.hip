@@ -211,6 +211,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int S, int CL, in
     __syncthreads();
   }
 
+  mfma_drain();
   if (qvalid) {
     const long long rows_all = (long long)a.B * a.Hq * N;
     const long long pr = (long long)s * rows_all + row_g;

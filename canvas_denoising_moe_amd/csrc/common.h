@@ -27,6 +27,15 @@ template <typename T> DG_DEV T from_f(float v);
 template <> DG_DEV float from_f<float>(float v) { return v; }
 template <> DG_DEV bf16_t from_f<bf16_t>(float v) { return f2bf(v); }
 
+// Separation between the last MFMA of a loop and the first read of its
+// accumulators: nothing is scheduled across the barrier and 16 wait states
+// follow, more than the result latency of any 16x16 MFMA used here.
+DG_DEV void mfma_drain() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // wave64 reductions
 DG_DEV float wave_sum(float v) {
 #pragma unroll

@@ -287,6 +287,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g, EpiArgs e) {
       __syncthreads();
     }
 
+    mfma_drain();
     if (nb_valid > 0) {
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
@@ -355,79 +356,86 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs g, EpiArgs e) {
   const int KB = KBall / ksplit;  // k-steps of this split
   const int kbase = ks * KB;
 
-  // ---- weight prefetch first: the HBM stream is the long pole
-  const T* __restrict__ Bg = reinterpret_cast<const T*>(g.B) + (long long)group * g.b_group_stride;
-  const int nb0 = tile * 4 * WN + wave * WN;
-  const int nbv = g.NB - nb0;  // wave-uniform count of valid n-blocks
-  const T* bptr[WN];
-#pragma unroll
-  for (int w = 0; w < WN; ++w) bptr[w] = Bg + ((long long)(nb0 + w) * KBall + kbase) * 512 + lane * 8;
-  Frag<T> b[R][WN];
-#pragma unroll
-  for (int i = 0; i < R; ++i)
-#pragma unroll
-    for (int w = 0; w < WN; ++w)
-      b[i][w] = (i < KB && w < nbv) ? ld_frag<T>(bptr[w] + (long long)i * 512) : zero_frag<T>();
-
-  // ---- stage A rows [rs, re) into fragment order, loads batched ahead of the stores
+  // ---- A rows: gathered row indices once into LDS, then every tile load is
+  // unconditional (rows past the entry repeat its last row; those output rows
+  // are never stored, and an MFMA row depends only on its own A row)
+  __shared__ int s_rows[16];
+  if (tid < 16) {
+    const int row = min(rs + tid, re - 1);
+    long long ar = row;
+    if (g.a_rows) {
+      ar = g.a_rows[row];
+      ar = ar < 0 ? 0 : (ar >= g.a_rows_max ? g.a_rows_max - 1 : ar);
+    }
+    s_rows[tid] = (int)ar;
+  }
+  __syncthreads();
   {
-    const T* __restrict__ A = reinterpret_cast<const T*>(g.A);
+    const T* __restrict__ A = reinterpret_cast<const T*>(g.A) + kbase * 32;
     const int k8s = KB * 4;  // 8-element groups per row within the split
     const int groups8 = 16 * k8s;
-    A += kbase * 32;
-    constexpr int U = 8;
+    constexpr int U = 16;
     for (int base = tid; base < groups8; base += 256 * U) {
       Frag<T> v[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int q = base + u * 256;
-        v[u] = zero_frag<T>();
-        if (q < groups8) {
-          const int r = q / k8s, k8 = q - r * k8s;  // consecutive threads read along a row
-          const int row = rs + r;
-          if (row < re) {
-            long long ar = row;
-            if (g.a_rows) {
-              ar = g.a_rows[row];
-              ar = ar < 0 ? 0 : (ar >= g.a_rows_max ? g.a_rows_max - 1 : ar);
-            }
-            v[u] = ld_frag<T>(A + ar * g.lda + k8 * 8);
-          }
-        }
+        const int q = min(base + u * 256, groups8 - 1);  // a repeated group rewrites the same value
+        const int r = q / k8s, k8 = q - r * k8s;          // consecutive threads read along a row
+        v[u] = ld_frag<T>(A + (long long)s_rows[r] * g.lda + k8 * 8);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int q = base + u * 256;
-        if (q < groups8) {
-          const int r = q / k8s, k8 = q - r * k8s;
-          st_frag<T>(As + ((k8 >> 2) * 64 + r + 16 * (k8 & 3)) * 8, v[u]);
-        }
+        const int q = min(base + u * 256, groups8 - 1);
+        const int r = q / k8s, k8 = q - r * k8s;
+        st_frag<T>(As + ((k8 >> 2) * 64 + r + 16 * (k8 & 3)) * 8, v[u]);
       }
     }
   }
+
+  // ---- W stream: R k-steps in flight per wave.  Loads in the steady-state
+  // loop are unconditional so the compiler's wait counts stay exact (a
+  // conditional load would make it wait for every outstanding load).
+  const T* __restrict__ Bg = reinterpret_cast<const T*>(g.B) + (long long)group * g.b_group_stride;
+  const int nb0 = tile * 4 * WN + wave * WN;
+  const int nbv = g.NB - nb0;  // wave-uniform count of valid n-blocks (others computed, not stored)
+  const T* bptr[WN];
+#pragma unroll
+  for (int w = 0; w < WN; ++w) {
+    const int nb = min(nb0 + w, g.NB - 1);
+    bptr[w] = Bg + ((long long)nb * KBall + kbase) * 512 + lane * 8;
+  }
+  Frag<T> b[R][WN];
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int w = 0; w < WN; ++w) b[i][w] = ld_frag<T>(bptr[w] + (long long)min(i, KB - 1) * 512);
   __syncthreads();
 
   floatx4 acc[WN];
 #pragma unroll
   for (int w = 0; w < WN; ++w) acc[w] = floatx4{0.f, 0.f, 0.f, 0.f};
-  if (nbv > 0) {
-    for (int kb0 = 0; kb0 < KB; kb0 += R) {
+  // One branch-free loop over ceil(KB / R) groups: k-steps past the end use a
+  // zero A fragment (adding nothing) and their refill loads are clamped to the
+  // last k-step (served from cache).  Keeping the accumulators in one loop with
+  // no peeled tail also keeps them in place: a peeled tail made the register
+  // allocator copy them out of the accumulator registers right behind the last
+  // MFMA, and those reads returned values the MFMA had not yet written.
+  const T* Ap = As + lane * 8;
+  for (int kb0 = 0; kb0 < KB; kb0 += R) {
 #pragma unroll
-      for (int i = 0; i < R; ++i) {
-        const int kb = kb0 + i;
-        if (kb < KB) {
-          const Frag<T> a = ld_frag<T>(As + (kb * 64 + lane) * 8);
+    for (int i = 0; i < R; ++i) {
+      const int kb = kb0 + i;
+      Frag<T> a = ld_frag<T>(Ap + min(kb, KB - 1) * 512);
+      if (kb >= KB) a = zero_frag<T>();
 #pragma unroll
-          for (int w = 0; w < WN; ++w) mma(acc[w], a, b[i][w]);
-          const int kn = kb + R;
-          if (kn < KB) {
+      for (int w = 0; w < WN; ++w) mma(acc[w], a, b[i][w]);
+      const int kn = min(kb + R, KB - 1);
 #pragma unroll
-            for (int w = 0; w < WN; ++w)
-              if (w < nbv) b[i][w] = ld_frag<T>(bptr[w] + (long long)kn * 512);
-          }
-        }
-      }
+      for (int w = 0; w < WN; ++w) b[i][w] = ld_frag<T>(bptr[w] + (long long)kn * 512);
     }
+  }
+  mfma_drain();
+  if (nbv > 0) {
     const int c = lane & 15, rg = (lane >> 4) * 4;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -453,8 +461,9 @@ hipError_t run_stream(const StreamArgs& g, const EpiArgs& e, hipStream_t s) {
   const size_t lds = (size_t)16 * (g.K / ksplit) * sizeof(T);
   static bool attr_set = false;  // one attribute call per instantiation
   if (!attr_set) {
+    // 16 rows x 4096 bf16 (or 2048 fp32) = 128 KB; the kernel's static LDS comes on top
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_stream<T, WN, EPI, R>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
     if (err != hipSuccess) return err;
     attr_set = true;
   }
