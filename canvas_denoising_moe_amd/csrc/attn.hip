@@ -212,7 +212,18 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int S, int CL, in
   }
 
   mfma_drain();
-  if (qvalid) {
+  if (qvalid && S == 1) {
+    // a single split: normalise and store the bf16 output directly
+    bf16_t* o = reinterpret_cast<bf16_t*>(a.o) + ((long long)b * N + qi) * a.Hq * D + (long long)qh * D;
+    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+      const int d = db * 16 + lg * 4;
+      *reinterpret_cast<uint2*>(o + d) =
+          make_uint2((uint32_t)f2bf(oacc[db][0] * inv) | ((uint32_t)f2bf(oacc[db][1] * inv) << 16),
+                     (uint32_t)f2bf(oacc[db][2] * inv) | ((uint32_t)f2bf(oacc[db][3] * inv) << 16));
+    }
+  } else if (qvalid) {
     const long long rows_all = (long long)a.B * a.Hq * N;
     const long long pr = (long long)s * rows_all + row_g;
     float* po = a.part_o + pr * D;
@@ -234,14 +245,34 @@ __global__ void k_attn_merge(AttnArgs a, int S) {
   const long long row = blockIdx.x;
   const int d = threadIdx.x;
   if (d >= a.D) return;
+  constexpr int U = 8;  // splits whose loads are in flight together
   float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, a.part_m[s * rows_all + row]);
+  for (int s0 = 0; s0 < S; s0 += U) {
+    float mv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) mv[u] = s0 + u < S ? a.part_m[(s0 + u) * rows_all + row] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) M = fmaxf(M, mv[u]);
+  }
   float num = 0.f, den = 0.f;
   if (M != -INFINITY) {
-    for (int s = 0; s < S; ++s) {
-      const float w = exp2f(a.part_m[s * rows_all + row] - M);
-      num += w * a.part_o[(s * rows_all + row) * a.D + d];
-      den += w * a.part_l[s * rows_all + row];
+    for (int s0 = 0; s0 < S; s0 += U) {
+      float mv[U], ov[U], lv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int s = min(s0 + u, S - 1);
+        mv[u] = a.part_m[s * rows_all + row];
+        ov[u] = a.part_o[(s * rows_all + row) * a.D + d];
+        lv[u] = a.part_l[s * rows_all + row];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (s0 + u < S) {  // splits in order
+          const float w = exp2f(mv[u] - M);
+          num += w * ov[u];
+          den += w * lv[u];
+        }
+      }
     }
   }
   const int i = (int)(row % a.N);
@@ -318,12 +349,13 @@ __global__ __launch_bounds__(256) void k_attn_simple(AttnArgs a) {
 
 }  // namespace
 
-// Split count and length: aim for ~1024 workgroups; splits are whole 64-key tiles.
+// Split count and length: enough workgroups to cover the 256 CUs once, and no
+// split longer than 4096 keys (long prompts); splits are whole 64-key tiles.
 static void choose_splits(const AttnArgs& a, int QT, int* S_out, int* CL_out) {
   int maxtot = 0;
   for (int b = 0; b < a.B; ++b) maxtot = max(maxtot, a.lw[b] + (a.canvas_keys ? a.N : 0));
   const long long base = (long long)a.B * a.Hkv * QT;
-  int S = (int)((1024 + base - 1) / base);
+  int S = max((int)((256 + base - 1) / base), (maxtot + 4095) / 4096);
   const int tiles = (maxtot + 63) / 64;
   if (S > tiles) S = tiles;
   if (S < 1) S = 1;
@@ -353,7 +385,7 @@ hipError_t launch_attention(int is_bf16, const AttnArgs& a, hipStream_t st) {
     else
       hipLaunchKernelGGL(k_attn_mfma<64>, grid, dim3(256), 0, st, a, S, CL, QT, xcd_map);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || S == 1) return e;  // one split: the kernel stored the output itself
     hipLaunchKernelGGL(k_attn_merge<bf16_t>, dim3((unsigned)rows_all), dim3(a.D), 0, st, a, S);
     return hipGetLastError();
   }

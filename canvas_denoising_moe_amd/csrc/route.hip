@@ -1,25 +1,25 @@
-// MoE routing of a decoder layer (one launch):
+// MoE routing of a decoder layer (two launches):
 //
-//   1. top-k of the router logits per token (logit descending, ties to the
-//      lower expert) and gates = softmax over the kept logits
-//      ([4xFaster] "DiffusionGemma's Technical Architecture": 8 of 128 experts
-//      active); the logits may arrive as split-K partial sums, added here in a
-//      fixed order;
-//   2. token -> expert scatter: per-expert counts and offsets, the rows of
-//      every expert in ascending token order, and the work list of <= 16-row
-//      entries the streaming expert GEMMs consume.
+//   k_route_topk: top-k of the router logits per token (logit descending, ties
+//     to the lower expert) and gates = softmax over the kept logits
+//     ([4xFaster] "DiffusionGemma's Technical Architecture": 8 of 128 experts
+//     active); the logits may arrive as split-K partial sums, added here in a
+//     fixed order.  One wave per token; expert membership is recorded as bits
+//     (expert, token) with device-scope atomicOr, which is order-independent.
+//   k_route_scatter: one workgroup turns the bitmap into per-expert counts and
+//     offsets, the rows of every expert in ascending token order, and the work
+//     list of <= 16-row entries the streaming expert GEMMs consume; it then
+//     clears the bitmap for the next launch.
 //
-// Step 1 runs one wave per token, four tokens per workgroup.  Expert
-// membership is accumulated as bits (expert, token) with device-scope
-// atomicOr, which is order-independent; the last workgroup to finish (a
-// device-scope ticket) turns the bitmap into counts, offsets, ranks and the
-// work list, then clears the bitmap and the ticket for the next launch, so
-// the result never depends on scheduling and no host-side reset is needed.
+// The result never depends on scheduling, and the kernel boundary between the
+// two steps provides the device-wide visibility a single-launch version would
+// need device-scope fences for.
 #include "common.h"
 
 namespace {
 
 constexpr int kRowsPerBlock = 4;
+constexpr int kBmLds = 4096;  // bitmap words staged in LDS (128 experts x 4096 tokens / 32)
 
 DG_DEV void argmax_pair(float& v, int& e) {
 #pragma unroll
@@ -30,92 +30,100 @@ DG_DEV void argmax_pair(float& v, int& e) {
   }
 }
 
-__global__ __launch_bounds__(256) void k_route(RouteArgs a) {
+__global__ __launch_bounds__(256) void k_route_topk(RouteArgs a) {
   __shared__ float rs[kRowsPerBlock * 256];
-  __shared__ int s_last;
   const int E = a.E, K = a.k;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = blockIdx.x * kRowsPerBlock + wave;
-  const bool row_ok = t < a.rows;
   const int W = (a.rows + 31) >> 5;
 
-  if (a.mode == ROUTE_LOGITS) {
-    const int parts = a.logit_parts > 0 ? a.logit_parts : 1;
-    for (int u = tid; u < kRowsPerBlock * E; u += 256) {
-      const int r = u / E, e = u % E;
-      const int tt = blockIdx.x * kRowsPerBlock + r;
-      float s = 0.f;
-      if (tt < a.rows)
-        for (int q = 0; q < parts; ++q) s += a.logits[q * a.part_stride + (long long)tt * E + e];
-      rs[r * E + e] = s;
-      if (a.r_out && tt < a.rows) a.r_out[(long long)tt * E + e] = s;
-    }
-    __syncthreads();
-  }
-
-  // ---- 1. top-k and gates, one wave per token
-  if (row_ok) {
-    if (a.mode == ROUTE_LOGITS) {
-      const float* rr = rs + wave * E;
-      float sel_v[8];
-      int sel_e[8];
-      unsigned used = 0u;  // bit j: expert lane + 64 j taken
-      for (int s = 0; s < K; ++s) {
-        float v = -INFINITY;
-        int be = 0x7fffffff;
-        for (int j = 0; j * 64 + lane < E; ++j) {
-          if (used & (1u << j)) continue;
-          const int e = j * 64 + lane;
-          const float x = rr[e];
-          if (be == 0x7fffffff || x > v || (x == v && e < be)) { v = x; be = e; }
-        }
-        argmax_pair(v, be);
-        if ((be & 63) == lane) used |= 1u << (be >> 6);
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if (q == s) { sel_v[q] = v; sel_e[q] = be; }
-      }
-      if (lane == 0) {
-        float ex[8], sum = 0.f;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          ex[q] = q < K ? expf(sel_v[q] - sel_v[0]) : 0.f;
-          sum += ex[q];
-        }
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if (q < K) {
-            a.idx[(long long)t * K + q] = sel_e[q];
-            a.gates[(long long)t * K + q] = ex[q] / sum;
-          }
-      }
-      // every lane holds sel_e; lanes < K set the membership bits
-      if (lane < K) {
-        int e = 0;
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-          if (q == lane) e = sel_e[q];
-        atomicOr(&a.bm[e * W + (t >> 5)], 1u << (t & 31));
-      }
-    } else if (lane < K) {
+  if (a.mode == ROUTE_GIVEN) {
+    if (t < a.rows && lane < K) {
       int e = a.idx[(long long)t * K + lane];
       e = e < 0 ? 0 : (e >= E ? E - 1 : e);  // out-of-range ids must not leave the bitmap
       atomicOr(&a.bm[e * W + (t >> 5)], 1u << (t & 31));
     }
+    return;
   }
 
-  // ---- 2. the last workgroup builds the scatter
-  __threadfence();
+  const int parts = a.logit_parts > 0 ? a.logit_parts : 1;
+  for (int u = tid; u < kRowsPerBlock * E; u += 256) {
+    const int r = u / E, e = u % E;
+    const int tt = blockIdx.x * kRowsPerBlock + r;
+    float pv[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)  // all partial loads in flight together
+      pv[q] = (tt < a.rows && q < parts) ? a.logits[q * a.part_stride + (long long)tt * E + e] : 0.f;
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (q < parts) s += pv[q];  // fixed order
+    rs[r * E + e] = s;
+    if (a.r_out && tt < a.rows) a.r_out[(long long)tt * E + e] = s;
+  }
   __syncthreads();
-  if (tid == 0) s_last = atomicAdd(a.done, 1) == (int)gridDim.x - 1;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+  if (t >= a.rows) return;
+
+  const float* rr = rs + wave * E;
+  float sel_v[8];
+  int sel_e[8];
+  unsigned used = 0u;  // bit j: expert lane + 64 j taken
+  for (int s = 0; s < K; ++s) {
+    float v = -INFINITY;
+    int be = 0x7fffffff;
+    for (int j = 0; j * 64 + lane < E; ++j) {
+      if (used & (1u << j)) continue;
+      const int e = j * 64 + lane;
+      const float x = rr[e];
+      if (be == 0x7fffffff || x > v || (x == v && e < be)) { v = x; be = e; }
+    }
+    argmax_pair(v, be);
+    if ((be & 63) == lane) used |= 1u << (be >> 6);
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (q == s) { sel_v[q] = v; sel_e[q] = be; }
+  }
+  if (lane == 0) {
+    float ex[8], sum = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      ex[q] = q < K ? expf(sel_v[q] - sel_v[0]) : 0.f;
+      sum += ex[q];
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (q < K) {
+        a.idx[(long long)t * K + q] = sel_e[q];
+        a.gates[(long long)t * K + q] = ex[q] / sum;
+      }
+  }
+  // every lane holds sel_e; lanes < K set the membership bits
+  if (lane < K) {
+    int e = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (q == lane) e = sel_e[q];
+    atomicOr(&a.bm[e * W + (t >> 5)], 1u << (t & 31));
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_route_scatter(RouteArgs a) {
+  __shared__ uint32_t bml[kBmLds];
   __shared__ int s_cnt[256], s_off[258], s_ent[256];
   __shared__ int s_total;
-  for (int e = tid; e < E; e += 256) {
+  const int E = a.E, K = a.k;
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int W = (a.rows + 31) >> 5;
+  // the membership bitmap into LDS (coalesced, all loads in flight); counts and
+  // ranks then read LDS
+  const bool bm_in_lds = E * W <= kBmLds;
+  if (bm_in_lds)
+    for (int i = tid; i < E * W; i += nt) bml[i] = a.bm[i];
+  __syncthreads();
+  const uint32_t* bmr = bm_in_lds ? bml : a.bm;
+  for (int e = tid; e < E; e += nt) {
     int c = 0;
-    for (int w = 0; w < W; ++w) c += __popc(a.bm[e * W + w]);
+    for (int w = 0; w < W; ++w) c += __popc(bmr[e * W + w]);
     s_cnt[e] = c;
     if (a.counts) a.counts[e] = c;
   }
@@ -137,38 +145,49 @@ __global__ __launch_bounds__(256) void k_route(RouteArgs a) {
   }
   __syncthreads();
   if (a.offsets)
-    for (int e = tid; e < E + 2; e += 256) a.offsets[e] = s_off[e];
+    for (int e = tid; e < E + 2; e += nt) a.offsets[e] = s_off[e];
   if (a.work) {
-    for (int e = tid; e < E; e += 256) {
+    for (int e = tid; e < E; e += nt) {
       const int c = s_cnt[e], base = s_off[e];
       for (int q = 0; q * 16 < c; ++q)
         a.work[s_ent[e] + q] = make_int4(e, base + q * 16, base + min(c, q * 16 + 16), 0);
     }
     const int ne = s_total - n_shared;
-    for (int q = tid; q < n_shared; q += 256)
+    for (int q = tid; q < n_shared; q += nt)
       a.work[ne + q] = make_int4(E, RK + q * 16, RK + min(a.rows, q * 16 + 16), 0);
   }
-  for (int p = tid; p < RK; p += 256) {
-    const int tt = p / K;
-    int e = a.idx[p];
-    e = e < 0 ? 0 : (e >= E ? E - 1 : e);
-    const uint32_t* row = a.bm + e * W;
-    const int wt = tt >> 5;
-    int rank = __popc(row[wt] & ((1u << (tt & 31)) - 1u));
-    for (int w = 0; w < wt; ++w) rank += __popc(row[w]);
-    const int pos = s_off[e] + rank;
-    if (a.perm) a.perm[pos] = p;
-    if (a.a_rows) a.a_rows[pos] = tt;
+  for (int p0 = tid; p0 < RK; p0 += nt * 8) {
+    int ev[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {  // expert ids of 8 entries in flight together
+      const int p = p0 + u * nt;
+      ev[u] = p < RK ? a.idx[p] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = p0 + u * nt;
+      if (p < RK) {
+        const int tt = p / K;
+        int e = ev[u];
+        e = e < 0 ? 0 : (e >= E ? E - 1 : e);
+        const uint32_t* row = bmr + e * W;
+        const int wt = tt >> 5;
+        int rank = __popc(row[wt] & ((1u << (tt & 31)) - 1u));
+        for (int w = 0; w < wt; ++w) rank += __popc(row[w]);
+        const int pos = s_off[e] + rank;
+        if (a.perm) a.perm[pos] = p;
+        if (a.a_rows) a.a_rows[pos] = tt;
+      }
+    }
   }
   if (a.with_shared) {
-    for (int tt = tid; tt < a.rows; tt += 256) {
+    for (int tt = tid; tt < a.rows; tt += nt) {
       if (a.perm) a.perm[RK + tt] = RK + tt;
       if (a.a_rows) a.a_rows[RK + tt] = tt;
     }
   }
   __syncthreads();
-  for (int i = tid; i < E * W; i += 256) a.bm[i] = 0u;
-  if (tid == 0) *a.done = 0;
+  for (int i = tid; i < E * W; i += nt) a.bm[i] = 0u;
 }
 
 }  // namespace
@@ -177,6 +196,9 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
   if (a.E > 256 || a.k > 8 || (a.mode != ROUTE_LOGITS && a.mode != ROUTE_GIVEN)) return hipErrorInvalidValue;
   const int blocks = (a.rows + kRowsPerBlock - 1) / kRowsPerBlock;
-  hipLaunchKernelGGL(k_route, dim3(blocks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_route_topk, dim3(blocks), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_route_scatter, dim3(1), dim3(1024), 0, s, a);
   return hipGetLastError();
 }

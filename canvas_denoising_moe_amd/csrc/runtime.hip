@@ -54,10 +54,9 @@ struct dg_ctx {
   int32_t *idx = nullptr, *offsets = nullptr, *perm = nullptr, *arows = nullptr, *pred = nullptr;
   long long part_cap = 0;
   int32_t* trace = nullptr;
-  // router scatter state: membership bitmap and ticket (kept zero between launches),
+  // router scatter state: membership bitmap (kept zero between launches),
   // expert work list
   uint32_t* bm = nullptr;
-  int32_t* done = nullptr;
   int4* work = nullptr;
   int32_t* work_count = nullptr;
   std::string err;
@@ -143,26 +142,23 @@ void prof_stop(dg_ctx* ctx, int kind, hipEvent_t s) {
 }
 
 // Scratch of the context-free routing entry point: membership bitmap for up to
-// 256 experts x 4096 rows and the completion ticket, per device, allocated on
-// first use and kept zero between launches by the kernel itself.
-dg_status route_scratch(uint32_t** bm, int32_t** done) {
+// 256 experts x 4096 rows, per device, allocated on first use and kept zero
+// between launches by the kernels themselves.
+dg_status route_scratch(uint32_t** bm) {
   static uint32_t* s_bm[DG_MAX_BATCH] = {};
-  static int32_t* s_done[DG_MAX_BATCH] = {};
   dg_ctx* ctx = nullptr;
   int dev = 0;
   HIPX(hipGetDevice(&dev));
   if (dev < 0 || dev >= DG_MAX_BATCH) return fail(ctx, DG_EUNSUPPORTED, "device index %d too large", dev);
   if (!s_bm[dev]) {
-    const size_t words = 256 * (4096 / 32);
+    const size_t bytes = 256 * (4096 / 32) * 4;
     void* p = nullptr;
-    HIPX(hipMalloc(&p, words * 4 + 256));
-    HIPX(hipMemset(p, 0, words * 4 + 256));
+    HIPX(hipMalloc(&p, bytes));
+    HIPX(hipMemset(p, 0, bytes));
     HIPX(hipDeviceSynchronize());
     s_bm[dev] = reinterpret_cast<uint32_t*>(p);
-    s_done[dev] = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(p) + words * 4);
   }
   *bm = s_bm[dev];
-  *done = s_done[dev];
   return DG_OK;
 }
 
@@ -263,11 +259,9 @@ dg_status alloc_workspaces(dg_ctx* ctx) {
   TRY(dalloc_t(ctx, &ctx->part_l, (size_t)ctx->part_cap * 4));
   const size_t bm_words = E * ((M + 31) / 32);
   TRY(dalloc_t(ctx, &ctx->bm, bm_words * 4));
-  TRY(dalloc_t(ctx, &ctx->done, 4));
   TRY(dalloc_t(ctx, &ctx->work, (size_t)work_cap(c, (int)M) * sizeof(int4)));
   TRY(dalloc_t(ctx, &ctx->work_count, 4));
   HIPX(hipMemset(ctx->bm, 0, bm_words * 4));
-  HIPX(hipMemset(ctx->done, 0, 4));
   HIPX(hipMemset(ctx->work_count, 0, 4));
   HIPX(hipDeviceSynchronize());
   return DG_OK;
@@ -352,7 +346,7 @@ dg_status enqueue_route(dg_ctx* ctx, int l, int M, int mode) {
   r.idx = ctx->idx; r.gates = ctx->gates;
   r.offsets = ctx->offsets; r.perm = ctx->perm; r.a_rows = ctx->arows;
   r.work = ctx->work; r.work_count = ctx->work_count;
-  r.bm = ctx->bm; r.done = ctx->done;
+  r.bm = ctx->bm;
   r.with_shared = 1;
   HIPX(launch_route(r, ctx->st));
   return DG_OK;
@@ -741,14 +735,13 @@ dg_status dg_k_moe_route(const float* logits, int32_t rows, int32_t n_experts, i
   if ((long long)n_experts * ((rows + 31) / 32) > 16384)
     return fail(ctx, DG_EINVAL, "E * ceil(rows / 32) must be <= 16384");
   uint32_t* bm = nullptr;
-  int32_t* done = nullptr;
-  TRY(route_scratch(&bm, &done));
+  TRY(route_scratch(&bm));
   RouteArgs r{};
   r.mode = ROUTE_LOGITS; r.rows = rows; r.E = n_experts; r.k = top_k;
   r.logits = logits; r.logit_parts = 1;
   r.idx = idx; r.gates = gates;
   r.counts = counts; r.offsets = offsets; r.perm = perm;
-  r.bm = bm; r.done = done;
+  r.bm = bm;
   HIPX(launch_route(r, reinterpret_cast<hipStream_t>(stream)));
   return DG_OK;
 }

@@ -216,7 +216,9 @@ dg_status dg_k_canvas_attn(dg_ctx* ctx, int32_t layer, int32_t batch, const void
  * int32 [batch*N, k], gates float [batch*N, k] -> m float [batch*N, H] =
  * sum_s gates[t,s] * FFN_idx[t,s](f_t) + FFN_shared(f_t), with
  * FFN(z) = (gelu_tanh(z Wg) * (z Wu)) Wd and the gated activation stored as
- * T ([HandsOn] "Detailed Specs": GELU-tanh gated MLP). */
+ * T ([HandsOn] "Detailed Specs": GELU-tanh gated MLP).  The k ids of a row
+ * must be distinct and in [0, E): ids out of range are clamped, and a
+ * repeated id yields an unspecified (finite, in-bounds) result. */
 dg_status dg_k_moe_ffn(dg_ctx* ctx, int32_t layer, int32_t batch, const void* f,
                        const int32_t* idx, const float* gates, float* m);
 

@@ -194,6 +194,36 @@ def test_canvas_attention_matches_oracle(torch, actx, layer, lens, ck):
     assert e <= TOL["bf16"]
 
 
+MHA_MODEL = configs.ModelConfig(
+    n_layers=1, hidden=2048, n_heads=32, n_kv_heads=32, head_dim=128, n_experts=16, top_k=8,
+    expert_ffn=64, vocab=0, canvas_len=256, window=1024, global_layer_mask=0b1,
+    has_lm_head=False, dtype="bf16")
+MHA_W = configs.Workload(name="attn-mha-test", model=MHA_MODEL, batch=2, prompt_len=100, n_steps=1, seed=17)
+
+
+def test_canvas_attention_single_split(torch, dg):
+    # 2 canvases x 32 KV heads x 4 query tiles fill the chip without key splits,
+    # so the attention kernel normalises and stores its output itself
+    m = MHA_MODEL
+    say("attention single split")
+    with dg.Context(m, max_batch=2, max_prompt_len=128) as ctx:
+        ctx.set_layer_weights(0, upload.layer_to_device(MHA_W, 0))
+        kv = _load_prompts(torch, ctx, MHA_W, [100, 37])
+        B, N = 2, m.canvas_len
+        qb = gen.activations(18, 3, (B, N, m.n_heads, m.head_dim), std=1.0, dtype="bf16")
+        kb = gen.activations(18, 4, (B, N, m.n_kv_heads, m.head_dim), std=1.0, dtype="bf16")
+        vb = gen.activations(18, 5, (B, N, m.n_kv_heads, m.head_dim), std=1.0, dtype="bf16")
+        o = torch.empty((B, N, m.n_heads * m.head_dim), dtype=torch.bfloat16, device="cuda")
+        ctx.k_canvas_attn(0, B, upload.to_device(qb, "bf16"), upload.to_device(kb, "bf16"),
+                          upload.to_device(vb, "bf16"), o)
+        torch.cuda.synchronize()
+    ref = om.canvas_attention(om.bf16_bits_to_f64(qb), om.bf16_bits_to_f64(kb), om.bf16_bits_to_f64(vb),
+                              [kv[b][0] for b in range(B)], om.bf16_round)
+    e = rel_err(host64(o).reshape(B * N, -1), ref)
+    print(f"attention single split: rel err {e:.3e}")
+    assert e <= TOL["bf16"]
+
+
 def test_single_cached_kv_returns_that_value_bit_exact(torch, actx):
     m = ATTN_MODEL
     say("attention single cached kv")
