@@ -73,7 +73,7 @@ _SIGS = {
     "dg_profile_read": (c_int32, [c_void_p, c_int32, POINTER(c_int32), POINTER(ctypes.c_double)]),
 }
 
-PROF_GATE_UP, PROF_DOWN, PROF_ATTN, PROF_LM_HEAD, PROF_PASS = range(5)
+PROF_GATE_UP, PROF_DOWN, PROF_ATTN, PROF_LM_HEAD, PROF_PASS, PROF_COUNT = range(6)
 
 
 def lib():
@@ -246,8 +246,15 @@ class Context:
         self._c(lib().dg_set_trace(self._h, _ptr(route_idx, torch.int32, "route_idx")))
 
     # -- kernel timing -------------------------------------------------------------
-    def profile(self, enable: bool):
-        self._c(lib().dg_profile(self._h, int(bool(enable))))
+    def profile(self, kernels=()):
+        """Time the given kernel classes (PROF_* ids; True = all, () = off)."""
+        if kernels is True:
+            mask = (1 << PROF_COUNT) - 1
+        else:
+            mask = 0
+            for k in (kernels or ()):
+                mask |= 1 << int(k)
+        self._c(lib().dg_profile(self._h, mask))
 
     def profile_read(self, kernel: int):
         """(launches, total milliseconds) recorded for a kernel class."""

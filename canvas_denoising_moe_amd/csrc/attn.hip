@@ -369,7 +369,7 @@ static void choose_splits(const AttnArgs& a, int QT, int* S_out, int* CL_out) {
   *CL_out = CL;
 }
 
-hipError_t launch_attention(int is_bf16, const AttnArgs& a, hipStream_t st) {
+hipError_t launch_attention(int is_bf16, const AttnArgs& a, hipStream_t st, KTime t) {
   const long long rows_all = (long long)a.B * a.Hq * a.N;
   if (rows_all == 0) return hipSuccess;
   if (is_bf16 && (a.D == 128 || a.D == 64)) {
@@ -380,19 +380,17 @@ hipError_t launch_attention(int is_bf16, const AttnArgs& a, hipStream_t st) {
     const long long units = (long long)a.B * a.Hkv * S;
     const int xcd_map = (units % 8) == 0;
     const dim3 grid((unsigned)(units * QT));
-    if (a.D == 128)
-      hipLaunchKernelGGL(k_attn_mfma<128>, grid, dim3(256), 0, st, a, S, CL, QT, xcd_map);
-    else
-      hipLaunchKernelGGL(k_attn_mfma<64>, grid, dim3(256), 0, st, a, S, CL, QT, xcd_map);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || S == 1) return e;  // one split: the kernel stored the output itself
-    hipLaunchKernelGGL(k_attn_merge<bf16_t>, dim3((unsigned)rows_all), dim3(a.D), 0, st, a, S);
-    return hipGetLastError();
+    // one split: the kernel stores the output itself and closes the timing
+    hipEvent_t stop1 = S == 1 ? t.stop : nullptr;
+    hipError_t e = a.D == 128
+        ? launch_k(k_attn_mfma<128>, grid, dim3(256), 0, st, t.start, stop1, a, S, CL, QT, xcd_map)
+        : launch_k(k_attn_mfma<64>, grid, dim3(256), 0, st, t.start, stop1, a, S, CL, QT, xcd_map);
+    if (e != hipSuccess || S == 1) return e;
+    return launch_k(k_attn_merge<bf16_t>, dim3((unsigned)rows_all), dim3(a.D), 0, st, nullptr, t.stop,
+                    a, S);
   }
   if (a.D > 256) return hipErrorInvalidValue;
   if (is_bf16)
-    hipLaunchKernelGGL(k_attn_simple<bf16_t>, dim3((unsigned)rows_all), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(k_attn_simple<float>, dim3((unsigned)rows_all), dim3(256), 0, st, a);
-  return hipGetLastError();
+    return launch_k(k_attn_simple<bf16_t>, dim3((unsigned)rows_all), dim3(256), 0, st, t.start, t.stop, a);
+  return launch_k(k_attn_simple<float>, dim3((unsigned)rows_all), dim3(256), 0, st, t.start, t.stop, a);
 }

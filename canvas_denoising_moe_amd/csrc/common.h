@@ -1,6 +1,7 @@
 // Shared device helpers and launcher declarations of the gfx950 kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -64,6 +65,21 @@ DG_DEV float block_sum(float v, float* red) {
 // launchers (implemented in the .hip files); all return hipError_t
 // ----------------------------------------------------------------------------
 
+// Optional timing of one launcher call: `start` takes the start time of its
+// first kernel and `stop` the end time of its last one.  The events are bound
+// to the kernel dispatches themselves, so timing adds no packets to the stream.
+struct KTime { hipEvent_t start = nullptr, stop = nullptr; };
+
+template <typename F, typename... Args>
+inline hipError_t launch_k(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                           hipEvent_t ev0, hipEvent_t ev1, Args... args) {
+  if (ev0 || ev1)
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, ev0, ev1, 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+  return hipGetLastError();
+}
+
 // Weight repack into matrix-core fragment order:
 //   dst[((nb*KB + kb)*64 + lane)*8 + j] = W(k = kb*32 + (lane/16)*8 + j,
 //                                           n = colmap(nb)*16 + lane%16)
@@ -101,7 +117,8 @@ struct EpiArgs {
   const float2* rope_cs;               // [batch][N][D/2] (cos, sin)
   int N, D, Hq, Hkv, n_rot_local, n_rot_global, is_global;
 };
-hipError_t launch_gemm(int is_bf16, const GemmArgs& g, const EpiArgs& e, int mt, hipStream_t s);
+hipError_t launch_gemm(int is_bf16, const GemmArgs& g, const EpiArgs& e, int mt, hipStream_t s,
+                       KTime t = {});
 
 // Streaming GEMM over work entries of <= 16 rows (see gemm.hip).  Dense entries
 // cover rows [dense_row0, dense_row0 + dense_rows) of group dense_group in steps
@@ -118,7 +135,8 @@ struct StreamArgs {
   // partial sums at out + s * split_stride
   int ksplit; long long split_stride;
 };
-hipError_t launch_stream(int is_bf16, const StreamArgs& g, const EpiArgs& e, hipStream_t s);
+hipError_t launch_stream(int is_bf16, const StreamArgs& g, const EpiArgs& e, hipStream_t s,
+                         KTime t = {});
 
 // Attention.
 #define DG_MAX_BATCH 64
@@ -134,7 +152,7 @@ struct AttnArgs {
   const void* vp[DG_MAX_BATCH];  // per canvas: prompt V^T [Hkv][D][Lw]
   int lw[DG_MAX_BATCH];          // per canvas: prompt keys visible to the layer
 };
-hipError_t launch_attention(int is_bf16, const AttnArgs& a, hipStream_t s);
+hipError_t launch_attention(int is_bf16, const AttnArgs& a, hipStream_t s, KTime t = {});
 
 // Routing, combine, norms.
 // MoE routing (route.hip).  ROUTE_LOGITS: top-k + gates of the router logits

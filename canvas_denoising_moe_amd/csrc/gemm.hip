@@ -356,6 +356,25 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs g, EpiArgs e) {
   const int KB = KBall / ksplit;  // k-steps of this split
   const int kbase = ks * KB;
 
+  // ---- W stream: R k-steps in flight per wave, issued first so the weight
+  // stream is already under way while A is staged.  Loads in the steady-state
+  // loop are unconditional so the compiler's wait counts stay exact (a
+  // conditional load would make it wait for every outstanding load).
+  const T* __restrict__ Bg = reinterpret_cast<const T*>(g.B) + (long long)group * g.b_group_stride;
+  const int nb0 = tile * 4 * WN + wave * WN;
+  const int nbv = g.NB - nb0;  // wave-uniform count of valid n-blocks (others computed, not stored)
+  const T* bptr[WN];
+#pragma unroll
+  for (int w = 0; w < WN; ++w) {
+    const int nb = min(nb0 + w, g.NB - 1);
+    bptr[w] = Bg + ((long long)nb * KBall + kbase) * 512 + lane * 8;
+  }
+  Frag<T> b[R][WN];
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int w = 0; w < WN; ++w) b[i][w] = ld_frag<T>(bptr[w] + (long long)min(i, KB - 1) * 512);
+
   // ---- A rows: gathered row indices once into LDS, then every tile load is
   // unconditional (rows past the entry repeat its last row; those output rows
   // are never stored, and an MFMA row depends only on its own A row)
@@ -374,7 +393,7 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs g, EpiArgs e) {
     const T* __restrict__ A = reinterpret_cast<const T*>(g.A) + kbase * 32;
     const int k8s = KB * 4;  // 8-element groups per row within the split
     const int groups8 = 16 * k8s;
-    constexpr int U = 16;
+    constexpr int U = sizeof(T) == 2 ? 16 : 8;  // loads in flight, bounded by the W ring's registers
     for (int base = tid; base < groups8; base += 256 * U) {
       Frag<T> v[U];
 #pragma unroll
@@ -391,24 +410,6 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs g, EpiArgs e) {
       }
     }
   }
-
-  // ---- W stream: R k-steps in flight per wave.  Loads in the steady-state
-  // loop are unconditional so the compiler's wait counts stay exact (a
-  // conditional load would make it wait for every outstanding load).
-  const T* __restrict__ Bg = reinterpret_cast<const T*>(g.B) + (long long)group * g.b_group_stride;
-  const int nb0 = tile * 4 * WN + wave * WN;
-  const int nbv = g.NB - nb0;  // wave-uniform count of valid n-blocks (others computed, not stored)
-  const T* bptr[WN];
-#pragma unroll
-  for (int w = 0; w < WN; ++w) {
-    const int nb = min(nb0 + w, g.NB - 1);
-    bptr[w] = Bg + ((long long)nb * KBall + kbase) * 512 + lane * 8;
-  }
-  Frag<T> b[R][WN];
-#pragma unroll
-  for (int i = 0; i < R; ++i)
-#pragma unroll
-    for (int w = 0; w < WN; ++w) b[i][w] = ld_frag<T>(bptr[w] + (long long)min(i, KB - 1) * 512);
   __syncthreads();
 
   floatx4 acc[WN];
@@ -451,7 +452,7 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs g, EpiArgs e) {
 }
 
 template <typename T, int WN, int EPI, int R>
-hipError_t run_stream(const StreamArgs& g, const EpiArgs& e, hipStream_t s) {
+hipError_t run_stream(const StreamArgs& g, const EpiArgs& e, hipStream_t s, KTime t) {
   const int tiles = (g.NB + 4 * WN - 1) / (4 * WN);
   const int ksplit = g.ksplit > 1 ? g.ksplit : 1;
   if (((g.K >> 5) % ksplit) != 0 || (ksplit > 1 && EPI != EPI_STORE_F32)) return hipErrorInvalidValue;
@@ -467,17 +468,16 @@ hipError_t run_stream(const StreamArgs& g, const EpiArgs& e, hipStream_t s) {
     if (err != hipSuccess) return err;
     attr_set = true;
   }
-  hipLaunchKernelGGL((k_stream<T, WN, EPI, R>), dim3((unsigned)blocks), dim3(256), lds, s, g, e);
-  return hipGetLastError();
+  return launch_k(k_stream<T, WN, EPI, R>, dim3((unsigned)blocks), dim3(256), lds, s, t.start, t.stop, g, e);
 }
 
 template <typename T>
-hipError_t run_stream_t(const StreamArgs& g, const EpiArgs& e, hipStream_t s) {
+hipError_t run_stream_t(const StreamArgs& g, const EpiArgs& e, hipStream_t s, KTime t) {
   switch (e.kind) {
-    case EPI_STORE_F32: return run_stream<T, 2, EPI_STORE_F32, 8>(g, e, s);
-    case EPI_GEGLU: return run_stream<T, 2, EPI_GEGLU, 8>(g, e, s);
-    case EPI_DOWN: return run_stream<T, 2, EPI_DOWN, 8>(g, e, s);
-    case EPI_QKV: return run_stream<T, 2, EPI_QKV, 8>(g, e, s);
+    case EPI_STORE_F32: return run_stream<T, 2, EPI_STORE_F32, 8>(g, e, s, t);
+    case EPI_GEGLU: return run_stream<T, 2, EPI_GEGLU, 8>(g, e, s, t);
+    case EPI_DOWN: return run_stream<T, 2, EPI_DOWN, 8>(g, e, s, t);
+    case EPI_QKV: return run_stream<T, 2, EPI_QKV, 8>(g, e, s, t);
   }
   return hipErrorInvalidValue;
 }
@@ -515,44 +515,43 @@ __global__ void k_pack(PackArgs a, int nbatch, long long src_bs, long long dst_b
 }
 
 template <typename T, int MT, int WN, int EPI>
-hipError_t run_gemm(const GemmArgs& g, const EpiArgs& e, hipStream_t s) {
+hipError_t run_gemm(const GemmArgs& g, const EpiArgs& e, hipStream_t s, KTime t) {
   constexpr int ROWS = MT * 16;
   const int tiles = (g.NB + 4 * WN - 1) / (4 * WN);
   const int smc = (g.static_rows + ROWS - 1) / ROWS;
   const long long blocks = (long long)tiles * smc + (long long)tiles * g.n_groups;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemm<T, MT, WN, EPI>), dim3((unsigned)blocks), dim3(256), 0, s, g, e);
-  return hipGetLastError();
+  return launch_k(k_gemm<T, MT, WN, EPI>, dim3((unsigned)blocks), dim3(256), 0, s, t.start, t.stop, g, e);
 }
 
 template <typename T, int EPI>
-hipError_t run_gemm_mt(const GemmArgs& g, const EpiArgs& e, int mt, hipStream_t s) {
+hipError_t run_gemm_mt(const GemmArgs& g, const EpiArgs& e, int mt, hipStream_t s, KTime t) {
   // 128-row chunks only for bf16 (the fp32 chunk would exceed 64 KB of LDS)
   if constexpr (sizeof(T) == 2) {
-    if (mt >= 8) return run_gemm<T, 8, 2, EPI>(g, e, s);
+    if (mt >= 8) return run_gemm<T, 8, 2, EPI>(g, e, s, t);
   }
-  return run_gemm<T, 4, 2, EPI>(g, e, s);
+  return run_gemm<T, 4, 2, EPI>(g, e, s, t);
 }
 
 template <typename T>
-hipError_t run_gemm_t(const GemmArgs& g, const EpiArgs& e, int mt, hipStream_t s) {
+hipError_t run_gemm_t(const GemmArgs& g, const EpiArgs& e, int mt, hipStream_t s, KTime t) {
   switch (e.kind) {
-    case EPI_STORE_F32: return run_gemm_mt<T, EPI_STORE_F32>(g, e, mt, s);
-    case EPI_GEGLU: return run_gemm_mt<T, EPI_GEGLU>(g, e, mt, s);
-    case EPI_DOWN: return run_gemm_mt<T, EPI_DOWN>(g, e, mt, s);
-    case EPI_QKV: return run_gemm_mt<T, EPI_QKV>(g, e, mt, s);
+    case EPI_STORE_F32: return run_gemm_mt<T, EPI_STORE_F32>(g, e, mt, s, t);
+    case EPI_GEGLU: return run_gemm_mt<T, EPI_GEGLU>(g, e, mt, s, t);
+    case EPI_DOWN: return run_gemm_mt<T, EPI_DOWN>(g, e, mt, s, t);
+    case EPI_QKV: return run_gemm_mt<T, EPI_QKV>(g, e, mt, s, t);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_gemm(int is_bf16, const GemmArgs& g, const EpiArgs& e, int mt, hipStream_t s) {
-  return is_bf16 ? run_gemm_t<bf16_t>(g, e, mt, s) : run_gemm_t<float>(g, e, mt, s);
+hipError_t launch_gemm(int is_bf16, const GemmArgs& g, const EpiArgs& e, int mt, hipStream_t s, KTime t) {
+  return is_bf16 ? run_gemm_t<bf16_t>(g, e, mt, s, t) : run_gemm_t<float>(g, e, mt, s, t);
 }
 
-hipError_t launch_stream(int is_bf16, const StreamArgs& g, const EpiArgs& e, hipStream_t s) {
-  return is_bf16 ? run_stream_t<bf16_t>(g, e, s) : run_stream_t<float>(g, e, s);
+hipError_t launch_stream(int is_bf16, const StreamArgs& g, const EpiArgs& e, hipStream_t s, KTime t) {
+  return is_bf16 ? run_stream_t<bf16_t>(g, e, s, t) : run_stream_t<float>(g, e, s, t);
 }
 
 hipError_t launch_pack(int is_bf16, const PackArgs& a, hipStream_t s) {

@@ -61,8 +61,9 @@ struct dg_ctx {
   int32_t* work_count = nullptr;
   std::string err;
   std::vector<void*> owned;
-  // kernel timing: event pairs per kernel class (pool reused after a reset)
-  bool prof = false;
+  // kernel timing: classes timed (bit mask) and event pairs per class (pool
+  // reused after a reset)
+  int prof = 0;
   std::vector<hipEvent_t> ev_pool;
   size_t ev_used = 0;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> prof_rec[DG_PROF_COUNT];
@@ -128,8 +129,8 @@ hipEvent_t next_event(dg_ctx* ctx) {
   }
   return ctx->ev_pool[ctx->ev_used++];
 }
-hipEvent_t prof_start(dg_ctx* ctx) {
-  if (!ctx->prof) return nullptr;
+hipEvent_t prof_start(dg_ctx* ctx, int kind) {
+  if (!((ctx->prof >> kind) & 1)) return nullptr;
   hipEvent_t e = next_event(ctx);
   if (e && hipEventRecord(e, ctx->st) != hipSuccess) return nullptr;
   return e;
@@ -139,6 +140,18 @@ void prof_stop(dg_ctx* ctx, int kind, hipEvent_t s) {
   hipEvent_t e = next_event(ctx);
   if (!e || hipEventRecord(e, ctx->st) != hipSuccess) return;
   ctx->prof_rec[kind].push_back({s, e});
+}
+// Event pair bound to the dispatches of one launcher call (no marker packets
+// between kernels); empty when timing is off.  Every profiled launcher call
+// launches at least one kernel, so both events are always recorded.
+KTime prof_kernel(dg_ctx* ctx, int kind) {
+  KTime t;
+  if (!((ctx->prof >> kind) & 1)) return t;
+  hipEvent_t a = next_event(ctx), b = next_event(ctx);
+  if (!a || !b) return t;
+  t.start = a; t.stop = b;
+  ctx->prof_rec[kind].push_back({a, b});
+  return t;
 }
 
 // Scratch of the context-free routing entry point: membership bitmap for up to
@@ -320,9 +333,7 @@ dg_status enqueue_attention(dg_ctx* ctx, int l, int B, void* o, int canvas_keys)
     aa.vp[b] = ctx->slots[b].v[l];
     aa.lw[b] = ctx->slots[b].len[l];
   }
-  hipEvent_t ev = prof_start(ctx);
-  HIPX(launch_attention(ctx->bf16, aa, ctx->st));
-  prof_stop(ctx, DG_PROF_ATTN, ev);
+  HIPX(launch_attention(ctx->bf16, aa, ctx->st, prof_kernel(ctx, DG_PROF_ATTN)));
   return DG_OK;
 }
 
@@ -364,9 +375,7 @@ dg_status enqueue_experts(dg_ctx* ctx, int l, int M, const void* f) {
   g.work = ctx->work; g.work_count = ctx->work_count; g.work_cap = work_cap(c, M);
   EpiArgs e{};
   e.kind = EPI_GEGLU; e.out = ctx->u; e.ldo = F;
-  hipEvent_t ev = prof_start(ctx);
-  HIPX(launch_stream(ctx->bf16, g, e, ctx->st));
-  prof_stop(ctx, DG_PROF_GATE_UP, ev);
+  HIPX(launch_stream(ctx->bf16, g, e, ctx->st, prof_kernel(ctx, DG_PROF_GATE_UP)));
 
   StreamArgs d{};
   d.A = ctx->u; d.lda = F; d.a_rows = nullptr;
@@ -376,9 +385,7 @@ dg_status enqueue_experts(dg_ctx* ctx, int l, int M, const void* f) {
   EpiArgs ed{};
   ed.kind = EPI_DOWN; ed.out = ctx->y; ed.ldo = H;
   ed.slot = ctx->perm; ed.gates = ctx->gates; ed.routed_rows = M * K; ed.out_rows = M * K + M;
-  ev = prof_start(ctx);
-  HIPX(launch_stream(ctx->bf16, d, ed, ctx->st));
-  prof_stop(ctx, DG_PROF_DOWN, ev);
+  HIPX(launch_stream(ctx->bf16, d, ed, ctx->st, prof_kernel(ctx, DG_PROF_DOWN)));
   return DG_OK;
 }
 
@@ -386,18 +393,18 @@ dg_status enqueue_experts(dg_ctx* ctx, int l, int M, const void* f) {
 // 16-row tile and re-read W from L2; the LM head's 1 GB embedding is read once
 // per 64-row chunk by the chunked kernel instead.
 dg_status enqueue_dense(dg_ctx* ctx, const void* A, int lda, const void* Bp, int K, int N, int M, float* out,
-                        int ldo, bool streaming = true) {
+                        int ldo, bool streaming = true, KTime t = {}) {
   EpiArgs e{};
   e.kind = EPI_STORE_F32; e.out = out; e.ldo = ldo;
   if (streaming) {
     StreamArgs g{};
     g.A = A; g.lda = lda; g.B = Bp; g.K = K; g.NB = N / 16;
     g.n_dense = (M + 15) / 16; g.dense_rows = M;
-    HIPX(launch_stream(ctx->bf16, g, e, ctx->st));
+    HIPX(launch_stream(ctx->bf16, g, e, ctx->st, t));
   } else {
     GemmArgs g{};
     g.A = A; g.lda = lda; g.B = Bp; g.K = K; g.NB = N / 16; g.static_rows = M;
-    HIPX(launch_gemm(ctx->bf16, g, e, 4, ctx->st));
+    HIPX(launch_gemm(ctx->bf16, g, e, 4, ctx->st, t));
   }
   return DG_OK;
 }
@@ -446,9 +453,8 @@ dg_status enqueue_pass(dg_ctx* ctx, int B, int32_t* tokens, uint8_t* locked, con
   n0.x = ctx->x; n0.w_out = ctx->L[0].norm[0]; n0.out = ctx->a;
   HIPX(launch_residual_norm(ctx->bf16, n0, ctx->st));
   TRY(enqueue_layers(ctx, B, ctx->norm_final));
-  hipEvent_t ev = prof_start(ctx);
-  TRY(enqueue_dense(ctx, ctx->a, H, ctx->embed, H, c.vocab, M, ctx->logits, c.vocab, false));
-  prof_stop(ctx, DG_PROF_LM_HEAD, ev);
+  TRY(enqueue_dense(ctx, ctx->a, H, ctx->embed, H, c.vocab, M, ctx->logits, c.vocab, false,
+                    prof_kernel(ctx, DG_PROF_LM_HEAD)));
   HIPX(launch_argmax_conf(ctx->logits, M, c.vocab, ctx->pred, ctx->conf, ctx->st));
   HIPX(launch_lock_select(B, N, ctx->conf, ctx->pred, tokens, locked, steps, ctx->st));
   return DG_OK;
@@ -644,7 +650,7 @@ dg_status dg_denoise_step(dg_ctx* ctx, int32_t batch, int32_t* tokens, uint8_t* 
     if (steps_left_host[b] < 1) return fail(ctx, DG_EINVAL, "steps_left[%d] = %d < 1", b, steps_left_host[b]);
     steps.v[b] = steps_left_host[b];
   }
-  hipEvent_t evp = prof_start(ctx);
+  hipEvent_t evp = prof_start(ctx, DG_PROF_PASS);
   TRY(enqueue_pass(ctx, batch, tokens, locked, steps));
   prof_stop(ctx, DG_PROF_PASS, evp);
   const size_t M = (size_t)batch * c.canvas_len;
@@ -665,7 +671,7 @@ dg_status dg_generate_block(dg_ctx* ctx, int32_t batch, int32_t n_steps, int32_t
   for (int t = 0; t < n_steps; ++t) {
     StepsArg steps{};
     for (int b = 0; b < batch; ++b) steps.v[b] = n_steps - t;
-    hipEvent_t evp = prof_start(ctx);
+    hipEvent_t evp = prof_start(ctx, DG_PROF_PASS);
     TRY(enqueue_pass(ctx, batch, tokens, locked, steps));
     prof_stop(ctx, DG_PROF_PASS, evp);
   }
@@ -815,14 +821,15 @@ dg_status dg_k_lm_head(dg_ctx* ctx, int32_t batch, const void* h, float* logits)
                        false);
 }
 
-dg_status dg_profile(dg_ctx* ctx, int32_t enable) {
+dg_status dg_profile(dg_ctx* ctx, int32_t mask) {
   TRY(enter(ctx));
-  if (enable) {
+  if (mask & ~DG_PROF_ALL) return fail(ctx, DG_EINVAL, "profile mask 0x%x has unknown bits", mask);
+  if (mask) {
     HIPX(hipStreamSynchronize(ctx->st));  // recorded events are done before reuse
     for (auto& r : ctx->prof_rec) r.clear();
     ctx->ev_used = 0;
   }
-  ctx->prof = enable != 0;
+  ctx->prof = mask;
   return DG_OK;
 }
 

@@ -226,21 +226,25 @@ dg_status dg_k_moe_ffn(dg_ctx* ctx, int32_t layer, int32_t batch, const void* f,
 dg_status dg_k_lm_head(dg_ctx* ctx, int32_t batch, const void* h, float* logits);
 
 /* ---- kernel timing ----------------------------------------------------------
- * When on, every launch of the listed kernel classes made by the context is
- * bracketed by a pair of HIP events on the context's stream, so per-launch
- * device durations can be read back.  dg_profile(ctx, 1) clears the record and
- * switches timing on; dg_profile(ctx, 0) switches it off (the record stays).
- * dg_profile_read synchronises the stream and returns the number of recorded
- * launches of `kernel` and their summed duration in milliseconds. */
+ * Per-launch device durations of selected kernel classes.  dg_profile(ctx,
+ * mask) with mask != 0 clears the record and times every later launch of the
+ * classes whose bit (1 << DG_PROF_x) is set; mask = 0 switches timing off (the
+ * record stays).  Kernel classes are timed by HIP events bound to their own
+ * dispatches (start of the first kernel, end of the last); DG_PROF_PASS by an
+ * event pair recorded on the stream around the pass.  Each timed launch adds a
+ * few microseconds of dispatch latency around itself, so time only what is
+ * needed.  dg_profile_read synchronises the stream and returns the number of
+ * recorded launches of `kernel` and their summed duration in milliseconds. */
 typedef enum dg_prof_kernel {
   DG_PROF_GATE_UP = 0,  /* grouped expert GEMM gate|up with the gated GELU-tanh */
   DG_PROF_DOWN = 1,     /* grouped expert GEMM down with the gate scale */
   DG_PROF_ATTN = 2,     /* canvas attention (splits and merge) */
   DG_PROF_LM_HEAD = 3,  /* tied LM head GEMM */
   DG_PROF_PASS = 4,     /* one whole denoise pass */
-  DG_PROF_COUNT = 5
+  DG_PROF_COUNT = 5,
+  DG_PROF_ALL = (1 << 5) - 1
 } dg_prof_kernel;
-dg_status dg_profile(dg_ctx* ctx, int32_t enable);
+dg_status dg_profile(dg_ctx* ctx, int32_t mask);
 dg_status dg_profile_read(dg_ctx* ctx, int32_t kernel, int32_t* launches, double* total_ms);
 
 #ifdef __cplusplus
