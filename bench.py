@@ -61,13 +61,11 @@ def algorithmic(w, touched):
     return byts, flops, sum(gu_bytes) / len(gu_bytes), gu_flops
 
 
-def cpu_baseline(w, max_rows_head: int = 64):
-    """The oracle (float64 numpy) timed on a bounded sample of the workload:
-    the first group of layers up to and including the first global layer
-    (five sliding-window layers and one global layer in the 30-layer stack),
-    run in sequence over the whole canvas, and the LM head + argmax for
-    ``max_rows_head`` positions; the pass time is extrapolated to the full
-    stack and canvas (weight generation is not timed)."""
+def cpu_baseline(w):
+    """The oracle (float64 numpy) timed on one whole denoise pass of the
+    workload: every layer over every canvas position, the LM head, argmax and
+    the lock step.  Weight generation and widening to float64 happen before
+    each timed step and are not counted."""
     import numpy as np
     from oracle import model as om
     from oracle.inputs import prompt_kv_fn, weights_for
@@ -81,30 +79,28 @@ def cpu_baseline(w, max_rows_head: int = 64):
     M = w.batch * m.canvas_len
     W = weights_for(w)
     kvf = prompt_kv_fn(w)
-    tok, _ = gen.canvas(w)
+    tok, lk = gen.canvas(w)
+    rnd = om._rounder(m)
+    t_total = 0.0
+    t0 = time.perf_counter()
     x = W.embed_rows(tok.reshape(-1).astype(np.int64))
-    g_layer = next(l for l in range(m.n_layers) if m.is_global(l))
-    group = list(range(g_layer + 1))
-    t_layers = 0.0
-    for l in group:
-        lw = W.layer(l)
+    t_total += time.perf_counter() - t0
+    for l in range(m.n_layers):
+        lw = {k: np.asarray(v) for k, v in W.layer(l).items()}  # widened outside the timing
         kv = [kvf(l, b) for b in range(w.batch)]
         t0 = time.perf_counter()
-        x, _ = om.layer_forward(x, lw, m, l, kv, [w.prompt_len] * w.batch, om.bf16_round)
-        t_layers += time.perf_counter() - t0
-        del lw
+        x, _ = om.layer_forward(x, lw, m, l, kv, [w.prompt_len] * w.batch, rnd)
+        t_total += time.perf_counter() - t0
+        del lw, kv
     E = W.embed()
-    rows = min(max_rows_head, M)
-    h = om.bf16_round(om.rmsnorm(x[:rows], W.norm_final(), m.rms_eps))
     t0 = time.perf_counter()
-    om.argmax_conf(om.lm_logits(h, E))
-    t_head = time.perf_counter() - t0
-    est = t_layers * m.n_layers / len(group) + t_head * M / rows
-    sample = (f"oracle float64 on {cores} BLAS threads: layers 0-{g_layer} ({len(group) - 1} sliding-window "
-              f"+ 1 global) over all {M} canvas positions in {t_layers:.2f} s and the LM head + argmax "
-              f"for {rows} positions in {t_head:.2f} s; pass time extrapolated to {m.n_layers} layers "
-              f"and {M} positions = {est:.1f} s")
-    return {"value": M / est, "unit": "canvas tokens/s", "cores": int(cores), "kind": "oracle",
+    h = rnd(om.rmsnorm(x, W.norm_final(), m.rms_eps))
+    pred, conf = om.argmax_conf(om.lm_logits(h, E))
+    om.lock_select(conf.reshape(w.batch, -1), pred.reshape(w.batch, -1), tok, lk, [w.n_steps] * w.batch)
+    t_total += time.perf_counter() - t0
+    sample = (f"oracle float64 on {cores} BLAS threads: one whole pass ({m.n_layers} layers, LM head, "
+              f"argmax, lock) over all {M} canvas positions in {t_total:.1f} s")
+    return {"value": M / t_total, "unit": "canvas tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": sample}
 
 

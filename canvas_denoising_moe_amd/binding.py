@@ -58,6 +58,7 @@ _SIGS = {
     "dg_denoise_step": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, POINTER(c_int32), c_void_p, c_void_p]),
     "dg_generate_block": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
     "dg_forward_hidden": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p]),
+    "dg_forward_layers": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
     "dg_set_trace": (c_int32, [c_void_p, c_void_p]),
     "dg_k_argmax_conf": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
     "dg_k_lock_select": (c_int32, [c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -238,6 +239,12 @@ class Context:
         import torch
         B = x_in.shape[0] // self.model.canvas_len
         self._c(lib().dg_forward_hidden(self._h, B, _ptr(x_in, torch.float32, "x_in"),
+                                        _ptr(x_out, torch.float32, "x_out")))
+
+    def forward_layers(self, first: int, count: int, x_in, x_out):
+        import torch
+        B = x_in.shape[0] // self.model.canvas_len
+        self._c(lib().dg_forward_layers(self._h, B, first, count, _ptr(x_in, torch.float32, "x_in"),
                                         _ptr(x_out, torch.float32, "x_out")))
 
     def set_trace(self, route_idx=None):

@@ -29,7 +29,7 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D>
-__global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int S, int CL, int QT, int xcd_map) {
+__global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int QT, int xcd_map) {
   constexpr int KT = 64;            // keys per tile
   constexpr int KLD = D + 8;        // padded LDS row of K (elements)
   constexpr int VLD = KT + 8;       // padded LDS row of V^T
@@ -47,8 +47,10 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int S, int CL, in
     unit = bid / QT;
     qt = bid % QT;
   }
-  const int s = unit % S, bg = unit / S;
-  const int g = bg % a.Hkv, b = bg / a.Hkv;
+  int b = 0;
+  while (b + 1 < a.B && a.ubase[b + 1] <= unit) ++b;
+  const int S = a.ns[b], CL = a.cl[b];
+  const int s = (unit - a.ubase[b]) % S, g = (unit - a.ubase[b]) / S;
   const int group = a.Hq / a.Hkv;
   const int N = a.N;
   const int Lw = a.lw[b];
@@ -213,15 +215,16 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int S, int CL, in
 
   mfma_drain();
   if (qvalid && S == 1) {
-    // a single split: normalise and store the bf16 output directly
+    // a single split: normalise and store the bf16 output directly (the same
+    // quotient the merge forms from one split)
     bf16_t* o = reinterpret_cast<bf16_t*>(a.o) + ((long long)b * N + qi) * a.Hq * D + (long long)qh * D;
-    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+    auto nrm = [&](float x) { return f2bf(l_run > 0.f ? x / l_run : 0.f); };
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
       const int d = db * 16 + lg * 4;
       *reinterpret_cast<uint2*>(o + d) =
-          make_uint2((uint32_t)f2bf(oacc[db][0] * inv) | ((uint32_t)f2bf(oacc[db][1] * inv) << 16),
-                     (uint32_t)f2bf(oacc[db][2] * inv) | ((uint32_t)f2bf(oacc[db][3] * inv) << 16));
+          make_uint2((uint32_t)nrm(oacc[db][0]) | ((uint32_t)nrm(oacc[db][1]) << 16),
+                     (uint32_t)nrm(oacc[db][2]) | ((uint32_t)nrm(oacc[db][3]) << 16));
     }
   } else if (qvalid) {
     const long long rows_all = (long long)a.B * a.Hq * N;
@@ -240,11 +243,12 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int S, int CL, in
 
 // o[(b*N + i), h*D + d] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, splits in order
 template <typename T>
-__global__ void k_attn_merge(AttnArgs a, int S) {
+__global__ void k_attn_merge(AttnArgs a) {
   const long long rows_all = (long long)a.B * a.Hq * a.N;
   const long long row = blockIdx.x;
   const int d = threadIdx.x;
-  if (d >= a.D) return;
+  const int S = a.ns[row / ((long long)a.Hq * a.N)];
+  if (d >= a.D || S == 1) return;  // one split: stored by the attention kernel
   constexpr int U = 8;  // splits whose loads are in flight together
   float M = -INFINITY;
   for (int s0 = 0; s0 < S; s0 += U) {
@@ -351,46 +355,49 @@ __global__ __launch_bounds__(256) void k_attn_simple(AttnArgs a) {
 
 // Split count and length: enough workgroups to cover the 256 CUs once, and no
 // split longer than 4096 keys (long prompts); splits are whole 64-key tiles.
-static void choose_splits(const AttnArgs& a, int QT, int* S_out, int* CL_out) {
-  int maxtot = 0;
-  for (int b = 0; b < a.B; ++b) maxtot = max(maxtot, a.lw[b] + (a.canvas_keys ? a.N : 0));
-  const long long base = (long long)a.B * a.Hkv * QT;
-  int S = max((int)((256 + base - 1) / base), (maxtot + 4095) / 4096);
-  const int tiles = (maxtot + 63) / 64;
-  if (S > tiles) S = tiles;
-  if (S < 1) S = 1;
-  const long long rows_all = (long long)a.B * a.Hq * a.N;
-  while (S > 1 && (long long)S * rows_all > a.part_cap_rows) --S;
-  int CL = ((maxtot + S - 1) / S + 63) / 64 * 64;
+// Key splits of canvas b from its own key count only: enough (KV head x split)
+// units per canvas to spread one canvas over the chip, at most 4096 keys per
+// split, at least 64, at most 64 splits (the partial buffers hold 64 per row).
+static void choose_splits(int total, int Hkv, int QT, int* S_out, int* CL_out) {
+  const int base = Hkv * QT;
+  int S = max((256 + base - 1) / base, (total + 4095) / 4096);
+  S = min(S, max(1, (total + 63) / 64));
+  S = min(S, 64);
+  int CL = ((total + S - 1) / S + 63) / 64 * 64;
   if (CL < 64) CL = 64;
-  S = (maxtot + CL - 1) / CL;
-  if (S < 1) S = 1;
+  S = max(1, (total + CL - 1) / CL);
   *S_out = S;
   *CL_out = CL;
 }
 
-hipError_t launch_attention(int is_bf16, const AttnArgs& a, hipStream_t st, KTime t) {
-  const long long rows_all = (long long)a.B * a.Hq * a.N;
+hipError_t launch_attention(int is_bf16, const AttnArgs& a0, hipStream_t st, KTime t) {
+  const long long rows_all = (long long)a0.B * a0.Hq * a0.N;
   if (rows_all == 0) return hipSuccess;
-  if (is_bf16 && (a.D == 128 || a.D == 64)) {
+  if (a0.B > DG_MAX_BATCH) return hipErrorInvalidValue;
+  if (is_bf16 && (a0.D == 128 || a0.D == 64)) {
+    AttnArgs a = a0;
     const int QT = (a.Hq / a.Hkv * a.N + 63) / 64;
-    int S, CL;
-    choose_splits(a, QT, &S, &CL);
-    if ((long long)S * rows_all > a.part_cap_rows) return hipErrorInvalidValue;
-    const long long units = (long long)a.B * a.Hkv * S;
+    int smax = 1;
+    a.ubase[0] = 0;
+    for (int b = 0; b < a.B; ++b) {
+      choose_splits(a.lw[b] + (a.canvas_keys ? a.N : 0), a.Hkv, QT, &a.ns[b], &a.cl[b]);
+      smax = max(smax, a.ns[b]);
+      a.ubase[b + 1] = a.ubase[b] + a.Hkv * a.ns[b];
+    }
+    if ((long long)smax * rows_all > a.part_cap_rows) return hipErrorInvalidValue;
+    const long long units = a.ubase[a.B];
     const int xcd_map = (units % 8) == 0;
     const dim3 grid((unsigned)(units * QT));
-    // one split: the kernel stores the output itself and closes the timing
-    hipEvent_t stop1 = S == 1 ? t.stop : nullptr;
+    // every canvas in one split: the kernel stores the output itself and closes the timing
+    hipEvent_t stop1 = smax == 1 ? t.stop : nullptr;
     hipError_t e = a.D == 128
-        ? launch_k(k_attn_mfma<128>, grid, dim3(256), 0, st, t.start, stop1, a, S, CL, QT, xcd_map)
-        : launch_k(k_attn_mfma<64>, grid, dim3(256), 0, st, t.start, stop1, a, S, CL, QT, xcd_map);
-    if (e != hipSuccess || S == 1) return e;
-    return launch_k(k_attn_merge<bf16_t>, dim3((unsigned)rows_all), dim3(a.D), 0, st, nullptr, t.stop,
-                    a, S);
+        ? launch_k(k_attn_mfma<128>, grid, dim3(256), 0, st, t.start, stop1, a, QT, xcd_map)
+        : launch_k(k_attn_mfma<64>, grid, dim3(256), 0, st, t.start, stop1, a, QT, xcd_map);
+    if (e != hipSuccess || smax == 1) return e;
+    return launch_k(k_attn_merge<bf16_t>, dim3((unsigned)rows_all), dim3(a.D), 0, st, nullptr, t.stop, a);
   }
-  if (a.D > 256) return hipErrorInvalidValue;
+  if (a0.D > 256) return hipErrorInvalidValue;
   if (is_bf16)
-    return launch_k(k_attn_simple<bf16_t>, dim3((unsigned)rows_all), dim3(256), 0, st, t.start, t.stop, a);
-  return launch_k(k_attn_simple<float>, dim3((unsigned)rows_all), dim3(256), 0, st, t.start, t.stop, a);
+    return launch_k(k_attn_simple<bf16_t>, dim3((unsigned)rows_all), dim3(256), 0, st, t.start, t.stop, a0);
+  return launch_k(k_attn_simple<float>, dim3((unsigned)rows_all), dim3(256), 0, st, t.start, t.stop, a0);
 }

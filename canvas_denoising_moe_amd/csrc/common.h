@@ -151,6 +151,11 @@ struct AttnArgs {
   const void* kp[DG_MAX_BATCH];  // per canvas: prompt K [Hkv][Lw][D]
   const void* vp[DG_MAX_BATCH];  // per canvas: prompt V^T [Hkv][D][Lw]
   int lw[DG_MAX_BATCH];          // per canvas: prompt keys visible to the layer
+  // key splits, set by launch_attention from each canvas's own key count (so a
+  // canvas's result never depends on the other canvases of the batch)
+  int ns[DG_MAX_BATCH];          // per canvas: splits
+  int cl[DG_MAX_BATCH];          // per canvas: keys per split (multiple of 64)
+  int ubase[DG_MAX_BATCH + 1];   // per canvas: first work unit (unit = KV head x split)
 };
 hipError_t launch_attention(int is_bf16, const AttnArgs& a, hipStream_t s, KTime t = {});
 

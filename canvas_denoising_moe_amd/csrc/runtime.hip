@@ -412,14 +412,15 @@ dg_status enqueue_dense(dg_ctx* ctx, const void* A, int lda, const void* Bp, int
 // Decoder layers on ctx->x, with ctx->a holding the normalised input of the
 // first layer.  The last layer leaves RMSNorm(x)(1 + w_last_out) in ctx->a when
 // w_last_out is given (the final norm before the LM head).
-dg_status enqueue_layers(dg_ctx* ctx, int B, const void* w_last_out) {
+dg_status enqueue_layers(dg_ctx* ctx, int B, const void* w_last_out, int l0 = 0, int l1 = -1) {
   const dg_config& c = ctx->c;
+  if (l1 < 0) l1 = c.n_layers;
   const int N = c.canvas_len, M = B * N, H = c.hidden, D = c.head_dim;
   const int Hq = c.n_heads, Hkv = c.n_kv_heads, E = c.n_experts, K = c.top_k;
   const long long qs[4] = {(long long)Hq * N * D, (long long)N * D, D, 1};
   const long long ks[4] = {(long long)Hkv * N * D, (long long)N * D, D, 1};
   const long long vs[4] = {(long long)Hkv * D * N, (long long)D * N, 1, N};
-  for (int l = 0; l < c.n_layers; ++l) {
+  for (int l = l0; l < l1; ++l) {
     const LayerW& W = ctx->L[l];
     TRY(enqueue_qkv(ctx, l, B, ctx->a, ctx->q, ctx->kc, ctx->vc, qs, ks, vs));
     TRY(enqueue_attention(ctx, l, B, ctx->o, 1));
@@ -437,7 +438,7 @@ dg_status enqueue_layers(dg_ctx* ctx, int B, const void* w_last_out) {
     NormArgs nc{};
     nc.mode = 1; nc.rows = M; nc.H = H; nc.k = K; nc.eps = c.rms_eps;
     nc.x = ctx->x; nc.delta = ctx->y; nc.w_delta = c.post_ffn_norm ? W.norm[3] : nullptr;
-    nc.w_out = (l + 1 < c.n_layers) ? ctx->L[l + 1].norm[0] : w_last_out;
+    nc.w_out = (l + 1 < l1) ? ctx->L[l + 1].norm[0] : w_last_out;
     nc.out = ctx->a;
     HIPX(launch_residual_norm(ctx->bf16, nc, ctx->st));
   }
@@ -678,23 +679,31 @@ dg_status dg_generate_block(dg_ctx* ctx, int32_t batch, int32_t n_steps, int32_t
   return DG_OK;
 }
 
-dg_status dg_forward_hidden(dg_ctx* ctx, int32_t batch, const float* x_in, float* x_out) {
+dg_status dg_forward_layers(dg_ctx* ctx, int32_t batch, int32_t first, int32_t count, const float* x_in,
+                            float* x_out) {
   TRY(enter(ctx));
   const dg_config& c = ctx->c;
   if (batch < 1 || batch > c.max_batch) return fail(ctx, DG_EINVAL, "batch %d outside [1, %d]", batch, c.max_batch);
+  if (first < 0 || count < 1 || first > c.n_layers - count)
+    return fail(ctx, DG_EINVAL, "layers [%d, %d + %d) outside [0, %d)", first, first, count, c.n_layers);
   if (!x_in || !x_out) return fail(ctx, DG_EINVAL, "x_in and x_out are required");
-  for (const auto& l : ctx->L)
-    if (!l.set) return fail(ctx, DG_ESTATE, "layer weights are not loaded");
+  for (int l = first; l < first + count; ++l)
+    if (!ctx->L[l].set) return fail(ctx, DG_ESTATE, "weights of layer %d are not loaded", l);
   TRY(check_slots(ctx, batch));
   const int M = batch * c.canvas_len, H = c.hidden;
   HIPX(hipMemcpyAsync(ctx->x, x_in, (size_t)M * H * 4, hipMemcpyDeviceToDevice, ctx->st));
   NormArgs n0{};
   n0.mode = 2; n0.rows = M; n0.H = H; n0.k = c.top_k; n0.eps = c.rms_eps;
-  n0.x = ctx->x; n0.w_out = ctx->L[0].norm[0]; n0.out = ctx->a;
+  n0.x = ctx->x; n0.w_out = ctx->L[first].norm[0]; n0.out = ctx->a;
   HIPX(launch_residual_norm(ctx->bf16, n0, ctx->st));
-  TRY(enqueue_layers(ctx, batch, nullptr));
+  TRY(enqueue_layers(ctx, batch, nullptr, first, first + count));
   HIPX(hipMemcpyAsync(x_out, ctx->x, (size_t)M * H * 4, hipMemcpyDeviceToDevice, ctx->st));
   return DG_OK;
+}
+
+dg_status dg_forward_hidden(dg_ctx* ctx, int32_t batch, const float* x_in, float* x_out) {
+  if (!ctx) return dg_forward_layers(ctx, batch, 0, 1, x_in, x_out);
+  return dg_forward_layers(ctx, batch, 0, ctx->c.n_layers, x_in, x_out);
 }
 
 dg_status dg_set_trace(dg_ctx* ctx, int32_t* route_idx) {

@@ -164,6 +164,12 @@ dg_status dg_generate_block(dg_ctx* ctx, int32_t batch, int32_t n_steps, int32_t
  * [batch*N, H] device (may alias).  Prompt KV of slots 0..batch-1 required. */
 dg_status dg_forward_hidden(dg_ctx* ctx, int32_t batch, const float* x_in, float* x_out);
 
+/* Decoder layers [first, first + count) only, as dg_forward_hidden: x_in,
+ * x_out float [batch*N, H] device (may alias).  A trace set by dg_set_trace
+ * receives the routing of these layers at their own layer index. */
+dg_status dg_forward_layers(dg_ctx* ctx, int32_t batch, int32_t first, int32_t count, const float* x_in,
+                            float* x_out);
+
 /* Record every pass's expert choice: route_idx int32 [n_layers, batch*N,
  * top_k] device (slot order: logit descending, index ascending), written by
  * each following dg_denoise_step / dg_forward_hidden (a block overwrites it

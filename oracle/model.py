@@ -251,6 +251,24 @@ def _to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     return np.asarray(a, dtype=np.float32).astype(np.float64)
 
 
+_EXPERT_STACKS = ("w_gate", "w_up", "w_down")
+
+
+class _ExpertStack:
+    """``[E, in, out]`` expert weights kept in their stored form; indexing one
+    expert returns its float64 matrix."""
+
+    def __init__(self, raw: np.ndarray, dtype: str):
+        self.raw, self.dtype, self.shape = raw, dtype, raw.shape
+
+    def __getitem__(self, e: int) -> np.ndarray:
+        return _to_f64(self.raw[e], self.dtype)
+
+    def __array__(self, dtype=None, copy=None):
+        a = _to_f64(self.raw, self.dtype)
+        return a if dtype is None else a.astype(dtype)
+
+
 @dataclass
 class OracleWeights:
     """Weights as float64 arrays, fetched layer by layer from a provider so
@@ -271,7 +289,9 @@ class OracleWeights:
         if l in self._cache:
             return self._cache[l]
         raw = self.layer_fn(l)
-        out = {k: _to_f64(v, self.dtype) for k, v in raw.items()}
+        # per-expert stacks are widened one expert at a time, when an expert is used
+        out = {k: (_ExpertStack(v, self.dtype) if k in _EXPERT_STACKS else _to_f64(v, self.dtype))
+               for k, v in raw.items()}
         if self.cache_layers:
             self._cache[l] = out
         return out

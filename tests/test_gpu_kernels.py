@@ -195,15 +195,16 @@ def test_canvas_attention_matches_oracle(torch, actx, layer, lens, ck):
 
 
 MHA_MODEL = configs.ModelConfig(
-    n_layers=1, hidden=2048, n_heads=32, n_kv_heads=32, head_dim=128, n_experts=16, top_k=8,
+    n_layers=1, hidden=2048, n_heads=64, n_kv_heads=32, head_dim=64, n_experts=16, top_k=8,
     expert_ffn=64, vocab=0, canvas_len=256, window=1024, global_layer_mask=0b1,
     has_lm_head=False, dtype="bf16")
 MHA_W = configs.Workload(name="attn-mha-test", model=MHA_MODEL, batch=2, prompt_len=100, n_steps=1, seed=17)
 
 
 def test_canvas_attention_single_split(torch, dg):
-    # 2 canvases x 32 KV heads x 4 query tiles fill the chip without key splits,
-    # so the attention kernel normalises and stores its output itself
+    # 32 KV heads x 8 query tiles of 64 rows (2 query heads x 256 slots) fill
+    # the chip from one canvas without key splits, so the attention kernel
+    # normalises and stores its output itself (grouped heads, head size 64)
     m = MHA_MODEL
     say("attention single split")
     with dg.Context(m, max_batch=2, max_prompt_len=128) as ctx:

@@ -7,15 +7,12 @@ the oracle's optimum; any other disagreement is a hard failure."""
 import numpy as np
 import pytest
 
-from gpu_util import TOL, host64, needs_gpu, rel_err, say
+from gpu_util import DELTA_REL, TOL, host64, needs_gpu, rel_err, run_block_stepwise, say, shadow_compare
 from oracle import model as om
 from oracle.inputs import prompt_kv_fn, weights_for
 from synth import C1, C2, gen, upload
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
-
-DELTA_REL = {"f32": 1e-3, "bf16": 1e-2}
-
 
 @pytest.fixture(scope="module")
 def torch():
@@ -59,62 +56,13 @@ def test_one_layer_forward_hidden_c2(torch, dg):
     assert e2 <= TOL["bf16"]
 
 
-def _run_block_stepwise(torch, ctx, w):
-    m = w.model
-    B, N = w.batch, m.canvas_len
-    tok0, lk0 = gen.canvas(w)
-    tokens = torch.from_numpy(tok0).cuda()
-    locked = torch.from_numpy(lk0).cuda()
-    trace = torch.empty((m.n_layers, B * N, m.top_k), dtype=torch.int32, device="cuda")
-    ctx.set_trace(trace)
-    conf = torch.empty((B, N), dtype=torch.float32, device="cuda")
-    pred = torch.empty((B, N), dtype=torch.int32, device="cuda")
-    passes = []
-    for t in range(w.n_steps):
-        ctx.denoise_step(tokens, locked, [w.n_steps - t] * B, conf, pred)
-        torch.cuda.synchronize()
-        passes.append(dict(trace=trace.cpu().numpy().copy(), conf=conf.cpu().numpy().copy(),
-                           pred=pred.cpu().numpy().copy(), tokens=tokens.cpu().numpy().copy(),
-                           locked=locked.cpu().numpy().copy()))
-    ctx.set_trace(None)
-    return tok0, lk0, passes
-
-
-def _shadow_compare(w, tok0, lk0, passes, delta_rel, conf_tol):
-    m = w.model
-    W = weights_for(w, cache_layers=True)
-    kvf = prompt_kv_fn(w)
-    t_o, l_o = tok0, lk0
-    report = {"route": 0, "pred": 0, "lock": 0}
-    worst_conf = 0.0
-    for t, p in enumerate(passes):
-        # deltas relative to the RMS of the quantity a decision compares
-        sh = om.Shadow(route_idx=[p["trace"][l] for l in range(m.n_layers)], pred=p["pred"],
-                       locked_after=p["locked"])
-        trace = []
-        sh.delta_route = delta_rel  # router logits have unit-order RMS in these workloads
-        sh.delta_logit = delta_rel
-        sh.delta_conf = delta_rel * float(np.sqrt(np.mean(p["conf"].astype(np.float64) ** 2)))
-        t_o, l_o, pred_o, conf_o, _ = om.denoise_pass(t_o, l_o, [w.n_steps - t] * w.batch, W, m, kvf,
-                                                       [w.prompt_len] * w.batch, shadow=sh, trace=trace)
-        assert not sh.failures, (t, sh.failures[:5])
-        for k in report:
-            report[k] += sh.adopted[k]
-        ce = float(np.max(np.abs(p["conf"] - conf_o) / conf_o))
-        worst_conf = max(worst_conf, ce)
-        assert ce <= conf_tol, (t, ce)
-        assert np.array_equal(p["tokens"], t_o), t
-        assert np.array_equal(p["locked"], l_o), t
-    return report, worst_conf
-
-
 def test_c1_block_matches_oracle(torch, dg):
     w = C1
     m = w.model
     say("C1 block")
     with dg.Context(m, max_batch=w.batch, max_prompt_len=w.prompt_len) as ctx:
         upload.load_context(ctx, w)
-        tok0, lk0, passes = _run_block_stepwise(torch, ctx, w)
+        tok0, lk0, passes = run_block_stepwise(torch, ctx, w)
         # the one-call block gives the same canvas as the stepwise passes
         tokens = torch.from_numpy(tok0).cuda()
         locked = torch.from_numpy(lk0).cuda()
@@ -122,7 +70,7 @@ def test_c1_block_matches_oracle(torch, dg):
         torch.cuda.synchronize()
         assert np.array_equal(tokens.cpu().numpy(), passes[-1]["tokens"])
         assert locked.cpu().numpy().all()
-    report, worst = _shadow_compare(w, tok0, lk0, passes, DELTA_REL["f32"], TOL["f32"])
+    report, worst = shadow_compare(w, tok0, lk0, passes, DELTA_REL["f32"], TOL["f32"])
     print(f"C1: adopted decisions {report}; worst conf rel err {worst:.3e}")
     # fp32 end to end: the final canvas matches exactly, with no adopted decision
     assert report == {"route": 0, "pred": 0, "lock": 0}
@@ -133,7 +81,7 @@ def test_c1_lock_schedule_and_invariants(torch, dg):
     say("C1 schedule")
     with dg.Context(w.model, max_batch=w.batch, max_prompt_len=w.prompt_len) as ctx:
         upload.load_context(ctx, w)
-        tok0, lk0, passes = _run_block_stepwise(torch, ctx, w)
+        tok0, lk0, passes = run_block_stepwise(torch, ctx, w)
     prev_t, prev_l = tok0, lk0
     counts = []
     for p in passes:

@@ -332,7 +332,7 @@ def _counts(hist, locked0):
     return np.array(out).T.tolist()
 
 
-@pytest.mark.parametrize("cid", ["C1", "C3", "C5"])
+@pytest.mark.parametrize("cid", ["C1", "C3", "C4", "C5"])
 def test_lock_schedule_closed_form(cid):
     g = _gold("lock_schedules.json")[cid]
     # a tiny model with the workload's canvas length, pass count and pre-locks:
@@ -426,7 +426,7 @@ def test_zero_sublayers_leave_residual_unchanged():
     m = _tiny()
     w, W, kvf = _layer_setup(m)
     base = W.layer(0)
-    zero = {k: (np.zeros_like(v) if k in ("wo", "w_down", "sh_down") else v) for k, v in base.items()}
+    zero = {k: (np.zeros_like(np.asarray(v)) if k in ("wo", "w_down", "sh_down") else v) for k, v in base.items()}
     W0 = om.OracleWeights(dtype="f32", layer_fn=None)
     W0._cache = {0: zero}
     x = _rng(16).standard_normal((m.canvas_len, m.hidden))
@@ -499,10 +499,10 @@ def test_each_branch_is_normalised():
     y = run(base, x)
     s_o = dict(base, wo=base["wo"] * 7.0)
     assert np.allclose(run(s_o, x), y, rtol=1e-10, atol=1e-10)
-    s_d = dict(base, w_down=base["w_down"] * 5.0, sh_down=base["sh_down"] * 5.0)
+    s_d = dict(base, w_down=np.asarray(base["w_down"]) * 5.0, sh_down=base["sh_down"] * 5.0)
     assert np.allclose(run(s_d, x), y, rtol=1e-10, atol=1e-10)
     # input norm: with the FFN branch silenced, y - x is invariant under x -> c x
-    nf = dict(base, w_down=np.zeros_like(base["w_down"]), sh_down=np.zeros_like(base["sh_down"]))
+    nf = dict(base, w_down=np.zeros_like(np.asarray(base["w_down"])), sh_down=np.zeros_like(base["sh_down"]))
     assert np.allclose(run(nf, 3.0 * x) - 3.0 * x, run(nf, x) - x, rtol=1e-10, atol=1e-10)
     # the post-attention branch has unit RMS times (1 + w_pa) per channel
     zf = dict(nf, norm_pa=np.zeros_like(base["norm_pa"]))
