@@ -31,6 +31,81 @@ BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 
 METRIC = "canvas tokens/sec per denoise pass; resolved tok/s (30-layer bf16, 1 MI355X)"
 
+# HBM byte counters of the gate|up expert GEMM (rocprofv3 FETCH_SIZE / WRITE_SIZE
+# runs, scaled by a plain copy of known size), valid for the kernel sources
+# they were taken with
+COUNTERS = os.path.join(ROOT, "profiles", "moe_gate_up_C3_counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "canvas_denoising_moe_amd", "csrc", f) for f in ("gemm.hip", "common.h")]
+GATE_UP_KERNEL = r"k_stream<unsigned short, \d+, 1, \d+>"   # EPI_GEGLU instantiation
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def kernel_sources_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _counter_rows(d):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def summarize_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_mib):
+    """Per-launch HBM bytes of the gate|up GEMM from rocprofv3 counter runs
+    (KiB per dispatch), each counter scaled by what it reads for a plain
+    device copy of copy_mib MiB; written next to the other profiles."""
+    import re
+    import statistics
+    known_kib = copy_mib * 1024.0
+
+    def mean_kib(d, pattern, counter):
+        v = [float(r["Counter_Value"]) for r in _counter_rows(d)
+             if re.search(pattern, r["Kernel_Name"]) and r["Counter_Name"] == counter]
+        if not v:
+            raise SystemExit(f"no {counter} records of {pattern} under {d}")
+        return statistics.fmean(v), len(v)
+
+    cf, _ = mean_kib(copy_fetch_dir, re.escape(COPY_KERNEL), "FETCH_SIZE")
+    cw, _ = mean_kib(copy_write_dir, re.escape(COPY_KERNEL), "WRITE_SIZE")
+    f, nf = mean_kib(fetch_dir, GATE_UP_KERNEL, "FETCH_SIZE")
+    w, nw = mean_kib(write_dir, GATE_UP_KERNEL, "WRITE_SIZE")
+    out = {
+        "kernel": "moe_grouped_gemm gate|up (k_stream, GeGLU epilogue), 30-layer 4096-prompt workload",
+        "kernel_sources_sha256": kernel_sources_sha(),
+        "copy_mib": copy_mib,
+        "fetch_scale": known_kib / cf, "write_scale": known_kib / cw,
+        "fetch_kib_per_dispatch": f, "write_kib_per_dispatch": w, "dispatches": [nf, nw],
+        "fetch_bytes_per_launch": f * 1024.0 * known_kib / cf,
+        "write_bytes_per_launch": w * 1024.0 * known_kib / cw,
+    }
+    out["traffic_bytes_per_launch"] = out["fetch_bytes_per_launch"] + out["write_bytes_per_launch"]
+    with open(COUNTERS, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out))
+
+
+def measured_traffic():
+    """HBM bytes per gate|up launch from the committed counter summary, or None
+    when there is none or the kernel sources changed since it was taken."""
+    try:
+        with open(COUNTERS) as fh:
+            c = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_sources_sha256") != kernel_sources_sha():
+        return None
+    return int(c["traffic_bytes_per_launch"])
+
 
 def algorithmic(w, touched):
     """Algorithmic HBM bytes and flops of one pass and of one gate|up launch.
@@ -116,7 +191,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe-copy-mib", type=int, default=0,
                     help="only run 4 device copies of this many MiB (calibrates HBM byte counters) and exit")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                                                              "COPY_WRITE_DIR"),
+                    help="write the gate|up HBM traffic summary from rocprofv3 counter runs and exit")
+    ap.add_argument("--copy-mib", type=int, default=512, help="size of the calibration copy")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, args.copy_mib)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
               "multi-GPU path: independent canvases shard with no exchange, see the design notes.",
@@ -254,7 +336,7 @@ def main():
                    "prompt_len": w.prompt_len, "passes_per_block": T, "experts": m.n_experts,
                    "top_k": m.top_k, "vocab": m.vocab, "hidden": m.hidden},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "moe_grouped_gemm gate|up", "bytes_per_launch": int(gu_bytes),
                      "avg_launch_us": round(gu_avg_s * 1e6, 2)},
         "cpu_baseline": cpu,
