@@ -106,6 +106,7 @@ DG_DEV void epilogue(const EpiArgs& e, int row, int nb0, int nb_valid, int c, co
     // n-block 2p holds gate columns, 2p+1 the up columns of the same outputs
 #pragma unroll
     for (int p = 0; p < WN / 2; ++p) {
+      if (2 * p + 1 >= nb_valid) break;  // pairs past the last n-block
       const int col = ((nb0 + 2 * p) >> 1) * 16 + c;
       st<T>(e.out, (long long)row * e.ldo + col, gelu_tanh(v[2 * p]) * v[2 * p + 1]);
     }
@@ -114,6 +115,7 @@ DG_DEV void epilogue(const EpiArgs& e, int row, int nb0, int nb_valid, int c, co
     const int bph = e.D >> 4;  // 16-column blocks per head
 #pragma unroll
     for (int p = 0; p < WN / 2; ++p) {
+      if (2 * p + 1 >= nb_valid) break;  // pairs past the last n-block
       const int nb = nb0 + 2 * p;
       const int hs = nb / bph, w0 = nb - hs * bph;
       float x1 = v[2 * p], x2 = v[2 * p + 1];
