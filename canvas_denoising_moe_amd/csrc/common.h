@@ -162,9 +162,9 @@ hipError_t launch_attention(int is_bf16, const AttnArgs& a, hipStream_t s, KTime
 // Routing, combine, norms.
 // MoE routing (route.hip).  ROUTE_LOGITS: top-k + gates of the router logits
 // (sum of logit_parts split-K partials); ROUTE_GIVEN: idx/gates are inputs.  Both
-// then build counts/offsets/perm/a_rows/work.  bm (E * ceil(rows/32) words) must
-// be zero before the first launch; the kernels leave it zero again.
+// then build counts/offsets/perm/a_rows/work.  E * ceil(rows/32) <= 16384.
 enum RouteMode { ROUTE_LOGITS = 1, ROUTE_GIVEN = 2 };
+constexpr int kRouteMaxLds = 16384 * 8;  // bitmap + prefix counts of the scatter workgroup
 struct RouteArgs {
   int mode;
   int rows, E, k;
@@ -173,7 +173,6 @@ struct RouteArgs {
   int32_t* idx; float* gates;
   int32_t* counts; int32_t* offsets; int32_t* perm; int32_t* a_rows;
   int4* work; int32_t* work_count;
-  uint32_t* bm;
   int with_shared;
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);

@@ -97,7 +97,7 @@ DG_DEV void epilogue(const EpiArgs& e, int row, int nb0, int nb_valid, int c, co
   } else if constexpr (EPI == EPI_DOWN) {
     const int orow = e.slot[row];
     if ((unsigned)orow >= (unsigned)e.out_rows) return;
-    const float g = row < e.routed_rows ? e.gates[orow] : 1.0f;
+    const float g = orow < e.routed_rows ? e.gates[orow] : 1.0f;  // shared-expert rows: weight 1
     float* out = reinterpret_cast<float*>(e.out);
 #pragma unroll
     for (int w = 0; w < WN; ++w)

@@ -4,22 +4,19 @@
 //     to the lower expert) and gates = softmax over the kept logits
 //     ([4xFaster] "DiffusionGemma's Technical Architecture": 8 of 128 experts
 //     active); the logits may arrive as split-K partial sums, added here in a
-//     fixed order.  One wave per token; expert membership is recorded as bits
-//     (expert, token) with device-scope atomicOr, which is order-independent.
-//   k_route_scatter: one workgroup turns the bitmap into per-expert counts and
-//     offsets, the rows of every expert in ascending token order, and the work
-//     list of <= 16-row entries the streaming expert GEMMs consume; it then
-//     clears the bitmap for the next launch.
+//     fixed order.  One wave per token.
+//   k_route_scatter: one workgroup builds the (expert, token) membership bitmap
+//     in LDS from the chosen ids, then per-expert counts and offsets, the rows
+//     of every expert in ascending token order, and the work list of <= 16-row
+//     entries the streaming expert GEMMs consume.
 //
-// The result never depends on scheduling, and the kernel boundary between the
-// two steps provides the device-wide visibility a single-launch version would
-// need device-scope fences for.
+// The result never depends on scheduling: bits are set with order-independent
+// LDS atomics, and ranks are popcounts of the bitmap.
 #include "common.h"
 
 namespace {
 
 constexpr int kRowsPerBlock = 4;
-constexpr int kBmLds = 4096;  // bitmap words staged in LDS (128 experts x 4096 tokens / 32)
 
 DG_DEV void argmax_pair(float& v, int& e) {
 #pragma unroll
@@ -35,16 +32,6 @@ __global__ __launch_bounds__(256) void k_route_topk(RouteArgs a) {
   const int E = a.E, K = a.k;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = blockIdx.x * kRowsPerBlock + wave;
-  const int W = (a.rows + 31) >> 5;
-
-  if (a.mode == ROUTE_GIVEN) {
-    if (t < a.rows && lane < K) {
-      int e = a.idx[(long long)t * K + lane];
-      e = e < 0 ? 0 : (e >= E ? E - 1 : e);  // out-of-range ids must not leave the bitmap
-      atomicOr(&a.bm[e * W + (t >> 5)], 1u << (t & 31));
-    }
-    return;
-  }
 
   const int parts = a.logit_parts > 0 ? a.logit_parts : 1;
   for (int u = tid; u < kRowsPerBlock * E; u += 256) {
@@ -97,38 +84,48 @@ __global__ __launch_bounds__(256) void k_route_topk(RouteArgs a) {
         a.gates[(long long)t * K + q] = ex[q] / sum;
       }
   }
-  // every lane holds sel_e; lanes < K set the membership bits
-  if (lane < K) {
-    int e = 0;
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-      if (q == lane) e = sel_e[q];
-    atomicOr(&a.bm[e * W + (t >> 5)], 1u << (t & 31));
-  }
 }
 
 __global__ __launch_bounds__(1024) void k_route_scatter(RouteArgs a) {
-  __shared__ uint32_t bml[kBmLds];
+  extern __shared__ uint32_t dyn[];  // bitmap [E][W] words, then per-word prefix counts [E][W]
   __shared__ int s_cnt[256], s_off[258], s_ent[256];
   __shared__ int s_total;
   const int E = a.E, K = a.k;
   const int tid = threadIdx.x, nt = blockDim.x;
-  const int W = (a.rows + 31) >> 5;
-  // the membership bitmap into LDS (coalesced, all loads in flight); counts and
-  // ranks then read LDS
-  const bool bm_in_lds = E * W <= kBmLds;
-  if (bm_in_lds)
-    for (int i = tid; i < E * W; i += nt) bml[i] = a.bm[i];
+  const int W = (a.rows + 31) >> 5, EW = E * W;
+  uint32_t* bm = dyn;
+  int* pre = reinterpret_cast<int*>(dyn + EW);
+  const int RK = a.rows * K;
+  for (int i = tid; i < EW; i += nt) bm[i] = 0u;
   __syncthreads();
-  const uint32_t* bmr = bm_in_lds ? bml : a.bm;
+  for (int p0 = tid; p0 < RK; p0 += nt * 8) {
+    int ev[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {  // expert ids of 8 entries in flight together
+      const int p = p0 + u * nt;
+      ev[u] = p < RK ? a.idx[p] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = p0 + u * nt;
+      if (p < RK) {
+        const int e = ev[u] < 0 ? 0 : (ev[u] >= E ? E - 1 : ev[u]);  // ids stay inside the bitmap
+        const int tt = p / K;
+        atomicOr(&bm[e * W + (tt >> 5)], 1u << (tt & 31));
+      }
+    }
+  }
+  __syncthreads();
   for (int e = tid; e < E; e += nt) {
     int c = 0;
-    for (int w = 0; w < W; ++w) c += __popc(bmr[e * W + w]);
+    for (int w = 0; w < W; ++w) {
+      pre[e * W + w] = c;
+      c += __popc(bm[e * W + w]);
+    }
     s_cnt[e] = c;
     if (a.counts) a.counts[e] = c;
   }
   __syncthreads();
-  const int RK = a.rows * K;
   const int n_shared = a.with_shared ? (a.rows + 15) / 16 : 0;
   if (tid == 0) {
     int off = 0, ne = 0;
@@ -138,8 +135,10 @@ __global__ __launch_bounds__(1024) void k_route_scatter(RouteArgs a) {
       off += s_cnt[e];
       ne += (s_cnt[e] + 15) >> 4;
     }
-    s_off[E] = off;               // == rows * k
-    s_off[E + 1] = off + a.rows;  // the shared expert's rows follow the routed ones
+    // the shared expert's rows follow the routed ones at rows * k (== off when
+    // every row's ids are distinct; repeated ids leave [off, rows * k) unused)
+    s_off[E] = RK;
+    s_off[E + 1] = RK + a.rows;
     s_total = ne + n_shared;
     if (a.work_count) *a.work_count = s_total;
   }
@@ -159,7 +158,7 @@ __global__ __launch_bounds__(1024) void k_route_scatter(RouteArgs a) {
   for (int p0 = tid; p0 < RK; p0 += nt * 8) {
     int ev[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {  // expert ids of 8 entries in flight together
+    for (int u = 0; u < 8; ++u) {
       const int p = p0 + u * nt;
       ev[u] = p < RK ? a.idx[p] : 0;
     }
@@ -167,13 +166,9 @@ __global__ __launch_bounds__(1024) void k_route_scatter(RouteArgs a) {
     for (int u = 0; u < 8; ++u) {
       const int p = p0 + u * nt;
       if (p < RK) {
-        const int tt = p / K;
-        int e = ev[u];
-        e = e < 0 ? 0 : (e >= E ? E - 1 : e);
-        const uint32_t* row = bmr + e * W;
-        const int wt = tt >> 5;
-        int rank = __popc(row[wt] & ((1u << (tt & 31)) - 1u));
-        for (int w = 0; w < wt; ++w) rank += __popc(row[w]);
+        const int e = ev[u] < 0 ? 0 : (ev[u] >= E ? E - 1 : ev[u]);
+        const int tt = p / K, wt = tt >> 5;
+        const int rank = pre[e * W + wt] + __popc(bm[e * W + wt] & ((1u << (tt & 31)) - 1u));
         const int pos = s_off[e] + rank;
         if (a.perm) a.perm[pos] = p;
         if (a.a_rows) a.a_rows[pos] = tt;
@@ -186,8 +181,6 @@ __global__ __launch_bounds__(1024) void k_route_scatter(RouteArgs a) {
       if (a.a_rows) a.a_rows[RK + tt] = tt;
     }
   }
-  __syncthreads();
-  for (int i = tid; i < E * W; i += nt) a.bm[i] = 0u;
 }
 
 }  // namespace
@@ -195,10 +188,21 @@ __global__ __launch_bounds__(1024) void k_route_scatter(RouteArgs a) {
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
   if (a.E > 256 || a.k > 8 || (a.mode != ROUTE_LOGITS && a.mode != ROUTE_GIVEN)) return hipErrorInvalidValue;
-  const int blocks = (a.rows + kRowsPerBlock - 1) / kRowsPerBlock;
-  hipLaunchKernelGGL(k_route_topk, dim3(blocks), dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_route_scatter, dim3(1), dim3(1024), 0, s, a);
+  const size_t lds = (size_t)a.E * ((a.rows + 31) / 32) * 8;  // bitmap + prefix counts
+  if (lds > kRouteMaxLds) return hipErrorInvalidValue;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_route_scatter),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, kRouteMaxLds);
+    if (err != hipSuccess) return err;
+    attr_set = true;
+  }
+  if (a.mode == ROUTE_LOGITS) {
+    const int blocks = (a.rows + kRowsPerBlock - 1) / kRowsPerBlock;
+    hipLaunchKernelGGL(k_route_topk, dim3(blocks), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_route_scatter, dim3(1), dim3(1024), lds, s, a);
   return hipGetLastError();
 }

@@ -54,9 +54,7 @@ struct dg_ctx {
   int32_t *idx = nullptr, *offsets = nullptr, *perm = nullptr, *arows = nullptr, *pred = nullptr;
   long long part_cap = 0;
   int32_t* trace = nullptr;
-  // router scatter state: membership bitmap (kept zero between launches),
-  // expert work list
-  uint32_t* bm = nullptr;
+  // expert work list built by the router
   int4* work = nullptr;
   int32_t* work_count = nullptr;
   std::string err;
@@ -154,27 +152,6 @@ KTime prof_kernel(dg_ctx* ctx, int kind) {
   return t;
 }
 
-// Scratch of the context-free routing entry point: membership bitmap for up to
-// 256 experts x 4096 rows, per device, allocated on first use and kept zero
-// between launches by the kernels themselves.
-dg_status route_scratch(uint32_t** bm) {
-  static uint32_t* s_bm[DG_MAX_BATCH] = {};
-  dg_ctx* ctx = nullptr;
-  int dev = 0;
-  HIPX(hipGetDevice(&dev));
-  if (dev < 0 || dev >= DG_MAX_BATCH) return fail(ctx, DG_EUNSUPPORTED, "device index %d too large", dev);
-  if (!s_bm[dev]) {
-    const size_t bytes = 256 * (4096 / 32) * 4;
-    void* p = nullptr;
-    HIPX(hipMalloc(&p, bytes));
-    HIPX(hipMemset(p, 0, bytes));
-    HIPX(hipDeviceSynchronize());
-    s_bm[dev] = reinterpret_cast<uint32_t*>(p);
-  }
-  *bm = s_bm[dev];
-  return DG_OK;
-}
-
 bool is_global(const dg_config& c, int l) { return (c.global_layer_mask >> l) & 1ull; }
 
 // capacity of the expert work list for M tokens: every routed expert adds at
@@ -270,11 +247,8 @@ dg_status alloc_workspaces(dg_ctx* ctx) {
   TRY(dalloc_t(ctx, &ctx->part_o, (size_t)ctx->part_cap * D * 4));
   TRY(dalloc_t(ctx, &ctx->part_m, (size_t)ctx->part_cap * 4));
   TRY(dalloc_t(ctx, &ctx->part_l, (size_t)ctx->part_cap * 4));
-  const size_t bm_words = E * ((M + 31) / 32);
-  TRY(dalloc_t(ctx, &ctx->bm, bm_words * 4));
   TRY(dalloc_t(ctx, &ctx->work, (size_t)work_cap(c, (int)M) * sizeof(int4)));
   TRY(dalloc_t(ctx, &ctx->work_count, 4));
-  HIPX(hipMemset(ctx->bm, 0, bm_words * 4));
   HIPX(hipMemset(ctx->work_count, 0, 4));
   HIPX(hipDeviceSynchronize());
   return DG_OK;
@@ -357,7 +331,6 @@ dg_status enqueue_route(dg_ctx* ctx, int l, int M, int mode) {
   r.idx = ctx->idx; r.gates = ctx->gates;
   r.offsets = ctx->offsets; r.perm = ctx->perm; r.a_rows = ctx->arows;
   r.work = ctx->work; r.work_count = ctx->work_count;
-  r.bm = ctx->bm;
   r.with_shared = 1;
   HIPX(launch_route(r, ctx->st));
   return DG_OK;
@@ -749,14 +722,11 @@ dg_status dg_k_moe_route(const float* logits, int32_t rows, int32_t n_experts, i
     return fail(ctx, DG_EINVAL, "rows in [1, 4096], E in [1, 256], k in [1, min(8, E)] required");
   if ((long long)n_experts * ((rows + 31) / 32) > 16384)
     return fail(ctx, DG_EINVAL, "E * ceil(rows / 32) must be <= 16384");
-  uint32_t* bm = nullptr;
-  TRY(route_scratch(&bm));
   RouteArgs r{};
   r.mode = ROUTE_LOGITS; r.rows = rows; r.E = n_experts; r.k = top_k;
   r.logits = logits; r.logit_parts = 1;
   r.idx = idx; r.gates = gates;
   r.counts = counts; r.offsets = offsets; r.perm = perm;
-  r.bm = bm;
   HIPX(launch_route(r, reinterpret_cast<hipStream_t>(stream)));
   return DG_OK;
 }
