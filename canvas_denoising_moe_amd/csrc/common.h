@@ -120,15 +120,16 @@ struct EpiArgs {
 hipError_t launch_gemm(int is_bf16, const GemmArgs& g, const EpiArgs& e, int mt, hipStream_t s,
                        KTime t = {});
 
-// Streaming GEMM over work entries of <= 16 rows (see gemm.hip).  Dense entries
-// cover rows [dense_row0, dense_row0 + dense_rows) of group dense_group in steps
-// of 16; work entries {group, first row, end row, -} come from the router.
-// Needs 16 * K * sizeof(T) bytes of LDS (K <= 4096 for bf16, 2048 for fp32).
+// Streaming GEMM over work entries of <= 16*mt rows (see gemm.hip).  Dense
+// entries cover rows [dense_row0, dense_row0 + dense_rows) of group dense_group
+// in steps of 16*mt (n_dense of them); work entries {group, first row, end row,
+// -} come from the router, built for the same entry size.
 struct StreamArgs {
   const void* A; long long lda;
   const int32_t* a_rows; int a_rows_max;
   const void* B; long long b_group_stride;
   int K, NB;
+  int mt;  // row tiles of 16 per entry: 1 or 2
   int n_dense, dense_row0, dense_rows, dense_group;
   const int4* work; const int32_t* work_count; int work_cap;
   // split-K (fp32-store epilogue only): K/32 % ksplit == 0; split s writes its
@@ -173,6 +174,7 @@ struct RouteArgs {
   int32_t* idx; float* gates;
   int32_t* counts; int32_t* offsets; int32_t* perm; int32_t* a_rows;
   int4* work; int32_t* work_count;
+  int entry_rows;  // rows per work entry (16 * the expert GEMMs' mt)
   int with_shared;
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);

@@ -312,25 +312,41 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g, EpiArgs e) {
 }
 
 // ----------------------------------------------------------------------------
-// Streaming GEMM: one workgroup per (work entry of <= 16 rows, n-tile).
+// Streaming GEMM: one workgroup per (work entry of <= 16*MT rows, n-tile of
+// 4*WN n-blocks), 4 waves, each wave MT row tiles x WN n-blocks.
 //
-// The entry's A rows (<= 16) are staged once, over the whole of K, into LDS in
-// MFMA A-fragment order ([K/32][64 lanes][8]: every lane later reads its own
-// 16 contiguous bytes, no bank conflicts).  After a single barrier each wave
-// streams the W fragments of its WN n-blocks through an R-deep register ring:
-// the load of k-step kb+R is issued as soon as k-step kb is consumed, so every
-// wave keeps R*WN KB of weights in flight for the whole of K and no barrier
-// ever drains the pipeline.  Entries come either from a dense row range (16
-// rows each) or from the router's work list (expert, first row, end row), in
-// which heavy experts are split into several 16-row entries that run in
-// parallel.  Blocks are ordered tile-major over (tile, entry) and every XCD
-// takes a contiguous slice, so the entries of one expert run back to back on
-// one XCD and share that expert's W tile through its L2.
+// Each wave streams the W fragments of its WN n-blocks through an R-deep
+// register ring: the load of k-step kb+R is issued as soon as k-step kb is
+// consumed, so every wave keeps R*WN KB of weights in flight for the whole of
+// K.  The ring's first loads go out before anything else, so the weight
+// stream is under way while A is staged.  The entry's A rows are staged into
+// LDS in MFMA A-fragment order, [k-step][row tile][64 lanes][8] (every lane
+// reads its own 16 contiguous bytes), in chunks of at most 64 KB; the ring
+// runs on across chunk boundaries (weights do not depend on A).  Loads in the
+// k loop are unconditional so the compiler's wait counts stay exact; k-steps
+// past the end use a zero A fragment and clamped refills.
+//
+// Entries come either from a dense row range or from the router's work list
+// (expert, first row, end row), in which heavy experts are split into several
+// entries that run in parallel.  Blocks are ordered tile-major over (tile,
+// entry) and every XCD (blockIdx & 7) takes a contiguous slice, so the entries
+// of one expert run back to back on one XCD and share that expert's W tile
+// through its L2.  Wider entries (MT = 2) halve the weight reads of dense
+// GEMMs and of experts with more than 16 rows.
 // ----------------------------------------------------------------------------
-template <typename T, int WN, int EPI, int R>
+constexpr int kStreamLds = 64 * 1024;  // LDS budget of one A chunk
+
+template <typename T, int MT>
+constexpr int stream_kc() { return kStreamLds / (16 * MT * 32 * (int)sizeof(T)); }  // k-steps per chunk
+
+template <typename T, int MT, int WN, int EPI, int R>
 __global__ __launch_bounds__(256) void k_stream(StreamArgs g, EpiArgs e) {
+  constexpr int ROWS = 16 * MT;
+  constexpr int KC = stream_kc<T, MT>();
+  static_assert(KC % R == 0, "the register ring must tile an A chunk");
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  T* As = reinterpret_cast<T*>(smem_raw);  // [KB][64][8]
+  T* As = reinterpret_cast<T*>(smem_raw);  // [KC][MT][64][8]
+  __shared__ int s_rows[ROWS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tiles = (g.NB + 4 * WN - 1) / (4 * WN);
   const int J = g.n_dense + g.work_cap;
@@ -345,23 +361,20 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs g, EpiArgs e) {
   int group, rs, re;
   if (j < g.n_dense) {
     group = g.dense_group;
-    rs = g.dense_row0 + j * 16;
-    re = min(g.dense_row0 + g.dense_rows, rs + 16);
+    rs = g.dense_row0 + j * ROWS;
+    re = min(g.dense_row0 + g.dense_rows, rs + ROWS);
   } else {
     const int w = j - g.n_dense;
     if (w >= *g.work_count) return;
     const int4 en = g.work[w];
-    group = en.x; rs = en.y; re = en.z;
+    group = en.x; rs = en.y; re = min(en.z, en.y + ROWS);
   }
   if (rs >= re) return;
   const int KBall = g.K >> 5;
   const int KB = KBall / ksplit;  // k-steps of this split
   const int kbase = ks * KB;
 
-  // ---- W stream: R k-steps in flight per wave, issued first so the weight
-  // stream is already under way while A is staged.  Loads in the steady-state
-  // loop are unconditional so the compiler's wait counts stay exact (a
-  // conditional load would make it wait for every outstanding load).
+  // ---- W ring prologue
   const T* __restrict__ Bg = reinterpret_cast<const T*>(g.B) + (long long)group * g.b_group_stride;
   const int nb0 = tile * 4 * WN + wave * WN;
   const int nbv = g.NB - nb0;  // wave-uniform count of valid n-blocks (others computed, not stored)
@@ -377,11 +390,9 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs g, EpiArgs e) {
 #pragma unroll
     for (int w = 0; w < WN; ++w) b[i][w] = ld_frag<T>(bptr[w] + (long long)min(i, KB - 1) * 512);
 
-  // ---- A rows: gathered row indices once into LDS, then every tile load is
-  // unconditional (rows past the entry repeat its last row; those output rows
-  // are never stored, and an MFMA row depends only on its own A row)
-  __shared__ int s_rows[16];
-  if (tid < 16) {
+  // ---- A row indices (rows past the entry repeat its last row; those output
+  // rows are never stored, and an MFMA row depends only on its own A row)
+  if (tid < ROWS) {
     const int row = min(rs + tid, re - 1);
     long long ar = row;
     if (g.a_rows) {
@@ -390,70 +401,84 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs g, EpiArgs e) {
     }
     s_rows[tid] = (int)ar;
   }
-  __syncthreads();
-  {
-    const T* __restrict__ A = reinterpret_cast<const T*>(g.A) + kbase * 32;
-    const int k8s = KB * 4;  // 8-element groups per row within the split
-    const int groups8 = 16 * k8s;
-    constexpr int U = sizeof(T) == 2 ? 16 : 8;  // loads in flight, bounded by the W ring's registers
-    for (int base = tid; base < groups8; base += 256 * U) {
-      Frag<T> v[U];
+
+  floatx4 acc[MT][WN];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int q = min(base + u * 256, groups8 - 1);  // a repeated group rewrites the same value
-        const int r = q / k8s, k8 = q - r * k8s;          // consecutive threads read along a row
-        v[u] = ld_frag<T>(A + (long long)s_rows[r] * g.lda + k8 * 8);
-      }
+  for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int q = min(base + u * 256, groups8 - 1);
-        const int r = q / k8s, k8 = q - r * k8s;
-        st_frag<T>(As + ((k8 >> 2) * 64 + r + 16 * (k8 & 3)) * 8, v[u]);
+    for (int w = 0; w < WN; ++w) acc[m][w] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  const T* __restrict__ A = reinterpret_cast<const T*>(g.A) + kbase * 32;
+  for (int kc0 = 0; kc0 < KB; kc0 += KC) {
+    const int nk = min(KC, KB - kc0);  // k-steps in this chunk (< KC only in the last one)
+    __syncthreads();                   // row indices written / previous chunk consumed
+    {
+      const int k8s = nk * 4;          // 8-element groups per row within the chunk
+      const int groups8 = ROWS * k8s;
+      constexpr int U = sizeof(T) == 2 ? 8 : 4;  // loads in flight, bounded by the ring's registers
+      for (int base = tid; base < groups8; base += 256 * U) {
+        Frag<T> v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int q = min(base + u * 256, groups8 - 1);  // a repeated group rewrites the same value
+          const int r = q / k8s, k8 = q - r * k8s;          // consecutive threads read along a row
+          v[u] = ld_frag<T>(A + (long long)s_rows[r] * g.lda + (kc0 * 4 + k8) * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int q = min(base + u * 256, groups8 - 1);
+          const int r = q / k8s, k8 = q - r * k8s;
+          st_frag<T>(As + (((k8 >> 2) * MT + (r >> 4)) * 64 + (r & 15) + 16 * (k8 & 3)) * 8, v[u]);
+        }
       }
     }
-  }
-  __syncthreads();
-
-  floatx4 acc[WN];
+    __syncthreads();
+    // One branch-free loop over this chunk in groups of R k-steps.  Keeping the
+    // accumulators in one loop with no peeled tail also keeps them in place: a
+    // peeled tail made the register allocator copy them out of the accumulator
+    // registers right behind the last MFMA, and those reads returned values
+    // the MFMA had not yet written.
+    const T* Ap = As + lane * 8;
+    for (int kb0 = kc0; kb0 < kc0 + nk; kb0 += R) {
 #pragma unroll
-  for (int w = 0; w < WN; ++w) acc[w] = floatx4{0.f, 0.f, 0.f, 0.f};
-  // One branch-free loop over ceil(KB / R) groups: k-steps past the end use a
-  // zero A fragment (adding nothing) and their refill loads are clamped to the
-  // last k-step (served from cache).  Keeping the accumulators in one loop with
-  // no peeled tail also keeps them in place: a peeled tail made the register
-  // allocator copy them out of the accumulator registers right behind the last
-  // MFMA, and those reads returned values the MFMA had not yet written.
-  const T* Ap = As + lane * 8;
-  for (int kb0 = 0; kb0 < KB; kb0 += R) {
+      for (int i = 0; i < R; ++i) {
+        const int kb = kb0 + i;
+        const int kl = min(kb - kc0, nk - 1);
+        Frag<T> a[MT];
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const int kb = kb0 + i;
-      Frag<T> a = ld_frag<T>(Ap + min(kb, KB - 1) * 512);
-      if (kb >= KB) a = zero_frag<T>();
+        for (int m = 0; m < MT; ++m) {
+          a[m] = ld_frag<T>(Ap + (kl * MT + m) * 512);
+          if (kb >= kc0 + nk) a[m] = zero_frag<T>();
+        }
 #pragma unroll
-      for (int w = 0; w < WN; ++w) mma(acc[w], a, b[i][w]);
-      const int kn = min(kb + R, KB - 1);
+        for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int w = 0; w < WN; ++w) b[i][w] = ld_frag<T>(bptr[w] + (long long)kn * 512);
+          for (int w = 0; w < WN; ++w) mma(acc[m][w], a[m], b[i][w]);
+        const int kn = min(kb + R, KB - 1);
+#pragma unroll
+        for (int w = 0; w < WN; ++w) b[i][w] = ld_frag<T>(bptr[w] + (long long)kn * 512);
+      }
     }
   }
   mfma_drain();
   if (nbv > 0) {
     const int c = lane & 15, rg = (lane >> 4) * 4;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = rs + rg + r;
-      if (row < re) {
-        float v[WN];
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int w = 0; w < WN; ++w) v[w] = acc[w][r];
-        epilogue<T, WN, EPI>(e, row, nb0, nbv, c, v, ks * g.split_stride);
+      for (int r = 0; r < 4; ++r) {
+        const int row = rs + m * 16 + rg + r;
+        if (row < re) {
+          float v[WN];
+#pragma unroll
+          for (int w = 0; w < WN; ++w) v[w] = acc[m][w][r];
+          epilogue<T, WN, EPI>(e, row, nb0, nbv, c, v, ks * g.split_stride);
+        }
       }
-    }
   }
 }
 
-template <typename T, int WN, int EPI, int R>
+template <typename T, int MT, int WN, int EPI, int R>
 hipError_t run_stream(const StreamArgs& g, const EpiArgs& e, hipStream_t s, KTime t) {
   const int tiles = (g.NB + 4 * WN - 1) / (4 * WN);
   const int ksplit = g.ksplit > 1 ? g.ksplit : 1;
@@ -461,26 +486,35 @@ hipError_t run_stream(const StreamArgs& g, const EpiArgs& e, hipStream_t s, KTim
   const long long P = (long long)tiles * (g.n_dense + g.work_cap) * ksplit;
   if (P <= 0) return hipSuccess;
   const long long blocks = ((P + 7) >> 3) << 3;
-  const size_t lds = (size_t)16 * (g.K / ksplit) * sizeof(T);
+  const int KB = (g.K >> 5) / ksplit;
+  const size_t lds = (size_t)16 * MT * min(KB, stream_kc<T, MT>()) * 32 * sizeof(T);
   static bool attr_set = false;  // one attribute call per instantiation
   if (!attr_set) {
-    // 16 rows x 4096 bf16 (or 2048 fp32) = 128 KB; the kernel's static LDS comes on top
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_stream<T, WN, EPI, R>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+    // the 64 KB chunk plus the kernel's static LDS
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_stream<T, MT, WN, EPI, R>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, kStreamLds);
     if (err != hipSuccess) return err;
     attr_set = true;
   }
-  return launch_k(k_stream<T, WN, EPI, R>, dim3((unsigned)blocks), dim3(256), lds, s, t.start, t.stop, g, e);
+  return launch_k(k_stream<T, MT, WN, EPI, R>, dim3((unsigned)blocks), dim3(256), lds, s, t.start, t.stop,
+                  g, e);
+}
+
+template <typename T, int MT>
+hipError_t run_stream_mt(const StreamArgs& g, const EpiArgs& e, hipStream_t s, KTime t) {
+  switch (e.kind) {
+    case EPI_STORE_F32: return run_stream<T, MT, 2, EPI_STORE_F32, 8>(g, e, s, t);
+    case EPI_GEGLU: return run_stream<T, MT, 2, EPI_GEGLU, 8>(g, e, s, t);
+    case EPI_DOWN: return run_stream<T, MT, 2, EPI_DOWN, 8>(g, e, s, t);
+    case EPI_QKV: return run_stream<T, MT, 2, EPI_QKV, 8>(g, e, s, t);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <typename T>
 hipError_t run_stream_t(const StreamArgs& g, const EpiArgs& e, hipStream_t s, KTime t) {
-  switch (e.kind) {
-    case EPI_STORE_F32: return run_stream<T, 2, EPI_STORE_F32, 8>(g, e, s, t);
-    case EPI_GEGLU: return run_stream<T, 2, EPI_GEGLU, 8>(g, e, s, t);
-    case EPI_DOWN: return run_stream<T, 2, EPI_DOWN, 8>(g, e, s, t);
-    case EPI_QKV: return run_stream<T, 2, EPI_QKV, 8>(g, e, s, t);
-  }
+  if (g.mt == 1) return run_stream_mt<T, 1>(g, e, s, t);
+  if (g.mt == 2) return run_stream_mt<T, 2>(g, e, s, t);
   return hipErrorInvalidValue;
 }
 

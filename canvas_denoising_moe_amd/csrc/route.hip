@@ -126,21 +126,42 @@ __global__ __launch_bounds__(1024) void k_route_scatter(RouteArgs a) {
     if (a.counts) a.counts[e] = c;
   }
   __syncthreads();
-  const int n_shared = a.with_shared ? (a.rows + 15) / 16 : 0;
-  if (tid == 0) {
-    int off = 0, ne = 0;
-    for (int e = 0; e < E; ++e) {
-      s_off[e] = off;
-      s_ent[e] = ne;
-      off += s_cnt[e];
-      ne += (s_cnt[e] + 15) >> 4;
+  const int ER = a.entry_rows > 0 ? a.entry_rows : 16;
+  const int n_shared = a.with_shared ? (a.rows + ER - 1) / ER : 0;
+  if (tid < 64) {
+    // exclusive prefix sums of the row counts and entry counts over experts:
+    // lane l owns experts 4l..4l+3, then a wave-wide scan of the lane totals
+    int c[4], n[4], cs = 0, ns = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * tid + i;
+      c[i] = e < E ? s_cnt[e] : 0;
+      n[i] = (c[i] + ER - 1) / ER;
+      cs += c[i];
+      ns += n[i];
     }
-    // the shared expert's rows follow the routed ones at rows * k (== off when
-    // every row's ids are distinct; repeated ids leave [off, rows * k) unused)
-    s_off[E] = RK;
-    s_off[E + 1] = RK + a.rows;
-    s_total = ne + n_shared;
-    if (a.work_count) *a.work_count = s_total;
+    int ci = cs, ni = ns;  // inclusive scans
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int cu = __shfl_up(ci, o, 64), nu = __shfl_up(ni, o, 64);
+      if (tid >= o) { ci += cu; ni += nu; }
+    }
+    int off = ci - cs, ne = ni - ns;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * tid + i;
+      if (e < E) { s_off[e] = off; s_ent[e] = ne; }
+      off += c[i];
+      ne += n[i];
+    }
+    if (tid == 63) {
+      // the shared expert's rows follow the routed ones at rows * k (== off when
+      // every row's ids are distinct; repeated ids leave [off, rows * k) unused)
+      s_off[E] = RK;
+      s_off[E + 1] = RK + a.rows;
+      s_total = ne + n_shared;
+      if (a.work_count) *a.work_count = s_total;
+    }
   }
   __syncthreads();
   if (a.offsets)
@@ -148,12 +169,12 @@ __global__ __launch_bounds__(1024) void k_route_scatter(RouteArgs a) {
   if (a.work) {
     for (int e = tid; e < E; e += nt) {
       const int c = s_cnt[e], base = s_off[e];
-      for (int q = 0; q * 16 < c; ++q)
-        a.work[s_ent[e] + q] = make_int4(e, base + q * 16, base + min(c, q * 16 + 16), 0);
+      for (int q = 0; q * ER < c; ++q)
+        a.work[s_ent[e] + q] = make_int4(e, base + q * ER, base + min(c, q * ER + ER), 0);
     }
     const int ne = s_total - n_shared;
     for (int q = tid; q < n_shared; q += nt)
-      a.work[ne + q] = make_int4(E, RK + q * 16, RK + min(a.rows, q * 16 + 16), 0);
+      a.work[ne + q] = make_int4(E, RK + q * ER, RK + min(a.rows, q * ER + ER), 0);
   }
   for (int p0 = tid; p0 < RK; p0 += nt * 8) {
     int ev[8];

@@ -154,10 +154,15 @@ KTime prof_kernel(dg_ctx* ctx, int kind) {
 
 bool is_global(const dg_config& c, int l) { return (c.global_layer_mask >> l) & 1ull; }
 
+// Row tiles of 16 per streaming-GEMM entry for the expert and dense GEMMs
+// (the router GEMM, split over K, keeps 16-row entries).
+constexpr int kStreamMT = 2;
+constexpr int kEntryRows = 16 * kStreamMT;
+
 // capacity of the expert work list for M tokens: every routed expert adds at
-// most one partial 16-row entry beyond M*k/16, the shared expert M/16
+// most one partial entry beyond M*k/kEntryRows, the shared expert M/kEntryRows
 int work_cap(const dg_config& c, int M) {
-  return c.n_experts + (M * c.top_k + 15) / 16 + (M + 15) / 16;
+  return c.n_experts + (M * c.top_k + kEntryRows - 1) / kEntryRows + (M + kEntryRows - 1) / kEntryRows;
 }
 
 // split-K factor of the router GEMM: its weights are small (H x E), so the K
@@ -173,8 +178,8 @@ dg_status check_config(const dg_config* c) {
   dg_ctx* ctx = nullptr;
   if (!c) return fail(ctx, DG_EINVAL, "config is NULL");
   if (c->n_layers < 1 || c->n_layers > 64) return fail(ctx, DG_EINVAL, "n_layers must be in [1, 64]");
-  // the streaming GEMMs stage 16 rows x K in LDS: K <= 4096 (bf16) / 2048 (fp32)
-  const int kmax = c->dtype == DG_F32 ? 2048 : 4096;
+  // the norm kernels hold a row of the residual stream in registers: H <= 4096
+  const int kmax = 4096;
   if (c->hidden <= 0 || c->hidden % 32 || c->hidden > kmax)
     return fail(ctx, DG_EUNSUPPORTED, "hidden must be a positive multiple of 32 (<= %d)", kmax);
   if (c->expert_ffn > kmax) return fail(ctx, DG_EUNSUPPORTED, "expert_ffn must be <= %d", kmax);
@@ -279,7 +284,7 @@ dg_status enqueue_qkv(dg_ctx* ctx, int l, int B, const void* a, void* q, void* k
   StreamArgs g{};
   g.A = a; g.lda = H; g.B = ctx->L[l].qkv; g.K = H;
   g.NB = (c.n_heads + 2 * c.n_kv_heads) * D / 16;
-  g.n_dense = (M + 15) / 16; g.dense_rows = M;
+  g.mt = kStreamMT; g.n_dense = (M + kEntryRows - 1) / kEntryRows; g.dense_rows = M;
   EpiArgs e{};
   e.kind = EPI_QKV;
   e.q = q; e.k = k; e.v = v;
@@ -323,14 +328,14 @@ dg_status enqueue_route(dg_ctx* ctx, int l, int M, int mode) {
     e.kind = EPI_STORE_F32; e.out = ctx->rl; e.ldo = E;
     StreamArgs g{};
     g.A = ctx->f; g.lda = H; g.B = ctx->L[l].router; g.K = H; g.NB = E / 16;
-    g.n_dense = (M + 15) / 16; g.dense_rows = M;
+    g.mt = 1; g.n_dense = (M + 15) / 16; g.dense_rows = M;
     g.ksplit = router_split(c); g.split_stride = (long long)M * E;
     HIPX(launch_stream(ctx->bf16, g, e, ctx->st));
     r.logits = ctx->rl; r.logit_parts = g.ksplit; r.part_stride = g.split_stride;
   }
   r.idx = ctx->idx; r.gates = ctx->gates;
   r.offsets = ctx->offsets; r.perm = ctx->perm; r.a_rows = ctx->arows;
-  r.work = ctx->work; r.work_count = ctx->work_count;
+  r.work = ctx->work; r.work_count = ctx->work_count; r.entry_rows = kEntryRows;
   r.with_shared = 1;
   HIPX(launch_route(r, ctx->st));
   return DG_OK;
@@ -344,7 +349,7 @@ dg_status enqueue_experts(dg_ctx* ctx, int l, int M, const void* f) {
   StreamArgs g{};
   g.A = f; g.lda = H; g.a_rows = ctx->arows; g.a_rows_max = M;
   g.B = ctx->L[l].gu; g.b_group_stride = 2LL * F * H;
-  g.K = H; g.NB = 2 * F / 16;
+  g.K = H; g.NB = 2 * F / 16; g.mt = kStreamMT;
   g.work = ctx->work; g.work_count = ctx->work_count; g.work_cap = work_cap(c, M);
   EpiArgs e{};
   e.kind = EPI_GEGLU; e.out = ctx->u; e.ldo = F;
@@ -353,7 +358,7 @@ dg_status enqueue_experts(dg_ctx* ctx, int l, int M, const void* f) {
   StreamArgs d{};
   d.A = ctx->u; d.lda = F; d.a_rows = nullptr;
   d.B = ctx->L[l].down; d.b_group_stride = (long long)F * H;
-  d.K = F; d.NB = H / 16;
+  d.K = F; d.NB = H / 16; d.mt = kStreamMT;
   d.work = ctx->work; d.work_count = ctx->work_count; d.work_cap = work_cap(c, M);
   EpiArgs ed{};
   ed.kind = EPI_DOWN; ed.out = ctx->y; ed.ldo = H;
@@ -363,7 +368,7 @@ dg_status enqueue_experts(dg_ctx* ctx, int l, int M, const void* f) {
 }
 
 // Dense y = A @ W into fp32.  Small weights (the output projection) stream per
-// 16-row tile and re-read W from L2; the LM head's 1 GB embedding is read once
+// 32-row entry and re-read W from L2; the LM head's 1 GB embedding is read once
 // per 64-row chunk by the chunked kernel instead.
 dg_status enqueue_dense(dg_ctx* ctx, const void* A, int lda, const void* Bp, int K, int N, int M, float* out,
                         int ldo, bool streaming = true, KTime t = {}) {
@@ -372,7 +377,10 @@ dg_status enqueue_dense(dg_ctx* ctx, const void* A, int lda, const void* Bp, int
   if (streaming) {
     StreamArgs g{};
     g.A = A; g.lda = lda; g.B = Bp; g.K = K; g.NB = N / 16;
-    g.n_dense = (M + 15) / 16; g.dense_rows = M;
+    // 32-row entries unless that leaves fewer workgroups than the chip has CUs
+    const long long tiles = (g.NB + 7) / 8;
+    g.mt = tiles * ((M + kEntryRows - 1) / kEntryRows) >= 256 ? kStreamMT : 1;
+    g.n_dense = (M + 16 * g.mt - 1) / (16 * g.mt); g.dense_rows = M;
     HIPX(launch_stream(ctx->bf16, g, e, ctx->st, t));
   } else {
     GemmArgs g{};
