@@ -70,6 +70,7 @@ _SIGS = {
                                    c_int32]),
     "dg_k_moe_ffn": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
     "dg_k_lm_head": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p]),
+    "dg_k_lm_argmax": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p]),
     "dg_profile": (c_int32, [c_void_p, c_int32]),
     "dg_profile_read": (c_int32, [c_void_p, c_int32, POINTER(c_int32), POINTER(ctypes.c_double)]),
 }
@@ -290,6 +291,11 @@ class Context:
         import torch
         self._c(lib().dg_k_lm_head(self._h, batch, _ptr(h, self.wdtype, "h"),
                                    _ptr(logits, torch.float32, "logits")))
+
+    def k_lm_argmax(self, batch: int, h, pred, conf):
+        import torch
+        self._c(lib().dg_k_lm_argmax(self._h, batch, _ptr(h, self.wdtype, "h"),
+                                     _ptr(pred, torch.int32, "pred"), _ptr(conf, torch.float32, "conf")))
 
 
 def k_argmax_conf(logits, pred, conf, stream=None):

@@ -191,6 +191,20 @@ hipError_t launch_embed(int is_bf16, const int32_t* tokens, int rows, int H, int
                         const void* packed_embed, float* x, hipStream_t s);
 hipError_t launch_rope_table(float2* cs, int N, int D, int prompt_len, double theta, hipStream_t s);
 
+// Tied LM head for bf16 contexts (lmhead.hip): h bf16 [M, K] @ E^T with E packed
+// as the B operand ([V/16][K/32][64][8]).  Store mode writes logits fp32 [M, V];
+// argmax mode writes pred/conf [M] through per-(vocabulary tile, row) partials
+// part_* [(V/256 rounded up) * M].  Needs K % 256 == 0 and V % 16 == 0.
+struct LmArgs {
+  const void* h; int M, K, V;
+  const void* E;
+  float* logits;
+  float* part_m; float* part_s; int32_t* part_i;
+  int32_t* pred; float* conf;
+};
+bool lm_head_supported(int M, int K, int V);
+hipError_t launch_lm_head(const LmArgs& a, bool argmax, hipStream_t s, KTime t = {});
+
 // Head: argmax / confidence and the lock step.
 hipError_t launch_argmax_conf(const float* logits, int rows, int V, int32_t* pred, float* conf,
                               hipStream_t s);

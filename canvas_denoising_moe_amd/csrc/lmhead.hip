@@ -1,0 +1,249 @@
+// Tied LM head for bf16 contexts: logits = h @ E^T over the whole vocabulary
+// ([HandsOn] "Detailed Specs": the embedding matrix doubles as the LM head),
+// optionally reduced on the fly to each row's argmax and confidence
+// 1 / sum_v exp(l_v - l_max) ([HandsOn] "Detailed Specs": the decoder's output
+// distribution judges which tokens are final) so the [rows, V] logits never
+// reach memory.
+//
+// One workgroup covers 128 rows x 256 vocabulary columns: every wave holds all
+// 8 row tiles of 16 rows and 4 column blocks of 16 (128 fp32 accumulators per
+// lane).  The embedding (the packed B operand, 1 GB at V = 262144) streams
+// through a 4-deep register ring of fragments, 32 MFMAs per k-step per wave;
+// h rows are staged through LDS in double-buffered chunks of 8 k-steps, each
+// wave loading two k-steps of the next chunk into registers while the current
+// chunk is consumed, so no load latency sits between chunks.  Units
+// (vocabulary tile, row group) are sliced contiguously per XCD, so the row
+// groups of one vocabulary tile run side by side on one XCD and read its
+// embedding fragments from HBM once, through that XCD's L2.
+//
+// Argmax mode: each wave reduces its 64 columns per row with 16-lane shuffles
+// (max with the lowest index on ties, then the sum of exp(l - max)); the four
+// waves are merged in column order through LDS, and one (max, sum, argmax)
+// partial per (row, vocabulary tile) is written.  k_lm_merge folds the
+// partials of a row in a fixed tree order.
+#include "common.h"
+
+namespace {
+
+constexpr int kLmRT = 8;   // row tiles of 16 per workgroup
+constexpr int kLmRows = 16 * kLmRT;
+constexpr int kLmKC = 8;   // k-steps per staged A chunk
+constexpr int kLmR = 4;    // W ring depth in k-steps
+constexpr int kLmKS = kLmKC / 4;  // k-steps of a chunk staged by each wave
+static_assert(kLmKC % kLmR == 0, "ring slot == k-step within the chunk mod R");
+static_assert(kLmKC % 4 == 0, "the four waves stage equal shares of a chunk");
+constexpr int kLmLds = 2 * kLmKC * kLmRT * 512 * 2;  // two chunks, bf16
+
+struct Part { float m; int i; float s; };
+
+// (max, argmax, sum exp(l - max)) of two column ranges; equal maxima keep the lower index
+DG_DEV Part part_merge(Part a, Part b) {
+  Part r;
+  if (a.m > b.m || (a.m == b.m && a.i < b.i)) { r.m = a.m; r.i = a.i; } else { r.m = b.m; r.i = b.i; }
+  const float sa = a.s > 0.f ? a.s * expf(a.m - r.m) : 0.f;
+  const float sb = b.s > 0.f ? b.s * expf(b.m - r.m) : 0.f;
+  r.s = sa + sb;
+  return r;
+}
+
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // one lane's 8 bf16 of a fragment
+
+DG_DEV void mma_bf16(floatx4& c, const v4u& a, const v4u& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, a), __builtin_bit_cast(bf16x8_v, b),
+                                              c, 0, 0, 0);
+}
+
+template <bool ARGMAX>
+__global__ __launch_bounds__(256) void k_lm_head(LmArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16_t* As = reinterpret_cast<bf16_t*>(smem);  // [2][KC][RT][64][8]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int NB = a.V >> 4, KB = a.K >> 5;
+  const int NVT = (NB + 15) >> 4, NRG = (a.M + kLmRows - 1) / kLmRows;
+  const int U = NVT * NRG, Q = (U + 7) >> 3;
+  const int unit = (blockIdx.x & 7) * Q + (blockIdx.x >> 3);
+  if (unit >= U) return;
+  const int vt = unit / NRG, rg = unit - vt * NRG;
+  const int nb0 = vt * 16 + wave * 4;
+  const int rbase = rg * kLmRows;
+
+  const bf16_t* __restrict__ B = reinterpret_cast<const bf16_t*>(a.E);
+  const bf16_t* bp[4];
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) bp[cc] = B + (long long)min(nb0 + cc, NB - 1) * KB * 512 + lane * 8;
+  v4u b[kLmR][4];
+#pragma unroll
+  for (int i = 0; i < kLmR; ++i)
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+      b[i][cc] = *reinterpret_cast<const v4u*>(bp[cc] + (long long)min(i, KB - 1) * 512);
+
+  // A staging: wave w owns k-steps w*KS .. w*KS + KS-1 of every chunk, all
+  // row tiles; lane j carries row (j & 15) of a tile, k-group j >> 4 (fragment
+  // order).  Rows past M repeat the last row (their results are never used).
+  const bf16_t* __restrict__ H = reinterpret_cast<const bf16_t*>(a.h);
+  const bf16_t* hrow[kLmRT];
+#pragma unroll
+  for (int i = 0; i < kLmRT; ++i)
+    hrow[i] = H + (long long)min(rbase + i * 16 + (lane & 15), a.M - 1) * a.K + wave * kLmKS * 32 +
+              (lane >> 4) * 8;
+  v4u st[kLmKS][kLmRT];  // the next chunk's share of this wave, in flight
+#define LM_LOAD_CHUNK(c)                                                                     \
+  _Pragma("unroll") for (int j = 0; j < kLmKS; ++j)                                          \
+    _Pragma("unroll") for (int i = 0; i < kLmRT; ++i)                                        \
+      st[j][i] = *reinterpret_cast<const v4u*>(hrow[i] + ((c) * kLmKC + j) * 32);
+#define LM_STORE_CHUNK(c)                                                                    \
+  {                                                                                          \
+    bf16_t* dst = As + (((c) & 1) * kLmKC + wave * kLmKS) * kLmRT * 512 + lane * 8;          \
+    _Pragma("unroll") for (int j = 0; j < kLmKS; ++j)                                        \
+      _Pragma("unroll") for (int i = 0; i < kLmRT; ++i)                                      \
+        *reinterpret_cast<v4u*>(dst + (j * kLmRT + i) * 512) = st[j][i];                     \
+  }
+  const int NC = KB / kLmKC;
+  LM_LOAD_CHUNK(0)
+  LM_STORE_CHUNK(0)
+  LM_LOAD_CHUNK(min(1, NC - 1))
+  __syncthreads();
+
+  floatx4 acc[kLmRT][4];
+#pragma unroll
+  for (int rt = 0; rt < kLmRT; ++rt)
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) acc[rt][cc] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  for (int c = 0; c < NC; ++c) {
+    const bf16_t* Ab = As + (c & 1) * kLmKC * kLmRT * 512 + lane * 8;
+#pragma unroll
+    for (int kl = 0; kl < kLmKC; ++kl) {
+#pragma unroll
+      for (int rt = 0; rt < kLmRT; ++rt) {
+        const v4u af = *reinterpret_cast<const v4u*>(Ab + (kl * kLmRT + rt) * 512);
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) mma_bf16(acc[rt][cc], af, b[kl % kLmR][cc]);
+      }
+      const int kn = min(c * kLmKC + kl + kLmR, KB - 1);
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+        b[kl % kLmR][cc] = *reinterpret_cast<const v4u*>(bp[cc] + (long long)kn * 512);
+      // keep each k-step's refills where they are: the scheduler would otherwise
+      // sink them to the end of the chunk and drain the ring
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // unconditional, so the compiler's load counters stay exact: past the last
+    // chunk this rewrites a buffer nobody reads again
+    LM_STORE_CHUNK(c + 1)  // its buffer was last read in chunk c - 1, before the barrier
+    LM_LOAD_CHUNK(min(c + 2, NC - 1))
+    __syncthreads();
+  }
+#undef LM_LOAD_CHUNK
+#undef LM_STORE_CHUNK
+  mfma_drain();
+
+  const int col_in = lane & 15, rq = (lane >> 4) * 4;
+  if constexpr (!ARGMAX) {
+#pragma unroll
+    for (int rt = 0; rt < kLmRT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = rbase + rt * 16 + rq + r;
+        if (row >= a.M) continue;
+        float* out = a.logits + (long long)row * a.V;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+          if (nb0 + cc < NB) out[(nb0 + cc) * 16 + col_in] = acc[rt][cc][r];
+      }
+  } else {
+    Part* red = reinterpret_cast<Part*>(smem);  // [4 waves][rows]; A chunks are done
+#pragma unroll
+    for (int rt = 0; rt < kLmRT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        // this lane's 4 columns ascend with cc; columns past the vocabulary are skipped
+        float m = -INFINITY;
+        int mi = 0x7fffffff;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          const float v = acc[rt][cc][r];
+          if (nb0 + cc < NB && v > m) { m = v; mi = (nb0 + cc) * 16 + col_in; }
+        }
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) {  // the 16 lanes holding this row
+          const float om = __shfl_xor(m, o, 64);
+          const int oi = __shfl_xor(mi, o, 64);
+          if (om > m || (om == m && oi < mi)) { m = om; mi = oi; }
+        }
+        float s = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+          if (nb0 + cc < NB) s += expf(acc[rt][cc][r] - m);
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+        if (col_in == 0) red[wave * kLmRows + rt * 16 + rq + r] = Part{m, mi, s};
+      }
+    __syncthreads();
+    const int row = rbase + tid;
+    if (tid < kLmRows && row < a.M) {
+      Part p = red[tid];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) p = part_merge(p, red[w * kLmRows + tid]);  // column order
+      const long long o = (long long)vt * a.M + row;
+      a.part_m[o] = p.m;
+      a.part_s[o] = p.s;
+      a.part_i[o] = p.i;
+    }
+  }
+}
+
+// Per row: fold the partials of all vocabulary tiles in a fixed tree order.
+__global__ __launch_bounds__(256) void k_lm_merge(LmArgs a) {
+  __shared__ Part red[4];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int NVT = ((a.V >> 4) + 15) >> 4;
+  Part p{-INFINITY, 0x7fffffff, 0.f};
+  for (int t = tid; t < NVT; t += 256) {
+    const long long o = (long long)t * a.M + row;
+    p = part_merge(p, Part{a.part_m[o], a.part_i[o], a.part_s[o]});
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    Part q;
+    q.m = __shfl_xor(p.m, o, 64);
+    q.i = __shfl_xor(p.i, o, 64);
+    q.s = __shfl_xor(p.s, o, 64);
+    p = part_merge(p, q);
+  }
+  if ((tid & 63) == 0) red[tid >> 6] = p;
+  __syncthreads();
+  if (tid == 0) {
+    Part r = red[0];
+    for (int w = 1; w < 4; ++w) r = part_merge(r, red[w]);
+    a.pred[row] = r.i;
+    a.conf[row] = 1.0f / r.s;
+  }
+}
+
+}  // namespace
+
+bool lm_head_supported(int M, int K, int V) {
+  return M > 0 && K % (32 * kLmKC) == 0 && V % 16 == 0;
+}
+
+hipError_t launch_lm_head(const LmArgs& a, bool argmax, hipStream_t s, KTime t) {
+  if (a.M <= 0) return hipSuccess;
+  if (!lm_head_supported(a.M, a.K, a.V)) return hipErrorInvalidValue;
+  const int NVT = ((a.V >> 4) + 15) >> 4, NRG = (a.M + kLmRows - 1) / kLmRows;
+  const long long blocks = (((long long)NVT * NRG + 7) >> 3) << 3;
+  const void* fn = argmax ? reinterpret_cast<const void*>(&k_lm_head<true>)
+                          : reinterpret_cast<const void*>(&k_lm_head<false>);
+  static bool attr[2] = {false, false};
+  if (!attr[argmax]) {
+    hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLmLds);
+    if (err != hipSuccess) return err;
+    attr[argmax] = true;
+  }
+  if (!argmax)
+    return launch_k(k_lm_head<false>, dim3((unsigned)blocks), dim3(256), kLmLds, s, t.start, t.stop, a);
+  hipError_t e = launch_k(k_lm_head<true>, dim3((unsigned)blocks), dim3(256), kLmLds, s, t.start, nullptr, a);
+  if (e != hipSuccess) return e;
+  return launch_k(k_lm_merge, dim3((unsigned)a.M), dim3(256), 0, s, nullptr, t.stop, a);
+}

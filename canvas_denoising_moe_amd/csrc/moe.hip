@@ -36,11 +36,16 @@ __global__ __launch_bounds__(256) void k_residual_norm(NormArgs a) {
   const int H = a.H, n4 = H >> 2;
   float4* x4 = reinterpret_cast<float4*>(a.x + (long long)t * H);
   const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-  float4 xv[NV];
+  float4 xv[NV], gd[NV], go[NV];
+  const T* wd = reinterpret_cast<const T*>(a.w_delta);
+  const T* wo = reinterpret_cast<const T*>(a.w_out);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int c4 = tid + 256 * i;
     xv[i] = c4 < n4 ? x4[c4] : z4;
+    // the norm weights too, so no load waits behind a reduction
+    gd[i] = (wd && a.mode != 2 && c4 < n4) ? load4<T>(wd + 4 * c4) : z4;
+    go[i] = (wo && c4 < n4) ? load4<T>(wo + 4 * c4) : z4;
   }
   if (a.mode != 2) {
     const float4* d4 = reinterpret_cast<const float4*>(a.delta);
@@ -75,9 +80,8 @@ __global__ __launch_bounds__(256) void k_residual_norm(NormArgs a) {
         dv[i] = f4add(d, sv[i]);
       }
     }
-    const T* w = reinterpret_cast<const T*>(a.w_delta);
     float sc = 1.0f;
-    if (w) {
+    if (wd) {
       float ss = 0.f;
 #pragma unroll
       for (int i = 0; i < NV; ++i) ss += f4dot(dv[i]);
@@ -88,8 +92,8 @@ __global__ __launch_bounds__(256) void k_residual_norm(NormArgs a) {
       const int c4 = tid + 256 * i;
       if (c4 < n4) {
         float4 d = dv[i];
-        if (w) {
-          const float4 g = load4<T>(w + 4 * c4);
+        if (wd) {
+          const float4 g = gd[i];
           d = make_float4(d.x * sc * (1.f + g.x), d.y * sc * (1.f + g.y), d.z * sc * (1.f + g.z),
                           d.w * sc * (1.f + g.w));
         }
@@ -98,18 +102,17 @@ __global__ __launch_bounds__(256) void k_residual_norm(NormArgs a) {
       }
     }
   }
-  if (a.w_out) {
+  if (wo) {
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < NV; ++i) ss += f4dot(xv[i]);  // columns past H hold zeros
     const float sc = rsqrtf(block_sum(ss, red + 4) / H + a.eps);
-    const T* w = reinterpret_cast<const T*>(a.w_out);
     T* out = reinterpret_cast<T*>(a.out) + (long long)t * H;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int c4 = tid + 256 * i;
       if (c4 < n4) {
-        const float4 g = load4<T>(w + 4 * c4);
+        const float4 g = go[i];
         const float4 v = xv[i];
         store4<T>(out + 4 * c4, make_float4(v.x * sc * (1.f + g.x), v.y * sc * (1.f + g.y),
                                             v.z * sc * (1.f + g.z), v.w * sc * (1.f + g.w)));

@@ -16,7 +16,6 @@
 
 namespace {
 
-constexpr int kRowsPerBlock = 4;
 
 DG_DEV void argmax_pair(float& v, int& e) {
 #pragma unroll
@@ -27,62 +26,58 @@ DG_DEV void argmax_pair(float& v, int& e) {
   }
 }
 
-__global__ __launch_bounds__(256) void k_route_topk(RouteArgs a) {
-  __shared__ float rs[kRowsPerBlock * 256];
+// One wave per token: lane l holds the logits of experts l, l + 64, ... in
+// registers (split-K partials summed in slice order), the k winners come out
+// of k wave-wide arg-max rounds, and lane s < k writes slot s.
+__global__ __launch_bounds__(64) void k_route_topk(RouteArgs a) {
   const int E = a.E, K = a.k;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int t = blockIdx.x * kRowsPerBlock + wave;
-
+  const int t = blockIdx.x, lane = threadIdx.x;
   const int parts = a.logit_parts > 0 ? a.logit_parts : 1;
-  for (int u = tid; u < kRowsPerBlock * E; u += 256) {
-    const int r = u / E, e = u % E;
-    const int tt = blockIdx.x * kRowsPerBlock + r;
+  float v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
     float pv[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q)  // all partial loads in flight together
-      pv[q] = (tt < a.rows && q < parts) ? a.logits[q * a.part_stride + (long long)tt * E + e] : 0.f;
-    float s = 0.f;
+      pv[q] = (e < E && q < parts) ? a.logits[q * a.part_stride + (long long)t * E + e] : 0.f;
+    float sum = 0.f;
 #pragma unroll
     for (int q = 0; q < 8; ++q)
-      if (q < parts) s += pv[q];  // fixed order
-    rs[r * E + e] = s;
-    if (a.r_out && tt < a.rows) a.r_out[(long long)tt * E + e] = s;
+      if (q < parts) sum += pv[q];  // fixed order
+    v[j] = e < E ? sum : -INFINITY;
+    if (a.r_out && e < E) a.r_out[(long long)t * E + e] = sum;
   }
-  __syncthreads();
-  if (t >= a.rows) return;
-
-  const float* rr = rs + wave * E;
   float sel_v[8];
   int sel_e[8];
   unsigned used = 0u;  // bit j: expert lane + 64 j taken
-  for (int s = 0; s < K; ++s) {
-    float v = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    if (s >= K) break;
+    float bv = -INFINITY;
     int be = 0x7fffffff;
-    for (int j = 0; j * 64 + lane < E; ++j) {
-      if (used & (1u << j)) continue;
-      const int e = j * 64 + lane;
-      const float x = rr[e];
-      if (be == 0x7fffffff || x > v || (x == v && e < be)) { v = x; be = e; }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + 64 * j;
+      if (e < E && !(used & (1u << j)) && (be == 0x7fffffff || v[j] > bv)) { bv = v[j]; be = e; }
     }
-    argmax_pair(v, be);
+    argmax_pair(bv, be);
     if ((be & 63) == lane) used |= 1u << (be >> 6);
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-      if (q == s) { sel_v[q] = v; sel_e[q] = be; }
+    sel_v[s] = bv;
+    sel_e[s] = be;
   }
-  if (lane == 0) {
-    float ex[8], sum = 0.f;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      ex[q] = q < K ? expf(sel_v[q] - sel_v[0]) : 0.f;
-      sum += ex[q];
-    }
+  if (lane < K) {
+    float sum = 0.f, mine = 0.f;
+    int my_e = 0;
 #pragma unroll
     for (int q = 0; q < 8; ++q)
       if (q < K) {
-        a.idx[(long long)t * K + q] = sel_e[q];
-        a.gates[(long long)t * K + q] = ex[q] / sum;
+        const float x = expf(sel_v[q] - sel_v[0]);
+        sum += x;
+        if (q == lane) { mine = x; my_e = sel_e[q]; }
       }
+    a.idx[(long long)t * K + lane] = my_e;
+    a.gates[(long long)t * K + lane] = mine / sum;
   }
 }
 
@@ -219,8 +214,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
     attr_set = true;
   }
   if (a.mode == ROUTE_LOGITS) {
-    const int blocks = (a.rows + kRowsPerBlock - 1) / kRowsPerBlock;
-    hipLaunchKernelGGL(k_route_topk, dim3(blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_route_topk, dim3(a.rows), dim3(64), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

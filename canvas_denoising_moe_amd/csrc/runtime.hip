@@ -52,6 +52,10 @@ struct dg_ctx {
         *conf = nullptr, *part_o = nullptr, *part_m = nullptr, *part_l = nullptr;
   void *a = nullptr, *f = nullptr, *q = nullptr, *kc = nullptr, *vc = nullptr, *o = nullptr, *u = nullptr;
   int32_t *idx = nullptr, *offsets = nullptr, *perm = nullptr, *arows = nullptr, *pred = nullptr;
+  // fused LM head + argmax (bf16): per-(vocabulary tile, row) partials
+  float *lm_m = nullptr, *lm_s = nullptr;
+  int32_t* lm_i = nullptr;
+  bool lm_fused = false;
   long long part_cap = 0;
   int32_t* trace = nullptr;
   // expert work list built by the router
@@ -242,7 +246,15 @@ dg_status alloc_workspaces(dg_ctx* ctx) {
   TRY(dalloc_t(ctx, &ctx->arows, rows_r * 4));
   TRY(dalloc(ctx, &ctx->u, rows_r * F * es));
   TRY(dalloc_t(ctx, &ctx->y, rows_r * H * 4));
-  if (c.has_lm_head) TRY(dalloc_t(ctx, &ctx->logits, M * (size_t)c.vocab * 4));
+  ctx->lm_fused = c.has_lm_head && ctx->bf16 && lm_head_supported((int)M, c.hidden, c.vocab);
+  if (ctx->lm_fused) {
+    const size_t parts = (size_t)((c.vocab / 16 + 15) / 16) * M;
+    TRY(dalloc_t(ctx, &ctx->lm_m, parts * 4));
+    TRY(dalloc_t(ctx, &ctx->lm_s, parts * 4));
+    TRY(dalloc_t(ctx, &ctx->lm_i, parts * 4));
+  } else if (c.has_lm_head) {
+    TRY(dalloc_t(ctx, &ctx->logits, M * (size_t)c.vocab * 4));
+  }
   TRY(dalloc_t(ctx, &ctx->pred, M * 4));
   TRY(dalloc_t(ctx, &ctx->conf, M * 4));
   TRY(dalloc_t(ctx, &ctx->rope, (size_t)c.max_batch * c.canvas_len * (D / 2) * sizeof(float2)));
@@ -426,6 +438,27 @@ dg_status enqueue_layers(dg_ctx* ctx, int B, const void* w_last_out, int l0 = 0,
   return DG_OK;
 }
 
+// Tied LM head over h [M, H] into per-row argmax and confidence: fused on
+// matrix cores (bf16), else logits into the workspace and a row reduction.
+LmArgs lm_args(dg_ctx* ctx, const void* h, int M) {
+  LmArgs la{};
+  la.h = h; la.M = M; la.K = ctx->c.hidden; la.V = ctx->c.vocab; la.E = ctx->embed;
+  la.part_m = ctx->lm_m; la.part_s = ctx->lm_s; la.part_i = ctx->lm_i;
+  return la;
+}
+dg_status enqueue_head(dg_ctx* ctx, const void* h, int M, int32_t* pred, float* conf, KTime t = {}) {
+  const dg_config& c = ctx->c;
+  if (ctx->lm_fused) {
+    LmArgs la = lm_args(ctx, h, M);
+    la.pred = pred; la.conf = conf;
+    HIPX(launch_lm_head(la, true, ctx->st, t));
+    return DG_OK;
+  }
+  TRY(enqueue_dense(ctx, h, c.hidden, ctx->embed, c.hidden, c.vocab, M, ctx->logits, c.vocab, false, t));
+  HIPX(launch_argmax_conf(ctx->logits, M, c.vocab, pred, conf, ctx->st));
+  return DG_OK;
+}
+
 dg_status enqueue_pass(dg_ctx* ctx, int B, int32_t* tokens, uint8_t* locked, const StepsArg& steps) {
   const dg_config& c = ctx->c;
   const int N = c.canvas_len, M = B * N, H = c.hidden;
@@ -435,9 +468,7 @@ dg_status enqueue_pass(dg_ctx* ctx, int B, int32_t* tokens, uint8_t* locked, con
   n0.x = ctx->x; n0.w_out = ctx->L[0].norm[0]; n0.out = ctx->a;
   HIPX(launch_residual_norm(ctx->bf16, n0, ctx->st));
   TRY(enqueue_layers(ctx, B, ctx->norm_final));
-  TRY(enqueue_dense(ctx, ctx->a, H, ctx->embed, H, c.vocab, M, ctx->logits, c.vocab, false,
-                    prof_kernel(ctx, DG_PROF_LM_HEAD)));
-  HIPX(launch_argmax_conf(ctx->logits, M, c.vocab, ctx->pred, ctx->conf, ctx->st));
+  TRY(enqueue_head(ctx, ctx->a, M, ctx->pred, ctx->conf, prof_kernel(ctx, DG_PROF_LM_HEAD)));
   HIPX(launch_lock_select(B, N, ctx->conf, ctx->pred, tokens, locked, steps, ctx->st));
   return DG_OK;
 }
@@ -804,8 +835,23 @@ dg_status dg_k_lm_head(dg_ctx* ctx, int32_t batch, const void* h, float* logits)
   if (!c.has_lm_head || !ctx->embed_set) return fail(ctx, DG_ESTATE, "embedding not loaded");
   if (batch < 1 || batch > c.max_batch) return fail(ctx, DG_EINVAL, "batch out of range");
   if (!h || !logits) return fail(ctx, DG_EINVAL, "h and logits are required");
-  return enqueue_dense(ctx, h, c.hidden, ctx->embed, c.hidden, c.vocab, batch * c.canvas_len, logits, c.vocab,
-                       false);
+  const int M = batch * c.canvas_len;
+  if (ctx->lm_fused) {
+    LmArgs la = lm_args(ctx, h, M);
+    la.logits = logits;
+    HIPX(launch_lm_head(la, false, ctx->st));
+    return DG_OK;
+  }
+  return enqueue_dense(ctx, h, c.hidden, ctx->embed, c.hidden, c.vocab, M, logits, c.vocab, false);
+}
+
+dg_status dg_k_lm_argmax(dg_ctx* ctx, int32_t batch, const void* h, int32_t* pred, float* conf) {
+  TRY(enter(ctx));
+  const dg_config& c = ctx->c;
+  if (!c.has_lm_head || !ctx->embed_set) return fail(ctx, DG_ESTATE, "embedding not loaded");
+  if (batch < 1 || batch > c.max_batch) return fail(ctx, DG_EINVAL, "batch out of range");
+  if (!h || !pred || !conf) return fail(ctx, DG_EINVAL, "h, pred and conf are required");
+  return enqueue_head(ctx, h, batch * c.canvas_len, pred, conf);
 }
 
 dg_status dg_profile(dg_ctx* ctx, int32_t mask) {

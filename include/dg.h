@@ -231,6 +231,14 @@ dg_status dg_k_moe_ffn(dg_ctx* ctx, int32_t layer, int32_t batch, const void* f,
 /* Tied LM head: h T [batch*N, H] -> logits float [batch*N, V] = h @ embed^T. */
 dg_status dg_k_lm_head(dg_ctx* ctx, int32_t batch, const void* h, float* logits);
 
+/* Tied LM head reduced to per-row prediction and confidence, as a pass runs
+ * it (bf16 contexts: fused, the logits never reach memory): h T [batch*N, H]
+ * -> pred int32 [batch*N] = the lowest id among the largest logits, conf
+ * float [batch*N] = 1 / sum_v exp(l_v - l_max) ([HandsOn] "Detailed Specs":
+ * tied embedding and LM head; the output distribution judges which tokens
+ * are final). */
+dg_status dg_k_lm_argmax(dg_ctx* ctx, int32_t batch, const void* h, int32_t* pred, float* conf);
+
 /* ---- kernel timing ----------------------------------------------------------
  * Per-launch device durations of selected kernel classes.  dg_profile(ctx,
  * mask) with mask != 0 clears the record and times every later launch of the

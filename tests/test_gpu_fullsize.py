@@ -182,6 +182,31 @@ def test_c3_lm_head_sampled_rows(torch, c3ctx):
     assert np.array_equal(np.argmax(got, axis=1)[clear], np.argmax(ref, axis=1)[clear])
 
 
+def test_c3_fused_argmax_equals_row_reduction(torch, c3ctx):
+    # the pass's fused LM head + argmax against the row reduction of the
+    # same kernel's logits over the whole 262144-entry vocabulary
+    w = C3
+    m = w.model
+    M = w.batch * m.canvas_len
+    say("C3 fused argmax")
+    h = upload.to_device(gen.activations(26, 1, (M, m.hidden), std=1.0, dtype="bf16"), "bf16")
+    logits = torch.empty((M, m.vocab), dtype=torch.float32, device="cuda")
+    c3ctx.k_lm_head(w.batch, h, logits)
+    pred = torch.empty(M, dtype=torch.int32, device="cuda")
+    conf = torch.empty(M, dtype=torch.float32, device="cuda")
+    c3ctx.k_lm_argmax(w.batch, h, pred, conf)
+    pred2 = torch.empty_like(pred)
+    conf2 = torch.empty_like(conf)
+    dg_mod = __import__("canvas_denoising_moe_amd")
+    dg_mod.k_argmax_conf(logits, pred2, conf2)
+    torch.cuda.synchronize()
+    assert torch.equal(pred, pred2)
+    c, c2 = conf.cpu().numpy().astype(np.float64), conf2.cpu().numpy().astype(np.float64)
+    e = float(np.max(np.abs(c - c2) / c2))
+    print(f"C3 fused argmax: pred equal, conf rel diff {e:.3e}")
+    assert e <= 1e-6
+
+
 def test_c3_moe_sampled_tokens(torch, c3ctx):
     w = C3
     m = w.model

@@ -274,3 +274,54 @@ def test_moe_ffn_matches_oracle(torch, c2ctx):
     e = rel_err(host64(out), m_ref)
     print(f"moe_ffn rel err {e:.3e}")
     assert e <= TOL["bf16"]
+
+
+# ------------------------------------------------------------ LM head ------
+
+LM_MODEL = configs.ModelConfig(
+    n_layers=1, hidden=256, n_heads=2, n_kv_heads=1, head_dim=128, n_experts=16, top_k=2,
+    expert_ffn=64, vocab=1040, canvas_len=48, window=1024, global_layer_mask=0b1,
+    has_lm_head=True, dtype="bf16")
+LM_W = configs.Workload(name="lm-test", model=LM_MODEL, batch=2, prompt_len=16, n_steps=1, seed=19)
+
+
+def test_lm_head_and_fused_argmax(torch, dg):
+    # 96 rows (a partial 128-row group) and 65 column blocks (a partial
+    # 256-column vocabulary tile); two rows with planted exact ties
+    m = LM_MODEL
+    B, N, V, H = LM_W.batch, m.canvas_len, m.vocab, m.hidden
+    M = B * N
+    say("lm head", M, V)
+    E_bits = gen.embed(LM_W)
+    h_bits = gen.activations(25, 1, (M, H), std=1.0, dtype="bf16")
+    h_bits[5] = 0          # every logit 0: argmax id 0, conf 1/V
+    E_bits[700] = E_bits[300]  # ids 300 and 700 tie in every row: 300 can win, 700 never
+    with dg.Context(m, max_batch=B, max_prompt_len=LM_W.prompt_len) as ctx:
+        ctx.set_embedding(upload.to_device(E_bits, "bf16"), upload.to_device(gen.norm_final(LM_W), "bf16"))
+        h = upload.to_device(h_bits, "bf16")
+        logits = torch.empty((M, V), dtype=torch.float32, device="cuda")
+        ctx.k_lm_head(B, h, logits)
+        pred = torch.full((M,), -1, dtype=torch.int32, device="cuda")
+        conf = torch.zeros(M, dtype=torch.float32, device="cuda")
+        ctx.k_lm_argmax(B, h, pred, conf)
+        pred2 = torch.full((M,), -1, dtype=torch.int32, device="cuda")
+        conf2 = torch.zeros(M, dtype=torch.float32, device="cuda")
+        dg.k_argmax_conf(logits, pred2, conf2)
+        torch.cuda.synchronize()
+    E = om.bf16_bits_to_f64(E_bits)
+    ref = om.lm_logits(om.bf16_bits_to_f64(h_bits), E)
+    e = rel_err(host64(logits), ref)
+    print(f"LM head logits rel err {e:.3e}")
+    assert e <= TOL["bf16"]
+    # the fused reduction equals the row reduction of the same logits
+    p, c = pred.cpu().numpy(), conf.cpu().numpy().astype(np.float64)
+    assert np.array_equal(p, pred2.cpu().numpy())
+    assert np.max(np.abs(c - conf2.cpu().numpy()) / c) <= 1e-6
+    assert p[5] == 0 and abs(c[5] * V - 1.0) < 1e-5
+    assert not np.any(p == 700)
+    # and the oracle's decision wherever its top-2 gap clears the rounding noise
+    p_ref, c_ref = om.argmax_conf(ref)
+    srt = np.sort(ref, axis=1)
+    clear = (srt[:, -1] - srt[:, -2]) > 1e-4
+    assert np.array_equal(p[clear], p_ref[clear])
+    assert np.max(np.abs(c - c_ref) / c_ref) <= 1e-3
