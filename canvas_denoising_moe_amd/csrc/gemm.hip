@@ -334,7 +334,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g, EpiArgs e) {
 // through its L2.  Wider entries (MT = 2) halve the weight reads of dense
 // GEMMs and of experts with more than 16 rows.
 // ----------------------------------------------------------------------------
-constexpr int kStreamLds = 64 * 1024;  // LDS budget of one A chunk
+constexpr int kStreamLds = 32 * 1024;  // LDS budget of one A chunk
 
 template <typename T, int MT>
 constexpr int stream_kc() { return kStreamLds / (16 * MT * 32 * (int)sizeof(T)); }  // k-steps per chunk
