@@ -28,7 +28,7 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int D>
+template <int D, bool ALIGNED>
 __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int QT, int xcd_map) {
   constexpr int KT = 64;            // keys per tile
   constexpr int KLD = D + 8;        // padded LDS row of K (elements)
@@ -86,66 +86,81 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int QT, int xcd_m
   float m_run = -INFINITY, l_run = 0.f;
   const float sc = kLog2e / sqrtf((float)D);
 
-  uint4 kreg[KVEC], vreg[VVEC];
-  auto load_tile = [&](int t0) {
+  // K/V tiles go global -> registers -> LDS, two tiles ahead of the one being
+  // consumed.  ALIGNED (every 8-key group of V^T lies in one source and the
+  // key count is a multiple of 8): loads are unconditional, with key indices
+  // clamped into [k0, k1) -- rows past the split's last key only ever meet a
+  // score of -inf, i.e. P = 0 -- so the compiler's load counters stay exact
+  // and both tiles in flight stay in flight.  Otherwise partial groups are
+  // gathered element by element.
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  v4u kreg[2][KVEC], vreg[2][VVEC];
+  auto load_tile = [&](v4u* kr, v4u* vr, int t0) {
 #pragma unroll
     for (int it = 0; it < KVEC; ++it) {
       const int v = tid + it * 256;
       const int row = v / (D / 8), c8 = v % (D / 8);
-      const int key = t0 + row;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (key < k1) {
+      int key = t0 + row;
+      if constexpr (ALIGNED) {
+        key = min(key, k1 - 1);
         const bf16_t* src = key < Lw ? kp + (long long)key * D : kc + (long long)(key - Lw) * D;
-        val = *reinterpret_cast<const uint4*>(src + c8 * 8);
+        kr[it] = *reinterpret_cast<const v4u*>(src + c8 * 8);
+      } else {
+        v4u val = {0u, 0u, 0u, 0u};
+        if (key < k1) {
+          const bf16_t* src = key < Lw ? kp + (long long)key * D : kc + (long long)(key - Lw) * D;
+          val = *reinterpret_cast<const v4u*>(src + c8 * 8);
+        }
+        kr[it] = val;
       }
-      kreg[it] = val;
     }
 #pragma unroll
     for (int it = 0; it < VVEC; ++it) {
       const int v = tid + it * 256;
       const int d = v / (KT / 8), c8 = v % (KT / 8);
-      const int key = t0 + c8 * 8;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      const bool in_p = key + 8 <= Lw && (Lw & 7) == 0;
-      const bool in_c = key >= Lw && ((key - Lw) & 7) == 0 && (N & 7) == 0;
-      if (key + 8 <= k1 && (in_p || in_c)) {
-        const bf16_t* src = in_p ? vp + (long long)d * Lw + key : vc + (long long)d * N + (key - Lw);
-        val = *reinterpret_cast<const uint4*>(src);
+      int key = t0 + c8 * 8;
+      if constexpr (ALIGNED) {
+        key = min(key, k1 - 8);
+        const bf16_t* src = key < Lw ? vp + (long long)d * Lw + key : vc + (long long)d * N + (key - Lw);
+        vr[it] = *reinterpret_cast<const v4u*>(src);
       } else {
-        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        v4u val = {0u, 0u, 0u, 0u};
+        const bool in_p = key + 8 <= Lw && (Lw & 7) == 0;
+        const bool in_c = key >= Lw && ((key - Lw) & 7) == 0 && (N & 7) == 0;
+        if (key + 8 <= k1 && (in_p || in_c)) {
+          const bf16_t* src = in_p ? vp + (long long)d * Lw + key : vc + (long long)d * N + (key - Lw);
+          val = *reinterpret_cast<const v4u*>(src);
+        } else {
+          uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int kk = key + j;
-          uint32_t x = 0;
-          if (kk < k1) x = kk < Lw ? vp[(long long)d * Lw + kk] : vc[(long long)d * N + (kk - Lw)];
-          w[j >> 1] |= x << ((j & 1) * 16);
+          for (int j = 0; j < 8; ++j) {
+            const int kk = key + j;
+            uint32_t x = 0;
+            if (kk < k1) x = kk < Lw ? vp[(long long)d * Lw + kk] : vc[(long long)d * N + (kk - Lw)];
+            w[j >> 1] |= x << ((j & 1) * 16);
+          }
+          val = v4u{w[0], w[1], w[2], w[3]};
         }
-        val = make_uint4(w[0], w[1], w[2], w[3]);
+        vr[it] = val;
       }
-      vreg[it] = val;
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](const v4u* kr, const v4u* vr) {
 #pragma unroll
     for (int it = 0; it < KVEC; ++it) {
       const int v = tid + it * 256;
       const int row = v / (D / 8), c8 = v % (D / 8);
-      *reinterpret_cast<uint4*>(&Ks[row * KLD + c8 * 8]) = kreg[it];
+      *reinterpret_cast<v4u*>(&Ks[row * KLD + c8 * 8]) = kr[it];
     }
 #pragma unroll
     for (int it = 0; it < VVEC; ++it) {
       const int v = tid + it * 256;
       const int d = v / (KT / 8), c8 = v % (KT / 8);
-      *reinterpret_cast<uint4*>(&Vs[d * VLD + c8 * 8]) = vreg[it];
+      *reinterpret_cast<v4u*>(&Vs[d * VLD + c8 * 8]) = vr[it];
     }
   };
-
-  if (k0 < k1) load_tile(k0);
-  for (int t0 = k0; t0 < k1; t0 += KT) {
-    store_tile();
-    __syncthreads();
-    if (t0 + KT < k1) load_tile(t0 + KT);
-
+  // one 64-key tile of the online softmax from LDS
+  auto consume = [&](int t0) {
     // S^T for 4 blocks of 16 keys: sacc[kb][r] = score(key t0+kb*16+lg*4+r, query lc)
     floatx4 sacc[4];
 #pragma unroll
@@ -210,6 +225,24 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int QT, int xcd_m
                                                             oacc[db], 0, 0, 0);
       }
     }
+  };
+
+  const int ntiles = k1 > k0 ? (k1 - k0 + KT - 1) / KT : 0;
+  if (ntiles > 0) {
+    load_tile(kreg[0], vreg[0], k0);
+    load_tile(kreg[1], vreg[1], k0 + KT);  // clamped (ALIGNED) or masked past the split
+  }
+  for (int it = 0; it < ntiles; it += 2) {
+    store_tile(kreg[0], vreg[0]);
+    __syncthreads();
+    load_tile(kreg[0], vreg[0], k0 + (it + 2) * KT);
+    consume(k0 + it * KT);
+    __syncthreads();
+    if (it + 1 >= ntiles) break;
+    store_tile(kreg[1], vreg[1]);
+    __syncthreads();
+    load_tile(kreg[1], vreg[1], k0 + (it + 3) * KT);
+    consume(k0 + (it + 1) * KT);
     __syncthreads();
   }
 
@@ -390,9 +423,16 @@ hipError_t launch_attention(int is_bf16, const AttnArgs& a0, hipStream_t st, KTi
     const dim3 grid((unsigned)(units * QT));
     // every canvas in one split: the kernel stores the output itself and closes the timing
     hipEvent_t stop1 = smax == 1 ? t.stop : nullptr;
-    hipError_t e = a.D == 128
-        ? launch_k(k_attn_mfma<128>, grid, dim3(256), 0, st, t.start, stop1, a, QT, xcd_map)
-        : launch_k(k_attn_mfma<64>, grid, dim3(256), 0, st, t.start, stop1, a, QT, xcd_map);
+    // every 8-key group of V^T in one source, and key counts multiples of 8
+    bool aligned = (a.N & 7) == 0;
+    for (int b = 0; b < a.B; ++b) aligned = aligned && (a.lw[b] & 7) == 0;
+    hipError_t e;
+    if (a.D == 128)
+      e = aligned ? launch_k(k_attn_mfma<128, true>, grid, dim3(256), 0, st, t.start, stop1, a, QT, xcd_map)
+                  : launch_k(k_attn_mfma<128, false>, grid, dim3(256), 0, st, t.start, stop1, a, QT, xcd_map);
+    else
+      e = aligned ? launch_k(k_attn_mfma<64, true>, grid, dim3(256), 0, st, t.start, stop1, a, QT, xcd_map)
+                  : launch_k(k_attn_mfma<64, false>, grid, dim3(256), 0, st, t.start, stop1, a, QT, xcd_map);
     if (e != hipSuccess || smax == 1) return e;
     return launch_k(k_attn_merge<bf16_t>, dim3((unsigned)rows_all), dim3(a.D), 0, st, nullptr, t.stop, a);
   }
