@@ -76,6 +76,7 @@ _SIGS = {
 }
 
 PROF_GATE_UP, PROF_DOWN, PROF_ATTN, PROF_LM_HEAD, PROF_PASS, PROF_COUNT = range(6)
+PROF_KEEP = 1 << 30
 
 
 def lib():
@@ -254,15 +255,16 @@ class Context:
         self._c(lib().dg_set_trace(self._h, _ptr(route_idx, torch.int32, "route_idx")))
 
     # -- kernel timing -------------------------------------------------------------
-    def profile(self, kernels=()):
-        """Time the given kernel classes (PROF_* ids; True = all, () = off)."""
+    def profile(self, kernels=(), keep: bool = False):
+        """Time the given kernel classes (PROF_* ids; True = all, () = off).
+        keep: change the classes without synchronising or clearing the record."""
         if kernels is True:
             mask = (1 << PROF_COUNT) - 1
         else:
             mask = 0
             for k in (kernels or ()):
                 mask |= 1 << int(k)
-        self._c(lib().dg_profile(self._h, mask))
+        self._c(lib().dg_profile(self._h, mask | (PROF_KEEP if keep else 0)))
 
     def profile_read(self, kernel: int):
         """(launches, total milliseconds) recorded for a kernel class."""

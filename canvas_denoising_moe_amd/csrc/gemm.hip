@@ -505,7 +505,9 @@ hipError_t run_stream_mt(const StreamArgs& g, const EpiArgs& e, hipStream_t s, K
   switch (e.kind) {
     case EPI_STORE_F32: return run_stream<T, MT, 2, EPI_STORE_F32, 8>(g, e, s, t);
     case EPI_GEGLU: return run_stream<T, MT, 2, EPI_GEGLU, 8>(g, e, s, t);
-    case EPI_DOWN: return run_stream<T, MT, 2, EPI_DOWN, 8>(g, e, s, t);
+    // down: K = F is short, so wider tiles (4 n-blocks per wave) halve the A
+    // re-staging at the same ring depth in bytes
+    case EPI_DOWN: return run_stream<T, MT, (MT == 2 ? 4 : 2), EPI_DOWN, (MT == 2 ? 4 : 8)>(g, e, s, t);
     case EPI_QKV: return run_stream<T, MT, 2, EPI_QKV, 8>(g, e, s, t);
   }
   return hipErrorInvalidValue;

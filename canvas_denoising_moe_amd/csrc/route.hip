@@ -11,7 +11,9 @@
 //     entries the streaming expert GEMMs consume.
 //
 // The result never depends on scheduling: bits are set with order-independent
-// LDS atomics, and ranks are popcounts of the bitmap.
+// LDS atomics, and ranks are popcounts of the bitmap.  (Routing every token of
+// a canvas inside the one scatter workgroup was tried and is far slower: the
+// per-token load latencies then run in sequence.)
 #include "common.h"
 
 namespace {
@@ -26,12 +28,12 @@ DG_DEV void argmax_pair(float& v, int& e) {
   }
 }
 
-// One wave per token: lane l holds the logits of experts l, l + 64, ... in
-// registers (split-K partials summed in slice order), the k winners come out
-// of k wave-wide arg-max rounds, and lane s < k writes slot s.
-__global__ __launch_bounds__(64) void k_route_topk(RouteArgs a) {
+// Top-k of token t by one wave: lane l holds the logits of experts l, l + 64,
+// ... in registers (split-K partials summed in slice order), the k winners
+// come out of k wave-wide arg-max rounds; lane s < k returns slot s's expert
+// (and writes idx / gates), other lanes return -1.
+DG_DEV int topk_token(const RouteArgs& a, int t, int lane) {
   const int E = a.E, K = a.k;
-  const int t = blockIdx.x, lane = threadIdx.x;
   const int parts = a.logit_parts > 0 ? a.logit_parts : 1;
   float v[4];
 #pragma unroll
@@ -66,9 +68,9 @@ __global__ __launch_bounds__(64) void k_route_topk(RouteArgs a) {
     sel_v[s] = bv;
     sel_e[s] = be;
   }
+  int my_e = -1;
   if (lane < K) {
     float sum = 0.f, mine = 0.f;
-    int my_e = 0;
 #pragma unroll
     for (int q = 0; q < 8; ++q)
       if (q < K) {
@@ -79,38 +81,23 @@ __global__ __launch_bounds__(64) void k_route_topk(RouteArgs a) {
     a.idx[(long long)t * K + lane] = my_e;
     a.gates[(long long)t * K + lane] = mine / sum;
   }
+  return my_e;
 }
 
-__global__ __launch_bounds__(1024) void k_route_scatter(RouteArgs a) {
-  extern __shared__ uint32_t dyn[];  // bitmap [E][W] words, then per-word prefix counts [E][W]
-  __shared__ int s_cnt[256], s_off[258], s_ent[256];
-  __shared__ int s_total;
+__global__ __launch_bounds__(64) void k_route_topk(RouteArgs a) {
+  topk_token(a, blockIdx.x, threadIdx.x);
+}
+
+// The scatter once the membership bitmap bm [E][W] is complete in LDS: counts,
+// offsets and entries per expert, then every routed row's position.  ids(p)
+// returns the expert of entry p = t * k + s.
+template <typename Ids>
+DG_DEV void scatter_rows(const RouteArgs& a, uint32_t* bm, int* pre, int* s_cnt, int* s_off, int* s_ent,
+                         int* s_total, Ids ids) {
   const int E = a.E, K = a.k;
   const int tid = threadIdx.x, nt = blockDim.x;
-  const int W = (a.rows + 31) >> 5, EW = E * W;
-  uint32_t* bm = dyn;
-  int* pre = reinterpret_cast<int*>(dyn + EW);
+  const int W = (a.rows + 31) >> 5;
   const int RK = a.rows * K;
-  for (int i = tid; i < EW; i += nt) bm[i] = 0u;
-  __syncthreads();
-  for (int p0 = tid; p0 < RK; p0 += nt * 8) {
-    int ev[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {  // expert ids of 8 entries in flight together
-      const int p = p0 + u * nt;
-      ev[u] = p < RK ? a.idx[p] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int p = p0 + u * nt;
-      if (p < RK) {
-        const int e = ev[u] < 0 ? 0 : (ev[u] >= E ? E - 1 : ev[u]);  // ids stay inside the bitmap
-        const int tt = p / K;
-        atomicOr(&bm[e * W + (tt >> 5)], 1u << (tt & 31));
-      }
-    }
-  }
-  __syncthreads();
   for (int e = tid; e < E; e += nt) {
     int c = 0;
     for (int w = 0; w < W; ++w) {
@@ -154,8 +141,8 @@ __global__ __launch_bounds__(1024) void k_route_scatter(RouteArgs a) {
       // every row's ids are distinct; repeated ids leave [off, rows * k) unused)
       s_off[E] = RK;
       s_off[E + 1] = RK + a.rows;
-      s_total = ne + n_shared;
-      if (a.work_count) *a.work_count = s_total;
+      *s_total = ne + n_shared;
+      if (a.work_count) *a.work_count = ne + n_shared;
     }
   }
   __syncthreads();
@@ -167,16 +154,16 @@ __global__ __launch_bounds__(1024) void k_route_scatter(RouteArgs a) {
       for (int q = 0; q * ER < c; ++q)
         a.work[s_ent[e] + q] = make_int4(e, base + q * ER, base + min(c, q * ER + ER), 0);
     }
-    const int ne = s_total - n_shared;
+    const int ne = *s_total - n_shared;
     for (int q = tid; q < n_shared; q += nt)
       a.work[ne + q] = make_int4(E, RK + q * ER, RK + min(a.rows, q * ER + ER), 0);
   }
   for (int p0 = tid; p0 < RK; p0 += nt * 8) {
     int ev[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < 8; ++u) {  // expert ids of 8 entries in flight together
       const int p = p0 + u * nt;
-      ev[u] = p < RK ? a.idx[p] : 0;
+      ev[u] = p < RK ? ids(p) : 0;
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -197,6 +184,40 @@ __global__ __launch_bounds__(1024) void k_route_scatter(RouteArgs a) {
       if (a.a_rows) a.a_rows[RK + tt] = tt;
     }
   }
+}
+
+// Scatter of routing already in idx (given ids, or a preceding top-k launch).
+__global__ __launch_bounds__(1024) void k_route_scatter(RouteArgs a) {
+  extern __shared__ uint32_t dyn[];  // bitmap [E][W] words, then per-word prefix counts [E][W]
+  __shared__ int s_cnt[256], s_off[258], s_ent[256];
+  __shared__ int s_total;
+  const int E = a.E, K = a.k;
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int W = (a.rows + 31) >> 5, EW = E * W;
+  uint32_t* bm = dyn;
+  int* pre = reinterpret_cast<int*>(dyn + EW);
+  const int RK = a.rows * K;
+  for (int i = tid; i < EW; i += nt) bm[i] = 0u;
+  __syncthreads();
+  for (int p0 = tid; p0 < RK; p0 += nt * 8) {
+    int ev[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = p0 + u * nt;
+      ev[u] = p < RK ? a.idx[p] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = p0 + u * nt;
+      if (p < RK) {
+        const int e = ev[u] < 0 ? 0 : (ev[u] >= E ? E - 1 : ev[u]);  // ids stay inside the bitmap
+        const int tt = p / K;
+        atomicOr(&bm[e * W + (tt >> 5)], 1u << (tt & 31));
+      }
+    }
+  }
+  __syncthreads();
+  scatter_rows(a, bm, pre, s_cnt, s_off, s_ent, &s_total, [&](int p) { return a.idx[p]; });
 }
 
 }  // namespace

@@ -856,11 +856,19 @@ dg_status dg_k_lm_argmax(dg_ctx* ctx, int32_t batch, const void* h, int32_t* pre
 
 dg_status dg_profile(dg_ctx* ctx, int32_t mask) {
   TRY(enter(ctx));
+  const bool keep = (mask & DG_PROF_KEEP) != 0;
+  mask &= ~DG_PROF_KEEP;
   if (mask & ~DG_PROF_ALL) return fail(ctx, DG_EINVAL, "profile mask 0x%x has unknown bits", mask);
-  if (mask) {
+  if (mask && !keep) {
     HIPX(hipStreamSynchronize(ctx->st));  // recorded events are done before reuse
     for (auto& r : ctx->prof_rec) r.clear();
     ctx->ev_used = 0;
+    // events for 512 timed launches up front, so timing creates none in a timed loop
+    while (ctx->ev_pool.size() < 1024) {
+      hipEvent_t e = nullptr;
+      HIPX(hipEventCreate(&e));
+      ctx->ev_pool.push_back(e);
+    }
   }
   ctx->prof = mask;
   return DG_OK;

@@ -241,9 +241,11 @@ dg_status dg_k_lm_argmax(dg_ctx* ctx, int32_t batch, const void* h, int32_t* pre
 
 /* ---- kernel timing ----------------------------------------------------------
  * Per-launch device durations of selected kernel classes.  dg_profile(ctx,
- * mask) with mask != 0 clears the record and times every later launch of the
- * classes whose bit (1 << DG_PROF_x) is set; mask = 0 switches timing off (the
- * record stays).  Kernel classes are timed by HIP events bound to their own
+ * mask) with mask != 0 synchronises the stream, clears the record and times
+ * every later launch of the classes whose bit (1 << DG_PROF_x) is set; mask = 0
+ * switches timing off (the record stays).  With DG_PROF_KEEP or'd in, the mask
+ * changes without synchronising or clearing (timing resumes into the same
+ * record), so timing can be switched on for some passes of a timed loop.  Kernel classes are timed by HIP events bound to their own
  * dispatches (start of the first kernel, end of the last); DG_PROF_PASS by an
  * event pair recorded on the stream around the pass.  Each timed launch adds a
  * few microseconds of dispatch latency around itself, so time only what is
@@ -256,7 +258,8 @@ typedef enum dg_prof_kernel {
   DG_PROF_LM_HEAD = 3,  /* tied LM head GEMM */
   DG_PROF_PASS = 4,     /* one whole denoise pass */
   DG_PROF_COUNT = 5,
-  DG_PROF_ALL = (1 << 5) - 1
+  DG_PROF_ALL = (1 << 5) - 1,
+  DG_PROF_KEEP = 1 << 30
 } dg_prof_kernel;
 dg_status dg_profile(dg_ctx* ctx, int32_t mask);
 dg_status dg_profile_read(dg_ctx* ctx, int32_t kernel, int32_t* launches, double* total_ms);
