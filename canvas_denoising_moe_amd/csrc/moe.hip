@@ -25,13 +25,13 @@ DG_DEV float f4dot(float4 a) { return a.x * a.x + a.y * a.y + a.z * a.z + a.w * 
 // out[t] = T(RMSNorm(x[t]) * (1 + w_out))      (skipped without w_out)
 // delta_t: mode 0 one row of `delta`; mode 1 the MoE combine
 //   sum_{s<k} y[t*k + s] (slot order) + y[rows*k + t]; mode 2 nothing.
-// One workgroup per token; thread i owns float4 columns i, i + 256, ... (NV of
-// them, H <= 1024 * NV).  Every term of the row (up to k + 1 MoE outputs) is
+// One workgroup of NT threads per token; thread i owns float4 columns i,
+// i + NT, ... (NV of them, H <= 4 * NT * NV).  Every term of the row (up to k + 1 MoE outputs) is
 // loaded before any arithmetic, so a token's whole working set is in flight at
 // once; sums of squares are fixed-order block reductions.
-template <typename T, int NV>
-__global__ __launch_bounds__(256) void k_residual_norm(NormArgs a) {
-  __shared__ float red[8];
+template <typename T, int NV, int NT>
+__global__ __launch_bounds__(NT) void k_residual_norm(NormArgs a) {
+  __shared__ float red[32];
   const int t = blockIdx.x, tid = threadIdx.x;
   const int H = a.H, n4 = H >> 2;
   float4* x4 = reinterpret_cast<float4*>(a.x + (long long)t * H);
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void k_residual_norm(NormArgs a) {
   const T* wo = reinterpret_cast<const T*>(a.w_out);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int c4 = tid + 256 * i;
+    const int c4 = tid + NT * i;
     xv[i] = c4 < n4 ? x4[c4] : z4;
     // the norm weights too, so no load waits behind a reduction
     gd[i] = (wd && a.mode != 2 && c4 < n4) ? load4<T>(wd + 4 * c4) : z4;
@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256) void k_residual_norm(NormArgs a) {
     if (a.mode == 0) {
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
-        const int c4 = tid + 256 * i;
+        const int c4 = tid + NT * i;
         dv[i] = c4 < n4 ? d4[(long long)t * n4 + c4] : z4;
       }
     } else {
@@ -63,12 +63,12 @@ __global__ __launch_bounds__(256) void k_residual_norm(NormArgs a) {
       for (int s = 0; s < 8; ++s)
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-          const int c4 = tid + 256 * i;
+          const int c4 = tid + NT * i;
           tv[s][i] = (s < a.k && c4 < n4) ? d4[((long long)t * a.k + s) * n4 + c4] : z4;
         }
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
-        const int c4 = tid + 256 * i;
+        const int c4 = tid + NT * i;
         sv[i] = c4 < n4 ? d4[((long long)a.rows * a.k + t) * n4 + c4] : z4;
       }
 #pragma unroll
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(256) void k_residual_norm(NormArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int c4 = tid + 256 * i;
+      const int c4 = tid + NT * i;
       if (c4 < n4) {
         float4 d = dv[i];
         if (wd) {
@@ -106,11 +106,11 @@ __global__ __launch_bounds__(256) void k_residual_norm(NormArgs a) {
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < NV; ++i) ss += f4dot(xv[i]);  // columns past H hold zeros
-    const float sc = rsqrtf(block_sum(ss, red + 4) / H + a.eps);
+    const float sc = rsqrtf(block_sum(ss, red + 16) / H + a.eps);
     T* out = reinterpret_cast<T*>(a.out) + (long long)t * H;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int c4 = tid + 256 * i;
+      const int c4 = tid + NT * i;
       if (c4 < n4) {
         const float4 g = go[i];
         const float4 v = xv[i];
@@ -125,11 +125,11 @@ template <typename T>
 hipError_t run_residual_norm(const NormArgs& a, hipStream_t s) {
   const int n4 = a.H >> 2;
   if (n4 <= 256)
-    hipLaunchKernelGGL((k_residual_norm<T, 1>), dim3(a.rows), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_residual_norm<T, 1, 256>), dim3(a.rows), dim3(256), 0, s, a);
   else if (n4 <= 512)
-    hipLaunchKernelGGL((k_residual_norm<T, 2>), dim3(a.rows), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_residual_norm<T, 1, 512>), dim3(a.rows), dim3(512), 0, s, a);
   else
-    hipLaunchKernelGGL((k_residual_norm<T, 4>), dim3(a.rows), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_residual_norm<T, 2, 512>), dim3(a.rows), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
