@@ -132,6 +132,9 @@ struct StreamArgs {
   int mt;  // row tiles of 16 per entry: 1 or 2
   int n_dense, dense_row0, dense_rows, dense_group;
   const int4* work; const int32_t* work_count; int work_cap;
+  // expert-major order of the work list (router output): group e's entries are
+  // [ent_off[e], ent_off[e+1]), e < n_groups; NULL: tile-major (tile, entry)
+  const int32_t* ent_off; int n_groups;
   // split-K (fp32-store epilogue only): K/32 % ksplit == 0; split s writes its
   // partial sums at out + s * split_stride
   int ksplit; long long split_stride;
@@ -174,6 +177,7 @@ struct RouteArgs {
   int32_t* idx; float* gates;
   int32_t* counts; int32_t* offsets; int32_t* perm; int32_t* a_rows;
   int4* work; int32_t* work_count;
+  int32_t* ent_off;  // [E + 2]: first work entry of every expert, the shared expert, the end
   int entry_rows;  // rows per work entry (16 * the expert GEMMs' mt)
   int with_shared;
 };

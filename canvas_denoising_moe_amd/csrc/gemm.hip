@@ -349,25 +349,48 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs g, EpiArgs e) {
   __shared__ int s_rows[ROWS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tiles = (g.NB + 4 * WN - 1) / (4 * WN);
-  const int J = g.n_dense + g.work_cap;
   const int ksplit = g.ksplit > 1 ? g.ksplit : 1;
-  const long long P = (long long)tiles * J * ksplit;
-  const long long Q = (P + 7) >> 3;
-  const long long p = (long long)(blockIdx.x & 7) * Q + (blockIdx.x >> 3);
-  if (p >= P) return;
-  const int ks = (int)(p % ksplit);
-  const long long pp = p / ksplit;
-  const int tile = (int)(pp / J), j = (int)(pp - (long long)tile * J);
-  int group, rs, re;
-  if (j < g.n_dense) {
-    group = g.dense_group;
-    rs = g.dense_row0 + j * ROWS;
-    re = min(g.dense_row0 + g.dense_rows, rs + ROWS);
-  } else {
-    const int w = j - g.n_dense;
-    if (w >= *g.work_count) return;
-    const int4 en = g.work[w];
+  int group, rs, re, tile, ks = 0;
+  if (g.ent_off) {
+    // router work list, expert-major: (expert, tile, entry of the expert), so
+    // the entries of one expert share each weight tile through L2 and one
+    // entry's A rows are re-staged for consecutive tiles while still in L2.
+    // Items are counted on the device and cut into 8 XCD slices.
+    const int nw = min(*g.work_count, g.work_cap);
+    const long long P = (long long)tiles * nw;
+    const long long Q = (P + 7) >> 3, r = blockIdx.x >> 3;
+    const long long p = (long long)(blockIdx.x & 7) * Q + r;
+    if (r >= Q || p >= P) return;
+    int lo = 0, hi = g.n_groups;  // largest e with tiles * ent_off[e] <= p
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if ((long long)tiles * g.ent_off[mid] <= p) lo = mid; else hi = mid;
+    }
+    const int base = g.ent_off[lo], ne = g.ent_off[lo + 1] - base;
+    const long long u = p - (long long)tiles * base;
+    tile = (int)(u / ne);
+    const int4 en = g.work[base + (int)(u - (long long)tile * ne)];
     group = en.x; rs = en.y; re = min(en.z, en.y + ROWS);
+  } else {
+    const int J = g.n_dense + g.work_cap;
+    const long long P = (long long)tiles * J * ksplit;
+    const long long Q = (P + 7) >> 3;
+    const long long p = (long long)(blockIdx.x & 7) * Q + (blockIdx.x >> 3);
+    if (p >= P) return;
+    ks = (int)(p % ksplit);
+    const long long pp = p / ksplit;
+    tile = (int)(pp / J);
+    const int j = (int)(pp - (long long)tile * J);
+    if (j < g.n_dense) {
+      group = g.dense_group;
+      rs = g.dense_row0 + j * ROWS;
+      re = min(g.dense_row0 + g.dense_rows, rs + ROWS);
+    } else {
+      const int w = j - g.n_dense;
+      if (w >= *g.work_count) return;
+      const int4 en = g.work[w];
+      group = en.x; rs = en.y; re = min(en.z, en.y + ROWS);
+    }
   }
   if (rs >= re) return;
   const int KBall = g.K >> 5;
@@ -483,6 +506,7 @@ hipError_t run_stream(const StreamArgs& g, const EpiArgs& e, hipStream_t s, KTim
   const int tiles = (g.NB + 4 * WN - 1) / (4 * WN);
   const int ksplit = g.ksplit > 1 ? g.ksplit : 1;
   if (((g.K >> 5) % ksplit) != 0 || (ksplit > 1 && EPI != EPI_STORE_F32)) return hipErrorInvalidValue;
+  if (g.ent_off && (ksplit > 1 || g.n_dense > 0 || g.n_groups < 1)) return hipErrorInvalidValue;
   const long long P = (long long)tiles * (g.n_dense + g.work_cap) * ksplit;
   if (P <= 0) return hipSuccess;
   const long long blocks = ((P + 7) >> 3) << 3;

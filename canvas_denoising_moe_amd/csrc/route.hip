@@ -132,11 +132,19 @@ DG_DEV void scatter_rows(const RouteArgs& a, uint32_t* bm, int* pre, int* s_cnt,
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * tid + i;
-      if (e < E) { s_off[e] = off; s_ent[e] = ne; }
+      if (e < E) {
+        s_off[e] = off;
+        s_ent[e] = ne;
+        if (a.ent_off) a.ent_off[e] = ne;
+      }
       off += c[i];
       ne += n[i];
     }
     if (tid == 63) {
+      if (a.ent_off) {
+        a.ent_off[E] = ne;                 // the shared expert's entries follow
+        a.ent_off[E + 1] = ne + n_shared;  // end
+      }
       // the shared expert's rows follow the routed ones at rows * k (== off when
       // every row's ids are distinct; repeated ids leave [off, rows * k) unused)
       s_off[E] = RK;

@@ -58,7 +58,7 @@ struct dg_ctx {
   bool lm_fused = false;
   long long part_cap = 0;
   int32_t* trace = nullptr;
-  // expert work list built by the router
+  // expert work list built by the router: entries, and [count, ent_off[E + 2]]
   int4* work = nullptr;
   int32_t* work_count = nullptr;
   std::string err;
@@ -265,8 +265,9 @@ dg_status alloc_workspaces(dg_ctx* ctx) {
   TRY(dalloc_t(ctx, &ctx->part_m, (size_t)ctx->part_cap * 4));
   TRY(dalloc_t(ctx, &ctx->part_l, (size_t)ctx->part_cap * 4));
   TRY(dalloc_t(ctx, &ctx->work, (size_t)work_cap(c, (int)M) * sizeof(int4)));
-  TRY(dalloc_t(ctx, &ctx->work_count, 4));
-  HIPX(hipMemset(ctx->work_count, 0, 4));
+  // entry count, then the first entry of every expert, the shared expert and the end
+  TRY(dalloc_t(ctx, &ctx->work_count, (size_t)(E + 3) * 4));
+  HIPX(hipMemset(ctx->work_count, 0, (size_t)(E + 3) * 4));
   HIPX(hipDeviceSynchronize());
   return DG_OK;
 }
@@ -347,7 +348,8 @@ dg_status enqueue_route(dg_ctx* ctx, int l, int M, int mode) {
   }
   r.idx = ctx->idx; r.gates = ctx->gates;
   r.offsets = ctx->offsets; r.perm = ctx->perm; r.a_rows = ctx->arows;
-  r.work = ctx->work; r.work_count = ctx->work_count; r.entry_rows = kEntryRows;
+  r.work = ctx->work; r.work_count = ctx->work_count; r.ent_off = ctx->work_count + 1;
+  r.entry_rows = kEntryRows;
   r.with_shared = 1;
   HIPX(launch_route(r, ctx->st));
   return DG_OK;
@@ -363,6 +365,7 @@ dg_status enqueue_experts(dg_ctx* ctx, int l, int M, const void* f) {
   g.B = ctx->L[l].gu; g.b_group_stride = 2LL * F * H;
   g.K = H; g.NB = 2 * F / 16; g.mt = kStreamMT;
   g.work = ctx->work; g.work_count = ctx->work_count; g.work_cap = work_cap(c, M);
+  g.ent_off = ctx->work_count + 1; g.n_groups = c.n_experts + 1;
   EpiArgs e{};
   e.kind = EPI_GEGLU; e.out = ctx->u; e.ldo = F;
   HIPX(launch_stream(ctx->bf16, g, e, ctx->st, prof_kernel(ctx, DG_PROF_GATE_UP)));
@@ -371,6 +374,8 @@ dg_status enqueue_experts(dg_ctx* ctx, int l, int M, const void* f) {
   d.A = ctx->u; d.lda = F; d.a_rows = nullptr;
   d.B = ctx->L[l].down; d.b_group_stride = (long long)F * H;
   d.K = F; d.NB = H / 16; d.mt = kStreamMT;
+  // down keeps the tile-major order: its A rows (u) are few, and spreading the
+  // concurrent weight reads over many experts streams faster here
   d.work = ctx->work; d.work_count = ctx->work_count; d.work_cap = work_cap(c, M);
   EpiArgs ed{};
   ed.kind = EPI_DOWN; ed.out = ctx->y; ed.ldo = H;
