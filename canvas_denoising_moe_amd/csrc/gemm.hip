@@ -88,7 +88,7 @@ template <typename T> DG_DEV void st(void* base, long long off, float v) {
 // Epilogue for one output row and lane column, WN consecutive n-blocks.
 template <typename T, int WN, int EPI>
 DG_DEV void epilogue(const EpiArgs& e, int row, int nb0, int nb_valid, int c, const float* v,
-                     long long split_off = 0) {
+                     long long split_off = 0, const float2* rope = nullptr) {
   if constexpr (EPI == EPI_STORE_F32) {
     float* out = reinterpret_cast<float*>(e.out) + split_off;
 #pragma unroll
@@ -124,7 +124,7 @@ DG_DEV void epilogue(const EpiArgs& e, int row, int nb0, int nb_valid, int c, co
         const int d = (w0 >> 1) * 16 + c;
         const int n_rot = e.is_global ? e.n_rot_global : e.n_rot_local;
         if (d < n_rot) {
-          const float2 cs = e.rope_cs[((long long)row) * (e.D >> 1) + d];
+          const float2 cs = rope ? rope[p] : e.rope_cs[((long long)row) * (e.D >> 1) + d];
           const float y1 = x1 * cs.x - x2 * cs.y;
           const float y2 = x2 * cs.x + x1 * cs.y;
           x1 = y1; x2 = y2;
@@ -397,6 +397,16 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs g, EpiArgs e) {
   const int KB = KBall / ksplit;  // k-steps of this split
   const int kbase = ks * KB;
 
+  // ---- A row indices (rows past the entry repeat its last row; those output
+  // rows are never stored, and an MFMA row depends only on its own A row).
+  // The gather index load goes out ahead of the W ring so that its wait does
+  // not also wait for the ring.
+  int ar = min(rs + tid, re - 1), a_max = 0x7fffffff;
+  if (tid < ROWS && g.a_rows) {
+    ar = g.a_rows[ar];
+    a_max = g.a_rows_max;
+  }
+
   // ---- W ring prologue
   const T* __restrict__ Bg = reinterpret_cast<const T*>(g.B) + (long long)group * g.b_group_stride;
   const int nb0 = tile * 4 * WN + wave * WN;
@@ -413,16 +423,30 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs g, EpiArgs e) {
 #pragma unroll
     for (int w = 0; w < WN; ++w) b[i][w] = ld_frag<T>(bptr[w] + (long long)min(i, KB - 1) * 512);
 
-  // ---- A row indices (rows past the entry repeat its last row; those output
-  // rows are never stored, and an MFMA row depends only on its own A row)
   if (tid < ROWS) {
-    const int row = min(rs + tid, re - 1);
-    long long ar = row;
-    if (g.a_rows) {
-      ar = g.a_rows[row];
-      ar = ar < 0 ? 0 : (ar >= g.a_rows_max ? g.a_rows_max - 1 : ar);
+    ar = ar < 0 ? 0 : (ar >= a_max ? a_max - 1 : ar);
+    s_rows[tid] = ar;
+  }
+
+  // RoPE (cos, sin) of this lane's output rows and rotary columns, fetched now
+  // so the epilogue does not wait on a load
+  constexpr int NP = EPI == EPI_QKV ? WN / 2 : 1;
+  float2 rope[MT][4][NP];
+  if constexpr (EPI == EPI_QKV) {
+    const int c = lane & 15, rg = (lane >> 4) * 4, bph = e.D >> 4;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int nb = min(nb0 + 2 * p, g.NB - 1);
+      const int hs = nb / bph, d = ((nb - hs * bph) >> 1) * 16 + c;
+      const int dd = min(d, (e.D >> 1) - 1);  // columns past the rotary half are never used
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = min(rs + m * 16 + rg + r, re - 1);
+          rope[m][r][p] = e.rope_cs[(long long)row * (e.D >> 1) + dd];
+        }
     }
-    s_rows[tid] = (int)ar;
   }
 
   floatx4 acc[MT][WN];
@@ -432,13 +456,34 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs g, EpiArgs e) {
     for (int w = 0; w < WN; ++w) acc[m][w] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   const T* __restrict__ A = reinterpret_cast<const T*>(g.A) + kbase * 32;
+  // bf16: each lane's A source row for every row tile (lane l feeds row l % 16 of
+  // the tile at k offset 8 * (l / 16) of each k-step)
+  const T* arow[MT];
+  if constexpr (sizeof(T) == 2) {
+    __syncthreads();  // row indices written
+#pragma unroll
+    for (int m = 0; m < MT; ++m) arow[m] = A + (long long)s_rows[m * 16 + (lane & 15)] * g.lda + (lane >> 4) * 8;
+  }
   for (int kc0 = 0; kc0 < KB; kc0 += KC) {
     const int nk = min(KC, KB - kc0);  // k-steps in this chunk (< KC only in the last one)
     __syncthreads();                   // row indices written / previous chunk consumed
-    {
+    if constexpr (sizeof(T) == 2) {
+      // direct global->LDS copies: one 1 KB fragment block (k-step, row tile) per
+      // wave instruction, all of the chunk in flight at once and no registers
+      // held; the wait before the barrier below covers them
+      for (int q = wave; q < nk * MT; q += 4) {
+        const int kl = q / MT, m = q - kl * MT;
+        const T* src = arow[0];
+#pragma unroll
+        for (int mm = 1; mm < MT; ++mm)
+          if (m == mm) src = arow[mm];
+        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) const void*)(src + (kc0 + kl) * 32),
+                                         (__attribute__((address_space(3))) void*)(As + q * 512), 16, 0, 0);
+      }
+    } else {
       const int k8s = nk * 4;          // 8-element groups per row within the chunk
       const int groups8 = ROWS * k8s;
-      constexpr int U = sizeof(T) == 2 ? 8 : 4;  // loads in flight, bounded by the ring's registers
+      constexpr int U = 4;  // fp32: loads in flight, bounded by the ring's registers
       for (int base = tid; base < groups8; base += 256 * U) {
         Frag<T> v[U];
 #pragma unroll
@@ -495,7 +540,7 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs g, EpiArgs e) {
           float v[WN];
 #pragma unroll
           for (int w = 0; w < WN; ++w) v[w] = acc[m][w][r];
-          epilogue<T, WN, EPI>(e, row, nb0, nbv, c, v, ks * g.split_stride);
+          epilogue<T, WN, EPI>(e, row, nb0, nbv, c, v, ks * g.split_stride, rope[m][r]);
         }
       }
   }
