@@ -36,7 +36,7 @@ METRIC = "canvas tokens/sec per denoise pass; resolved tok/s (30-layer bf16, 1 M
 # they were taken with
 COUNTERS = os.path.join(ROOT, "profiles", "moe_gate_up_C3_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "canvas_denoising_moe_amd", "csrc", f) for f in ("gemm.hip", "common.h")]
-GATE_UP_KERNEL = r"k_stream<unsigned short, \d+, \d+, 1, \d+>"   # <T, MT, WN, EPI_GEGLU, R>
+GATE_UP_KERNEL = r"k_stream<unsigned short, \d+, \d+, 1, \d+, \d+>"   # <T, MT, WN, EPI_GEGLU, R, LDS KB>
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 

@@ -321,8 +321,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g, EpiArgs e) {
 // K.  The ring's first loads go out before anything else, so the weight
 // stream is under way while A is staged.  The entry's A rows are staged into
 // LDS in MFMA A-fragment order, [k-step][row tile][64 lanes][8] (every lane
-// reads its own 16 contiguous bytes), in chunks of at most 64 KB; the ring
-// runs on across chunk boundaries (weights do not depend on A).  Loads in the
+// reads its own 16 contiguous bytes), in chunks of LK KB copied straight from
+// global memory into LDS (bf16); the ring runs on across chunk boundaries
+// (weights do not depend on A).  Loads in the
 // k loop are unconditional so the compiler's wait counts stay exact; k-steps
 // past the end use a zero A fragment and clamped refills.
 //
@@ -334,15 +335,18 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g, EpiArgs e) {
 // through its L2.  Wider entries (MT = 2) halve the weight reads of dense
 // GEMMs and of experts with more than 16 rows.
 // ----------------------------------------------------------------------------
-constexpr int kStreamLds = 32 * 1024;  // LDS budget of one A chunk
+// LDS budget of one A chunk, in KB: 32 keeps three 32-row workgroups per CU;
+// a grid of at most one workgroup per CU (the dense projections of one canvas)
+// takes 128 and stages the whole K range of its rows at once.
+constexpr int kStreamLdsKB = 32, kStreamLdsWideKB = 128;
 
-template <typename T, int MT>
-constexpr int stream_kc() { return kStreamLds / (16 * MT * 32 * (int)sizeof(T)); }  // k-steps per chunk
+template <typename T, int MT, int R, int LK>
+constexpr int stream_kc() { return (LK * 1024 / (16 * MT * 32 * (int)sizeof(T))) / R * R; }  // k-steps per chunk
 
-template <typename T, int MT, int WN, int EPI, int R>
+template <typename T, int MT, int WN, int EPI, int R, int LK>
 __global__ __launch_bounds__(256) void k_stream(StreamArgs g, EpiArgs e) {
   constexpr int ROWS = 16 * MT;
-  constexpr int KC = stream_kc<T, MT>();
+  constexpr int KC = stream_kc<T, MT, R, LK>();
   static_assert(KC % R == 0, "the register ring must tile an A chunk");
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* As = reinterpret_cast<T*>(smem_raw);  // [KC][MT][64][8]
@@ -546,38 +550,69 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs g, EpiArgs e) {
   }
 }
 
-template <typename T, int MT, int WN, int EPI, int R>
-hipError_t run_stream(const StreamArgs& g, const EpiArgs& e, hipStream_t s, KTime t) {
+// workgroups of the streaming GEMM for g, 4*WN n-blocks per tile
+template <int WN>
+long long stream_blocks(const StreamArgs& g) {
   const int tiles = (g.NB + 4 * WN - 1) / (4 * WN);
+  const int ksplit = g.ksplit > 1 ? g.ksplit : 1;
+  const long long P = (long long)tiles * (g.n_dense + g.work_cap) * ksplit;
+  return ((P + 7) >> 3) << 3;
+}
+
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+template <typename T, int MT, int WN, int EPI, int R, int LK>
+hipError_t run_stream(const StreamArgs& g, const EpiArgs& e, hipStream_t s, KTime t) {
   const int ksplit = g.ksplit > 1 ? g.ksplit : 1;
   if (((g.K >> 5) % ksplit) != 0 || (ksplit > 1 && EPI != EPI_STORE_F32)) return hipErrorInvalidValue;
   if (g.ent_off && (ksplit > 1 || g.n_dense > 0 || g.n_groups < 1)) return hipErrorInvalidValue;
-  const long long P = (long long)tiles * (g.n_dense + g.work_cap) * ksplit;
-  if (P <= 0) return hipSuccess;
-  const long long blocks = ((P + 7) >> 3) << 3;
+  const long long blocks = stream_blocks<WN>(g);
+  if (blocks <= 0) return hipSuccess;
   const int KB = (g.K >> 5) / ksplit;
-  const size_t lds = (size_t)16 * MT * min(KB, stream_kc<T, MT>()) * 32 * sizeof(T);
+  const size_t lds = (size_t)16 * MT * min(KB, stream_kc<T, MT, R, LK>()) * 32 * sizeof(T);
   static bool attr_set = false;  // one attribute call per instantiation
   if (!attr_set) {
-    // the 64 KB chunk plus the kernel's static LDS
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_stream<T, MT, WN, EPI, R>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, kStreamLds);
+    // the chunk plus the kernel's static LDS
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_stream<T, MT, WN, EPI, R, LK>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, LK * 1024);
     if (err != hipSuccess) return err;
     attr_set = true;
   }
-  return launch_k(k_stream<T, MT, WN, EPI, R>, dim3((unsigned)blocks), dim3(256), lds, s, t.start, t.stop,
+  return launch_k(k_stream<T, MT, WN, EPI, R, LK>, dim3((unsigned)blocks), dim3(256), lds, s, t.start, t.stop,
                   g, e);
+}
+
+// dense projections (q/k/v, output projection, router): the whole K range in
+// one chunk when the grid leaves at most one workgroup per CU
+template <typename T, int MT, int EPI>
+hipError_t run_stream_dense(const StreamArgs& g, const EpiArgs& e, hipStream_t s, KTime t) {
+  if constexpr (sizeof(T) == 2) {
+    if (stream_blocks<2>(g) <= device_cus()) return run_stream<T, MT, 2, EPI, 8, kStreamLdsWideKB>(g, e, s, t);
+  }
+  return run_stream<T, MT, 2, EPI, 8, kStreamLdsKB>(g, e, s, t);
 }
 
 template <typename T, int MT>
 hipError_t run_stream_mt(const StreamArgs& g, const EpiArgs& e, hipStream_t s, KTime t) {
   switch (e.kind) {
-    case EPI_STORE_F32: return run_stream<T, MT, 2, EPI_STORE_F32, 8>(g, e, s, t);
-    case EPI_GEGLU: return run_stream<T, MT, 2, EPI_GEGLU, 8>(g, e, s, t);
-    // down: K = F is short, so wider tiles (4 n-blocks per wave) halve the A
-    // re-staging at the same ring depth in bytes
-    case EPI_DOWN: return run_stream<T, MT, (MT == 2 ? 4 : 2), EPI_DOWN, (MT == 2 ? 4 : 8)>(g, e, s, t);
-    case EPI_QKV: return run_stream<T, MT, 2, EPI_QKV, 8>(g, e, s, t);
+    case EPI_STORE_F32: return run_stream_dense<T, MT, EPI_STORE_F32>(g, e, s, t);
+    case EPI_GEGLU: return run_stream<T, MT, 2, EPI_GEGLU, 8, kStreamLdsKB>(g, e, s, t);
+    // down: K = F is short; 4 n-blocks per wave halve the A re-staging, and a
+    // 2-deep ring streams fastest here (a deeper one spends its tail on
+    // clamped repeat loads)
+    case EPI_DOWN:
+      return run_stream<T, MT, (MT == 2 ? 4 : 2), EPI_DOWN, (MT == 2 ? 2 : 8), kStreamLdsKB>(g, e, s, t);
+    case EPI_QKV: return run_stream_dense<T, MT, EPI_QKV>(g, e, s, t);
   }
   return hipErrorInvalidValue;
 }
