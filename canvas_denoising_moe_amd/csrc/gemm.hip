@@ -88,16 +88,18 @@ template <typename T> DG_DEV void st(void* base, long long off, float v) {
 // Epilogue for one output row and lane column, WN consecutive n-blocks.
 template <typename T, int WN, int EPI>
 DG_DEV void epilogue(const EpiArgs& e, int row, int nb0, int nb_valid, int c, const float* v,
-                     long long split_off = 0, const float2* rope = nullptr) {
+                     long long split_off = 0, const float2* rope = nullptr, const int* down_row = nullptr,
+                     const float* down_gate = nullptr) {
   if constexpr (EPI == EPI_STORE_F32) {
     float* out = reinterpret_cast<float*>(e.out) + split_off;
 #pragma unroll
     for (int w = 0; w < WN; ++w)
       if (w < nb_valid) out[(long long)row * e.ldo + (nb0 + w) * 16 + c] = v[w];
   } else if constexpr (EPI == EPI_DOWN) {
-    const int orow = e.slot[row];
+    const int orow = down_row ? *down_row : e.slot[row];
     if ((unsigned)orow >= (unsigned)e.out_rows) return;
-    const float g = orow < e.routed_rows ? e.gates[orow] : 1.0f;  // shared-expert rows: weight 1
+    // shared-expert rows: weight 1
+    const float g = down_gate ? *down_gate : (orow < e.routed_rows ? e.gates[orow] : 1.0f);
     float* out = reinterpret_cast<float*>(e.out);
 #pragma unroll
     for (int w = 0; w < WN; ++w)
@@ -348,9 +350,12 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs g, EpiArgs e) {
   constexpr int ROWS = 16 * MT;
   constexpr int KC = stream_kc<T, MT, R, LK>();
   static_assert(KC % R == 0, "the register ring must tile an A chunk");
+  static_assert(EPI != EPI_DOWN || sizeof(T) != 2 || 4 * ROWS * 16 * WN * 4 <= LK * 1024,
+                "the down output tiles must fit the LDS budget");
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* As = reinterpret_cast<T*>(smem_raw);  // [KC][MT][64][8]
   __shared__ int s_rows[ROWS];
+  __shared__ int s_orow[EPI == EPI_DOWN ? ROWS : 1];  // down: output slot of each entry row
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tiles = (g.NB + 4 * WN - 1) / (4 * WN);
   const int ksplit = g.ksplit > 1 ? g.ksplit : 1;
@@ -410,6 +415,19 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs g, EpiArgs e) {
     ar = g.a_rows[ar];
     a_max = g.a_rows_max;
   }
+  // down: output slot of each of this lane's rows, fetched early like the
+  // gather index (its gate follows once the slot is known)
+  constexpr int DM = EPI == EPI_DOWN ? MT : 1;
+  int dslot[DM][4];
+  int orow_t = 0;
+  if constexpr (EPI == EPI_DOWN) {
+    if (tid < ROWS) orow_t = e.slot[min(rs + tid, re - 1)];
+    const int rg = (lane >> 4) * 4;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dslot[m][r] = e.slot[min(rs + m * 16 + rg + r, re - 1)];
+  }
 
   // ---- W ring prologue
   const T* __restrict__ Bg = reinterpret_cast<const T*>(g.B) + (long long)group * g.b_group_stride;
@@ -430,6 +448,18 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs g, EpiArgs e) {
   if (tid < ROWS) {
     ar = ar < 0 ? 0 : (ar >= a_max ? a_max - 1 : ar);
     s_rows[tid] = ar;
+    if constexpr (EPI == EPI_DOWN) s_orow[tid] = orow_t;
+  }
+
+  float dgate[DM][4];
+  if constexpr (EPI == EPI_DOWN) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int orow = dslot[m][r];
+        dgate[m][r] = (unsigned)orow < (unsigned)e.routed_rows ? e.gates[orow] : 1.0f;
+      }
   }
 
   // RoPE (cos, sin) of this lane's output rows and rotary columns, fetched now
@@ -533,7 +563,39 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs g, EpiArgs e) {
     }
   }
   mfma_drain();
-  if (nbv > 0) {
+  if constexpr (EPI == EPI_DOWN && sizeof(T) == 2) {
+    // down: the gate-scaled tile goes through LDS (each wave its own ROWS x
+    // 16*WN fp32 block, 16-column groups XOR-swizzled by row quad against bank
+    // conflicts) so that every lane stores 16 contiguous bytes of a row
+    constexpr int TC = 16 * WN, Q = TC / 4, RPI = 64 / Q;
+    static_assert((WN & (WN - 1)) == 0 && 64 % Q == 0 && ROWS % RPI == 0, "down tile shape");
+    float* tl = reinterpret_cast<float*>(smem_raw) + wave * ROWS * TC;
+    __syncthreads();  // every wave is done with the A chunk
+    {
+      const int c = lane & 15, rg = (lane >> 4) * 4;
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tr = m * 16 + rg + r;
+#pragma unroll
+          for (int w = 0; w < WN; ++w) tl[tr * TC + (w ^ ((tr >> 2) & (WN - 1))) * 16 + c] = acc[m][w][r] * dgate[m][r];
+        }
+    }
+    __syncthreads();
+    float* out = reinterpret_cast<float*>(e.out);
+    const int q = lane % Q;
+#pragma unroll
+    for (int i = 0; i < ROWS / RPI; ++i) {
+      const int tr = i * RPI + lane / Q;
+      const int orow = s_orow[tr];
+      if (rs + tr < re && (q >> 2) < nbv && (unsigned)orow < (unsigned)e.out_rows) {
+        const float4 val = *reinterpret_cast<const float4*>(tl + tr * TC + (((q >> 2) ^ ((tr >> 2) & (WN - 1))) * 16) +
+                                                            (q & 3) * 4);
+        *reinterpret_cast<float4*>(out + (long long)orow * e.ldo + nb0 * 16 + q * 4) = val;
+      }
+    }
+  } else if (nbv > 0) {
     const int c = lane & 15, rg = (lane >> 4) * 4;
 #pragma unroll
     for (int m = 0; m < MT; ++m)
@@ -544,7 +606,10 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs g, EpiArgs e) {
           float v[WN];
 #pragma unroll
           for (int w = 0; w < WN; ++w) v[w] = acc[m][w][r];
-          epilogue<T, WN, EPI>(e, row, nb0, nbv, c, v, ks * g.split_stride, rope[m][r]);
+          if constexpr (EPI == EPI_DOWN)
+            epilogue<T, WN, EPI>(e, row, nb0, nbv, c, v, 0, nullptr, &dslot[m][r], &dgate[m][r]);
+          else
+            epilogue<T, WN, EPI>(e, row, nb0, nbv, c, v, ks * g.split_stride, rope[m][r]);
         }
       }
   }
@@ -579,7 +644,9 @@ hipError_t run_stream(const StreamArgs& g, const EpiArgs& e, hipStream_t s, KTim
   const long long blocks = stream_blocks<WN>(g);
   if (blocks <= 0) return hipSuccess;
   const int KB = (g.K >> 5) / ksplit;
-  const size_t lds = (size_t)16 * MT * min(KB, stream_kc<T, MT, R, LK>()) * 32 * sizeof(T);
+  size_t lds = (size_t)16 * MT * min(KB, stream_kc<T, MT, R, LK>()) * 32 * sizeof(T);
+  // bf16 down: the 4 waves' fp32 output tiles reuse the A chunk's LDS
+  if (EPI == EPI_DOWN && sizeof(T) == 2) lds = max(lds, (size_t)4 * 16 * MT * 16 * WN * sizeof(float));
   static bool attr_set = false;  // one attribute call per instantiation
   if (!attr_set) {
     // the chunk plus the kernel's static LDS
