@@ -26,6 +26,10 @@ HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # no packed-fp32 VALU forms in generated device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: with the default AGPR form the LM
+    # head's 128 accumulators were shuffled between register files on every
+    # loop iteration
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-result",
 ]
 

@@ -9,9 +9,10 @@
 // 8 row tiles of 16 rows and 4 column blocks of 16 (128 fp32 accumulators per
 // lane).  The embedding (the packed B operand, 1 GB at V = 262144) streams
 // through a 4-deep register ring of fragments, 32 MFMAs per k-step per wave;
-// h rows are staged through LDS in double-buffered chunks of 8 k-steps, each
-// wave loading two k-steps of the next chunk into registers while the current
-// chunk is consumed, so no load latency sits between chunks.  Units
+// h rows are staged through LDS in double-buffered chunks of 4 k-steps, each
+// wave loading one k-step of the next chunk into registers while the current
+// chunk is consumed, so no load latency sits between chunks.  The whole state
+// fits 256 VGPRs (accumulators included), so two workgroups share a CU.  Units
 // (vocabulary tile, row group) are sliced contiguously per XCD, so the row
 // groups of one vocabulary tile run side by side on one XCD and read its
 // embedding fragments from HBM once, through that XCD's L2.
@@ -27,7 +28,7 @@ namespace {
 
 constexpr int kLmRT = 8;   // row tiles of 16 per workgroup
 constexpr int kLmRows = 16 * kLmRT;
-constexpr int kLmKC = 8;   // k-steps per staged A chunk
+constexpr int kLmKC = 4;   // k-steps per staged A chunk
 constexpr int kLmR = 4;    // W ring depth in k-steps
 constexpr int kLmKS = kLmKC / 4;  // k-steps of a chunk staged by each wave
 static_assert(kLmKC % kLmR == 0, "ring slot == k-step within the chunk mod R");
@@ -81,17 +82,18 @@ __global__ __launch_bounds__(256) void k_lm_head(LmArgs a) {
   // A staging: wave w owns k-steps w*KS .. w*KS + KS-1 of every chunk, all
   // row tiles; lane j carries row (j & 15) of a tile, k-group j >> 4 (fragment
   // order).  Rows past M repeat the last row (their results are never used).
+  // One lane pointer plus a wave-uniform offset per row tile: a tile past M
+  // repeats the last full tile (M is a multiple of 16).
   const bf16_t* __restrict__ H = reinterpret_cast<const bf16_t*>(a.h);
-  const bf16_t* hrow[kLmRT];
+  const bf16_t* hbase = H + (long long)(lane & 15) * a.K + wave * kLmKS * 32 + (lane >> 4) * 8;
+  long long hoff[kLmRT];
 #pragma unroll
-  for (int i = 0; i < kLmRT; ++i)
-    hrow[i] = H + (long long)min(rbase + i * 16 + (lane & 15), a.M - 1) * a.K + wave * kLmKS * 32 +
-              (lane >> 4) * 8;
+  for (int i = 0; i < kLmRT; ++i) hoff[i] = (long long)min(rbase + i * 16, a.M - 16) * a.K;
   v4u st[kLmKS][kLmRT];  // the next chunk's share of this wave, in flight
 #define LM_LOAD_CHUNK(c)                                                                     \
   _Pragma("unroll") for (int j = 0; j < kLmKS; ++j)                                          \
     _Pragma("unroll") for (int i = 0; i < kLmRT; ++i)                                        \
-      st[j][i] = *reinterpret_cast<const v4u*>(hrow[i] + ((c) * kLmKC + j) * 32);
+      st[j][i] = *reinterpret_cast<const v4u*>(hbase + hoff[i] + ((c) * kLmKC + j) * 32);
 #define LM_STORE_CHUNK(c)                                                                    \
   {                                                                                          \
     bf16_t* dst = As + (((c) & 1) * kLmKC + wave * kLmKS) * kLmRT * 512 + lane * 8;          \
@@ -225,7 +227,7 @@ __global__ __launch_bounds__(256) void k_lm_merge(LmArgs a) {
 }  // namespace
 
 bool lm_head_supported(int M, int K, int V) {
-  return M > 0 && K % (32 * kLmKC) == 0 && V % 16 == 0;
+  return M > 0 && M % 16 == 0 && K % (32 * kLmKC) == 0 && V % 16 == 0;
 }
 
 hipError_t launch_lm_head(const LmArgs& a, bool argmax, hipStream_t s, KTime t) {
