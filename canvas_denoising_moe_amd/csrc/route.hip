@@ -19,23 +19,39 @@
 namespace {
 
 
-DG_DEV void argmax_pair(float& v, int& e) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ov = __shfl_xor(v, o, 64);
-    const int oe = __shfl_xor(e, o, 64);
-    if (ov > v || (ov == v && oe < e)) { v = ov; e = oe; }
-  }
+// Order-preserving key of a logit: a larger logit has a larger key.  NaN
+// counts as -inf and -0 as +0, so equal keys are exactly equal logits; key 0
+// is below every logit's key.
+DG_DEV unsigned logit_key(float v) {
+  unsigned u = v != v ? __float_as_uint(-INFINITY) : __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+DG_DEV float key_logit(unsigned k) { return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k); }
+
+// Maximum of v over the wave, on every lane: an inclusive max-scan within
+// rows of 16 lanes (DPP row shifts), then across rows (row broadcasts of
+// lanes 15 and 31); lane 63 ends with the whole wave's maximum.
+DG_DEV unsigned wave_max_key(unsigned v) {
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));  // row_shr:1
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));  // row_shr:2
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));  // row_shr:4
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));  // row_shr:8
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = max(v, (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return (unsigned)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // Top-k of token t by one wave: lane l holds the logits of experts l, l + 64,
-// ... in registers (split-K partials summed in slice order), the k winners
-// come out of k wave-wide arg-max rounds; lane s < k returns slot s's expert
-// (and writes idx / gates), other lanes return -1.
+// ... in registers (split-K partials summed in slice order).  Round s takes
+// the largest key not yet taken (one wave max) and, among the experts holding
+// it, the lowest index (ballots), so the slots are in logit-descending order
+// with ties to the lower expert.  Lane s < k returns slot s's expert (and
+// writes idx / gates), other lanes return -1.
 DG_DEV int topk_token(const RouteArgs& a, int t, int lane) {
   const int E = a.E, K = a.k;
   const int parts = a.logit_parts > 0 ? a.logit_parts : 1;
-  float v[4];
+  unsigned key[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = lane + 64 * j;
@@ -47,7 +63,7 @@ DG_DEV int topk_token(const RouteArgs& a, int t, int lane) {
 #pragma unroll
     for (int q = 0; q < 8; ++q)
       if (q < parts) sum += pv[q];  // fixed order
-    v[j] = e < E ? sum : -INFINITY;
+    key[j] = e < E ? logit_key(sum) : 0u;
     if (a.r_out && e < E) a.r_out[(long long)t * E + e] = sum;
   }
   float sel_v[8];
@@ -56,17 +72,21 @@ DG_DEV int topk_token(const RouteArgs& a, int t, int lane) {
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     if (s >= K) break;
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
+    unsigned cand = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (lane + 64 * j < E && !(used & (1u << j))) cand = max(cand, key[j]);
+    const unsigned m = wave_max_key(cand);
+    int pick = 0;
+    bool found = false;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      if (e < E && !(used & (1u << j)) && (be == 0x7fffffff || v[j] > bv)) { bv = v[j]; be = e; }
+      const unsigned long long b = __ballot(lane + 64 * j < E && !(used & (1u << j)) && key[j] == m);
+      if (!found && b) { pick = 64 * j + __builtin_ctzll(b); found = true; }
     }
-    argmax_pair(bv, be);
-    if ((be & 63) == lane) used |= 1u << (be >> 6);
-    sel_v[s] = bv;
-    sel_e[s] = be;
+    if ((pick & 63) == lane) used |= 1u << (pick >> 6);
+    sel_v[s] = key_logit(m);
+    sel_e[s] = pick;
   }
   int my_e = -1;
   if (lane < K) {
