@@ -274,40 +274,47 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int QT, int xcd_m
   }
 }
 
-// o[(b*N + i), h*D + d] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, splits in order
+// o[(b*N + i), h*D + d] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, splits in order.
+// One wave per query row (4 rows per workgroup): lane s fetches split s's
+// (m, l), the wave max gives M, then every lane accumulates its D / 64
+// columns over the splits in order, 8 splits' loads in flight at a time.
 template <typename T>
-__global__ void k_attn_merge(AttnArgs a) {
+__global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
   const long long rows_all = (long long)a.B * a.Hq * a.N;
-  const long long row = blockIdx.x;
-  const int d = threadIdx.x;
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows_all) return;
   const int S = a.ns[row / ((long long)a.Hq * a.N)];
-  if (d >= a.D || S == 1) return;  // one split: stored by the attention kernel
-  constexpr int U = 8;  // splits whose loads are in flight together
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < S; s0 += U) {
-    float mv[U];
+  if (S == 1) return;  // one split: stored by the attention kernel
+  constexpr int DJ = 4;  // columns per lane (D <= 256)
+  const int D = a.D;
+  const float m_l = lane < S ? a.part_m[lane * rows_all + row] : -INFINITY;
+  const float l_l = lane < S ? a.part_l[lane * rows_all + row] : 0.f;
+  float M = m_l;
 #pragma unroll
-    for (int u = 0; u < U; ++u) mv[u] = s0 + u < S ? a.part_m[(s0 + u) * rows_all + row] : -INFINITY;
-#pragma unroll
-    for (int u = 0; u < U; ++u) M = fmaxf(M, mv[u]);
-  }
-  float num = 0.f, den = 0.f;
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  float num[DJ] = {0.f, 0.f, 0.f, 0.f}, den = 0.f;
   if (M != -INFINITY) {
+    constexpr int U = 8;
     for (int s0 = 0; s0 < S; s0 += U) {
-      float mv[U], ov[U], lv[U];
+      float ov[U][DJ];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int s = min(s0 + u, S - 1);
-        mv[u] = a.part_m[s * rows_all + row];
-        ov[u] = a.part_o[(s * rows_all + row) * a.D + d];
-        lv[u] = a.part_l[s * rows_all + row];
+        const int sp = min(s0 + u, S - 1);
+#pragma unroll
+        for (int j = 0; j < DJ; ++j) {
+          const int d = lane + 64 * j;
+          ov[u][j] = d < D ? a.part_o[(sp * rows_all + row) * D + d] : 0.f;
+        }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if (s0 + u < S) {  // splits in order
-          const float w = exp2f(mv[u] - M);
-          num += w * ov[u];
-          den += w * lv[u];
+          const float mv = __shfl(m_l, s0 + u, 64), lv = __shfl(l_l, s0 + u, 64);
+          const float w = exp2f(mv - M);
+#pragma unroll
+          for (int j = 0; j < DJ; ++j) num[j] += w * ov[u][j];
+          den += w * lv;
         }
       }
     }
@@ -315,8 +322,12 @@ __global__ void k_attn_merge(AttnArgs a) {
   const int i = (int)(row % a.N);
   const long long bh = row / a.N;
   const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
-  T* o = reinterpret_cast<T*>(a.o);
-  o[((long long)b * a.N + i) * a.Hq * a.D + (long long)h * a.D + d] = from_f<T>(den > 0.f ? num / den : 0.f);
+  T* o = reinterpret_cast<T*>(a.o) + ((long long)b * a.N + i) * a.Hq * D + (long long)h * D;
+#pragma unroll
+  for (int j = 0; j < DJ; ++j) {
+    const int d = lane + 64 * j;
+    if (d < D) o[d] = from_f<T>(den > 0.f ? num[j] / den : 0.f);
+  }
 }
 
 // One query row per workgroup; generic in T and D (<= 256).
@@ -434,7 +445,7 @@ hipError_t launch_attention(int is_bf16, const AttnArgs& a0, hipStream_t st, KTi
       e = aligned ? launch_k(k_attn_mfma<64, true>, grid, dim3(256), 0, st, t.start, stop1, a, QT, xcd_map)
                   : launch_k(k_attn_mfma<64, false>, grid, dim3(256), 0, st, t.start, stop1, a, QT, xcd_map);
     if (e != hipSuccess || smax == 1) return e;
-    return launch_k(k_attn_merge<bf16_t>, dim3((unsigned)rows_all), dim3(a.D), 0, st, nullptr, t.stop, a);
+    return launch_k(k_attn_merge<bf16_t>, dim3((unsigned)((rows_all + 3) / 4)), dim3(256), 0, st, nullptr, t.stop, a);
   }
   if (a0.D > 256) return hipErrorInvalidValue;
   if (is_bf16)
