@@ -196,14 +196,11 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int QT, int xcd_m
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bf16_t p = f2bf(exp2f(sacc[kb][r] - mref));
-        ls += bf2f(p);
-        const int j = (kb & 1) * 4 + r;
-        if (j & 1)
-          pk[kb >> 1][j >> 1] |= ((uint32_t)p) << 16;
-        else
-          pk[kb >> 1][j >> 1] = p;
+      for (int q = 0; q < 2; ++q) {  // slots j = (kb & 1) * 4 + 2q, 2q + 1 share one word
+        const uint32_t w = f2bf2(exp2f(sacc[kb][2 * q] - mref), exp2f(sacc[kb][2 * q + 1] - mref));
+        ls += __uint_as_float(w << 16);
+        ls += __uint_as_float(w & 0xffff0000u);
+        pk[kb >> 1][(kb & 1) * 2 + q] = w;
       }
     ls += __shfl_xor(ls, 16, 64);
     ls += __shfl_xor(ls, 32, 64);

@@ -13,11 +13,13 @@ typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
 
 DG_DEV float bf2f(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
-// float -> bf16, round to nearest even (finite inputs)
-DG_DEV bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+// float -> bf16, round to nearest even (the hardware conversion)
+DG_DEV bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+// two floats -> packed bf16 pair (lo in bits 0..15), one conversion instruction
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef float floatx2_v __attribute__((ext_vector_type(2)));
+DG_DEV uint32_t f2bf2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2_v){lo, hi}, bf16x2_v));
 }
 
 template <typename T> DG_DEV float to_f(T v);
