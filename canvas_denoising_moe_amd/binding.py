@@ -57,6 +57,8 @@ _SIGS = {
     "dg_load_prompt_kv": (c_int32, [c_void_p, c_int32, c_int32, POINTER(c_void_p), POINTER(c_void_p)]),
     "dg_denoise_step": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, POINTER(c_int32), c_void_p, c_void_p]),
     "dg_generate_block": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
+    "dg_commit_block": (c_int32, [c_void_p, c_int32, c_void_p]),
+    "dg_get_prompt_kv": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
     "dg_forward_hidden": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p]),
     "dg_forward_layers": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
     "dg_set_trace": (c_int32, [c_void_p, c_void_p]),
@@ -236,6 +238,22 @@ class Context:
         import torch
         self._c(lib().dg_generate_block(self._h, tokens.shape[0], n_steps, _ptr(tokens, torch.int32, "tokens"),
                                         _ptr(locked, torch.uint8, "locked")))
+
+    def commit_block(self, tokens):
+        """Commit the canvases ``tokens [batch, N]`` (int32, device) to the
+        prompt KV caches (dg_commit_block): every slot's prompt_len grows by N."""
+        import torch
+        self._c(lib().dg_commit_block(self._h, tokens.shape[0], _ptr(tokens, torch.int32, "tokens")))
+
+    def prompt_kv_len(self, slot: int, layer: int) -> int:
+        n = c_int32()
+        self._c(lib().dg_get_prompt_kv(self._h, slot, layer, None, None, ctypes.byref(n)))
+        return n.value
+
+    def get_prompt_kv(self, slot: int, layer: int, k, v):
+        """Copy the slot's cache of one layer into ``k, v [len, Hkv, D]``."""
+        self._c(lib().dg_get_prompt_kv(self._h, slot, layer, _ptr(k, self.wdtype, "k"),
+                                       _ptr(v, self.wdtype, "v"), None))
 
     def forward_hidden(self, x_in, x_out):
         import torch

@@ -1,7 +1,10 @@
 // canvas_attn: every canvas query attends, in one softmax, to the cached
 // prompt keys visible to its layer and to every canvas key -- bidirectional,
 // no causal mask ([4xFaster] "DiffusionGemma's Technical Architecture"; GQA
-// and the local/global split: [HandsOn] "Detailed Specs").
+// and the local/global split: [HandsOn] "Detailed Specs").  With `causal`
+// set, canvas query i sees canvas keys j <= i only: the causal context
+// building of a resolved block before the next one ([HandsOn] "How Is This
+// Different from Previous Models?", Figure 3).
 //
 // bf16 path (k_attn_mfma): flash-style with 16x16x32 bf16 MFMAs.
 //   * Work unit = (canvas b, KV head g, key split s) x q-tile of 64 query rows.
@@ -180,7 +183,8 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int QT, int xcd_m
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int key = t0 + kb * 16 + lg * 4 + r;
-        const float sv = key < k1 ? sacc[kb][r] * sc : -INFINITY;
+        const bool vis = key < k1 && !(a.causal && key - Lw > qi);  // canvas key after the query
+        const float sv = vis ? sacc[kb][r] * sc : -INFINITY;
         sacc[kb][r] = sv;
         mx = fmaxf(mx, sv);
       }
@@ -354,7 +358,7 @@ __global__ __launch_bounds__(256) void k_attn_simple(AttnArgs a) {
   for (int c0 = 0; c0 < total; c0 += 256) {
     const int key = c0 + tid;
     float sv = -INFINITY;
-    if (key < total) {
+    if (key < total && !(a.causal && key - Lw > i)) {  // a canvas key after the query is masked
       const T* kr = key < Lw ? kp + (long long)key * D : kc + (long long)(key - Lw) * D;
       float acc = 0.f;
       for (int d = 0; d < D; ++d) acc += qs[d] * to_f<T>(kr[d]);

@@ -151,6 +151,7 @@ struct AttnArgs {
   const void* kc;         // canvas K [B][Hkv][N][D]
   const void* vc;         // canvas V^T [B][Hkv][D][N]
   int B, N, Hq, Hkv, D, canvas_keys;
+  int causal;             // canvas key j is visible to canvas query i only when j <= i
   void* o;                // [B*N][Hq*D]
   float* part_o; float* part_m; float* part_l;  // split partials
   long long part_cap_rows;  // capacity of the partial buffers in (split, row) pairs
@@ -221,6 +222,12 @@ hipError_t launch_lock_select(int B, int N, const float* conf, const int32_t* pr
 // Layout helpers.
 hipError_t launch_kv_repack(int is_bf16, const void* src, int L, int Hkv, int D, void* k_dst,
                             int transpose, hipStream_t s);
+// K [Hkv][new_len][D] / V^T [Hkv][D][new_len] of one layer after appending a
+// block of N positions (k [Hkv][N][D], v^T [Hkv][D][N]) to the old cache;
+// positions are absolute, the new range a suffix of [old ; block] (layout.hip)
+hipError_t launch_kv_append(int is_bf16, const void* kold, const void* vold, int old_len, long long old_first,
+                            const void* kblk, const void* vblk, int N, long long blk_first, int new_len,
+                            long long first, int Hkv, int D, void* knew, void* vnew, hipStream_t s);
 // generic 4-d permute copy: dst[(i0,i1,i2,i3) strides ds] = src[(i0,i1,i2,i3) strides ss]
 hipError_t launch_permute4(int is_bf16, const void* src, void* dst, const int* dims,
                            const long long* ss, const long long* ds, hipStream_t s);

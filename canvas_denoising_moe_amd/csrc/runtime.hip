@@ -31,6 +31,10 @@ struct SlotKV {
   std::vector<void*> k, v;       // per layer: K [Hkv][len][D], V^T [Hkv][D][len]
   std::vector<long long> cap;    // allocated positions per layer
   std::vector<int> len;
+  // per layer: the buffers a block commit writes the grown cache into (then
+  // swapped with k / v)
+  std::vector<void*> k2, v2;
+  std::vector<long long> cap2;
 };
 
 }  // namespace
@@ -311,12 +315,13 @@ dg_status enqueue_qkv(dg_ctx* ctx, int l, int B, const void* a, void* q, void* k
   return DG_OK;
 }
 
-dg_status enqueue_attention(dg_ctx* ctx, int l, int B, void* o, int canvas_keys) {
+dg_status enqueue_attention(dg_ctx* ctx, int l, int B, void* o, int canvas_keys, int causal = 0) {
   const dg_config& c = ctx->c;
   AttnArgs aa{};
   aa.q = ctx->q; aa.kc = ctx->kc; aa.vc = ctx->vc;
   aa.B = B; aa.N = c.canvas_len; aa.Hq = c.n_heads; aa.Hkv = c.n_kv_heads; aa.D = c.head_dim;
   aa.canvas_keys = canvas_keys;
+  aa.causal = causal;
   aa.o = o;
   aa.part_o = ctx->part_o; aa.part_m = ctx->part_m; aa.part_l = ctx->part_l;
   aa.part_cap_rows = ctx->part_cap;
@@ -407,10 +412,62 @@ dg_status enqueue_dense(dg_ctx* ctx, const void* A, int lda, const void* Bp, int
   return DG_OK;
 }
 
+// Appends the canvas K/V of layer l (ctx->kc / ctx->vc, canvas b) to slot b's
+// cache of that layer: the grown visible range goes into the spare buffers,
+// which then become the cache (stream order keeps the layer's attention on
+// the old ones).  The slot's prompt_len moves on after the last layer.
+dg_status append_block_kv(dg_ctx* ctx, int l, int b) {
+  const dg_config& c = ctx->c;
+  SlotKV& S = ctx->slots[b];
+  const int N = c.canvas_len, Hkv = c.n_kv_heads, D = c.head_dim;
+  const int old_len = S.len[l], new_len = kv_len(c, l, S.prompt_len + N);
+  if (S.k2.empty()) {
+    S.k2.assign(c.n_layers, nullptr);
+    S.v2.assign(c.n_layers, nullptr);
+    S.cap2.assign(c.n_layers, 0);
+  }
+  if (S.cap2[l] < new_len) {
+    const long long cap = kv_len(c, l, c.max_prompt_len);
+    HIPX(hipStreamSynchronize(ctx->st));
+    dfree(ctx, S.k2[l]);
+    dfree(ctx, S.v2[l]);
+    S.k2[l] = S.v2[l] = nullptr;
+    S.cap2[l] = 0;
+    TRY(dalloc(ctx, &S.k2[l], (size_t)(cap * Hkv * D) * ctx->es));
+    TRY(dalloc(ctx, &S.v2[l], (size_t)(cap * Hkv * D) * ctx->es));
+    S.cap2[l] = cap;
+  }
+  const long long blk_first = S.prompt_len, old_first = blk_first - old_len;
+  const long long first = blk_first + N - new_len;
+  const size_t kb = (size_t)b * Hkv * N * D;  // canvas b in the canvas K / V^T buffers
+  HIPX(launch_kv_append(ctx->bf16, S.k[l], S.v[l], old_len, old_first,
+                        static_cast<char*>(ctx->kc) + kb * ctx->es, static_cast<char*>(ctx->vc) + kb * ctx->es, N,
+                        blk_first, new_len, first, Hkv, D, S.k2[l], S.v2[l], ctx->st));
+  std::swap(S.k[l], S.k2[l]);
+  std::swap(S.v[l], S.v2[l]);
+  std::swap(S.cap[l], S.cap2[l]);
+  S.len[l] = new_len;
+  if (S.cap2[l] < S.cap[l]) {
+    // the spare is the buffer the cache was loaded into: give it the full
+    // capacity now, so later commits only enqueue work
+    HIPX(hipStreamSynchronize(ctx->st));
+    dfree(ctx, S.k2[l]);
+    dfree(ctx, S.v2[l]);
+    S.k2[l] = S.v2[l] = nullptr;
+    S.cap2[l] = 0;
+    TRY(dalloc(ctx, &S.k2[l], (size_t)(S.cap[l] * Hkv * D) * ctx->es));
+    TRY(dalloc(ctx, &S.v2[l], (size_t)(S.cap[l] * Hkv * D) * ctx->es));
+    S.cap2[l] = S.cap[l];
+  }
+  return DG_OK;
+}
+
 // Decoder layers on ctx->x, with ctx->a holding the normalised input of the
 // first layer.  The last layer leaves RMSNorm(x)(1 + w_last_out) in ctx->a when
-// w_last_out is given (the final norm before the LM head).
-dg_status enqueue_layers(dg_ctx* ctx, int B, const void* w_last_out, int l0 = 0, int l1 = -1) {
+// w_last_out is given (the final norm before the LM head).  commit: causal
+// canvas attention, each layer's canvas K/V appended to the caches right after
+// its attention, and nothing after the last layer's attention.
+dg_status enqueue_layers(dg_ctx* ctx, int B, const void* w_last_out, int l0 = 0, int l1 = -1, bool commit = false) {
   const dg_config& c = ctx->c;
   if (l1 < 0) l1 = c.n_layers;
   const int N = c.canvas_len, M = B * N, H = c.hidden, D = c.head_dim;
@@ -421,7 +478,11 @@ dg_status enqueue_layers(dg_ctx* ctx, int B, const void* w_last_out, int l0 = 0,
   for (int l = l0; l < l1; ++l) {
     const LayerW& W = ctx->L[l];
     TRY(enqueue_qkv(ctx, l, B, ctx->a, ctx->q, ctx->kc, ctx->vc, qs, ks, vs));
-    TRY(enqueue_attention(ctx, l, B, ctx->o, 1));
+    TRY(enqueue_attention(ctx, l, B, ctx->o, 1, commit ? 1 : 0));
+    if (commit) {
+      for (int b = 0; b < B; ++b) TRY(append_block_kv(ctx, l, b));
+      if (l + 1 == l1) break;  // later layers' inputs are not needed
+    }
     TRY(enqueue_dense(ctx, ctx->o, Hq * D, W.wo, Hq * D, H, M, ctx->ao, H));
     // x += RMSNorm(o Wo)(1 + w_pa); f = RMSNorm(x)(1 + w_pf)
     NormArgs na{};
@@ -674,6 +735,58 @@ dg_status dg_denoise_step(dg_ctx* ctx, int32_t batch, int32_t* tokens, uint8_t* 
   const size_t M = (size_t)batch * c.canvas_len;
   if (conf_out) HIPX(hipMemcpyAsync(conf_out, ctx->conf, M * 4, hipMemcpyDeviceToDevice, ctx->st));
   if (pred_out) HIPX(hipMemcpyAsync(pred_out, ctx->pred, M * 4, hipMemcpyDeviceToDevice, ctx->st));
+  return DG_OK;
+}
+
+dg_status dg_commit_block(dg_ctx* ctx, int32_t batch, const int32_t* tokens) {
+  TRY(enter(ctx));
+  const dg_config& c = ctx->c;
+  if (!c.has_lm_head || !ctx->embed_set) return fail(ctx, DG_ESTATE, "the embedding is not loaded");
+  if (batch < 1 || batch > c.max_batch) return fail(ctx, DG_EINVAL, "batch %d outside [1, %d]", batch, c.max_batch);
+  if (!tokens) return fail(ctx, DG_EINVAL, "tokens is required");
+  if (!weights_ready(ctx)) return fail(ctx, DG_ESTATE, "weights are not loaded");
+  TRY(check_slots(ctx, batch));
+  const int N = c.canvas_len, M = batch * N, H = c.hidden;
+  for (int b = 0; b < batch; ++b)
+    if (ctx->slots[b].prompt_len + N > c.max_prompt_len)
+      return fail(ctx, DG_EINVAL, "slot %d: prompt_len %d + %d exceeds max_prompt_len %d", b,
+                  ctx->slots[b].prompt_len, N, c.max_prompt_len);
+  // the block at positions prompt_len + i, causal within the block
+  HIPX(launch_embed(ctx->bf16, tokens, M, H, c.vocab, ctx->embed, ctx->x, ctx->st));
+  NormArgs n0{};
+  n0.mode = 2; n0.rows = M; n0.H = H; n0.k = c.top_k; n0.eps = c.rms_eps;
+  n0.x = ctx->x; n0.w_out = ctx->L[0].norm[0]; n0.out = ctx->a;
+  HIPX(launch_residual_norm(ctx->bf16, n0, ctx->st));
+  TRY(enqueue_layers(ctx, batch, nullptr, 0, c.n_layers, true));
+  const int D = c.head_dim;
+  for (int b = 0; b < batch; ++b) {
+    SlotKV& S = ctx->slots[b];
+    S.prompt_len += N;
+    HIPX(launch_rope_table(ctx->rope + (size_t)b * N * (D / 2), N, D, S.prompt_len, (double)c.rope_theta, ctx->st));
+  }
+  return DG_OK;
+}
+
+dg_status dg_get_prompt_kv(dg_ctx* ctx, int32_t slot, int32_t layer, void* k, void* v, int32_t* len_out) {
+  TRY(enter(ctx));
+  const dg_config& c = ctx->c;
+  if (slot < 0 || slot >= c.max_batch) return fail(ctx, DG_EINVAL, "slot %d out of range", slot);
+  if (layer < 0 || layer >= c.n_layers) return fail(ctx, DG_EINVAL, "layer %d out of range", layer);
+  const SlotKV& S = ctx->slots[slot];
+  if (S.prompt_len < 0) return fail(ctx, DG_ESTATE, "prompt KV of slot %d is not loaded", slot);
+  const int len = S.len[layer], Hkv = c.n_kv_heads, D = c.head_dim;
+  if (len_out) *len_out = len;
+  if (len == 0 || (!k && !v)) return DG_OK;
+  const int n[4] = {Hkv, len, D, 1};
+  if (k) {  // K [Hkv][len][D] -> [len][Hkv][D]
+    const long long ss[4] = {(long long)len * D, D, 1, 0}, ds[4] = {D, (long long)Hkv * D, 1, 0};
+    HIPX(launch_permute4(ctx->bf16, S.k[layer], k, n, ss, ds, ctx->st));
+  }
+  if (v) {  // V^T [Hkv][D][len] -> [len][Hkv][D]
+    const int nv[4] = {Hkv, D, len, 1};
+    const long long ss[4] = {(long long)D * len, len, 1, 0}, ds[4] = {D, 1, (long long)Hkv * D, 0};
+    HIPX(launch_permute4(ctx->bf16, S.v[layer], v, nv, ss, ds, ctx->st));
+  }
   return DG_OK;
 }
 

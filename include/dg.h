@@ -160,6 +160,31 @@ dg_status dg_denoise_step(dg_ctx* ctx, int32_t batch, int32_t* tokens, uint8_t* 
 dg_status dg_generate_block(dg_ctx* ctx, int32_t batch, int32_t n_steps, int32_t* tokens,
                             uint8_t* locked);
 
+/* Block continuation: commits the resolved canvases (or N prompt tokens) to
+ * the prompt KV cache.  The decoder stack runs once over tokens at positions
+ * prompt_len + i with causal attention inside the block (position i sees the
+ * cached context and block positions <= i), the causal context building of a
+ * finished block before the next one ([HandsOn] "How Is This Different from
+ * Previous Models?", Figure 3).  After each layer's attention the block's
+ * K (after RoPE) and V are appended to that layer's cache (sliding-window
+ * layers keep the last `window` positions), and every slot's prompt_len grows
+ * by N, so the next canvas sits at positions prompt_len + N + i.  Starting
+ * from an empty cache (dg_load_prompt_kv with prompt_len 0), successive
+ * commits of N prompt tokens build the prompt KV from token ids.
+ *   tokens  int32 [batch, N] device, ids in [0, V)
+ * Requires the embedding, all weights, the prompt KV of slots 0..batch-1 and
+ * prompt_len + N <= max_prompt_len for each (DG_EINVAL otherwise, nothing
+ * enqueued).  The first commit of a slot allocates the buffers its grown
+ * caches move between (synchronising the stream); later commits only enqueue
+ * work. */
+dg_status dg_commit_block(dg_ctx* ctx, int32_t batch, const int32_t* tokens);
+
+/* Test export: the prompt KV cache of one slot and layer as
+ * [len, Hkv, D] (k after RoPE, v) into caller buffers k, v (device, the
+ * context's element type, either may be NULL); *len_out (host, may be NULL)
+ * receives len, the positions visible to that layer. */
+dg_status dg_get_prompt_kv(dg_ctx* ctx, int32_t slot, int32_t layer, void* k, void* v, int32_t* len_out);
+
 /* Decoder layers only on a given residual stream: x_in, x_out float
  * [batch*N, H] device (may alias).  Prompt KV of slots 0..batch-1 required. */
 dg_status dg_forward_hidden(dg_ctx* ctx, int32_t batch, const float* x_in, float* x_out);

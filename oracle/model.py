@@ -89,13 +89,16 @@ def rope(x: np.ndarray, pos: np.ndarray, theta: float, n_rot: int) -> np.ndarray
 
 
 def softmax_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
-                      return_probs: bool = False):
-    """One head of non-causal scaled dot-product attention.
+                      return_probs: bool = False, mask: Optional[np.ndarray] = None):
+    """One head of scaled dot-product attention.
 
-    ``q [nq, D]``, ``k [nk, D]``, ``v [nk, D]``.  Every query sees every key:
-    no causal mask ([4xFaster] "What is Diffusion...": every token of the
-    block can access all other tokens)."""
+    ``q [nq, D]``, ``k [nk, D]``, ``v [nk, D]``.  Without ``mask`` every query
+    sees every key: no causal mask ([4xFaster] "What is Diffusion...": every
+    token of the block can access all other tokens).  ``mask [nq, nk]``
+    (True = visible) hides keys from queries."""
     s = (q @ k.T) * scale
+    if mask is not None:
+        s = np.where(mask, s, -np.inf)
     s = s - s.max(axis=1, keepdims=True)
     p = np.exp(s)
     p = p / p.sum(axis=1, keepdims=True)
@@ -103,7 +106,8 @@ def softmax_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     return (o, p) if return_probs else o
 
 
-def attention_heads(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+def attention_heads(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                    mask: Optional[np.ndarray] = None) -> np.ndarray:
     """Grouped-query attention over all heads.
 
     ``q [nq, Hq, D]``; ``k, v [nk, Hkv, D]``.  Query head ``h`` reads KV head
@@ -116,7 +120,7 @@ def attention_heads(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
     scale = 1.0 / math.sqrt(D)
     for h in range(Hq):
         g = h // group
-        out[:, h, :] = softmax_attention(q[:, h, :], k[:, g, :], v[:, g, :], scale)
+        out[:, h, :] = softmax_attention(q[:, h, :], k[:, g, :], v[:, g, :], scale, mask=mask)
     return out
 
 
@@ -396,13 +400,18 @@ def qkv_rope(a: np.ndarray, lw: Dict[str, np.ndarray], cfg, layer: int,
 
 def canvas_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                      prompt_kv: Sequence[Tuple[np.ndarray, np.ndarray]],
-                     rnd: Callable[[np.ndarray], np.ndarray], canvas_keys: bool = True) -> np.ndarray:
+                     rnd: Callable[[np.ndarray], np.ndarray], canvas_keys: bool = True,
+                     causal: bool = False) -> np.ndarray:
     """One softmax per canvas query over the keys [prompt KV ; all canvas
     positions]: the canvas attends to itself bidirectionally and to the
     cached prompt context ([4xFaster] "DiffusionGemma's Technical
     Architecture").  ``q [B, N, Hq, D]``; ``k, v [B, N, Hkv, D]``;
     ``prompt_kv[b] = (K, V)`` each ``[len, Hkv, D]``.  Returns ``o [B*N, Hq*D]``
-    rounded to the storage format."""
+    rounded to the storage format.
+
+    ``causal``: canvas position i sees the prompt keys and canvas keys j <= i
+    only -- the causal context building over a finished block ([HandsOn] "How
+    Is This Different from Previous Models?", Figure 3)."""
     B, N, Hq, D = q.shape
     o = np.empty((B * N, Hq * D))
     for b in range(B):
@@ -412,7 +421,13 @@ def canvas_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
             vals = np.concatenate([Vp, v[b]], axis=0)
         else:
             keys, vals = Kp, Vp
-        o[b * N:(b + 1) * N] = rnd(attention_heads(q[b], keys, vals)).reshape(N, Hq * D)
+        mask = None
+        if causal and canvas_keys:
+            Lp = Kp.shape[0]
+            i = np.arange(N)[:, None]
+            j = np.arange(Lp + N)[None, :]
+            mask = (j < Lp) | (j - Lp <= i)
+        o[b * N:(b + 1) * N] = rnd(attention_heads(q[b], keys, vals, mask)).reshape(N, Hq * D)
     return o
 
 
@@ -420,7 +435,7 @@ def layer_forward(x: np.ndarray, lw: Dict[str, np.ndarray], cfg, layer: int,
                   prompt_kv: Sequence[Tuple[np.ndarray, np.ndarray]],
                   prompt_lens: Sequence[int], rnd: Callable[[np.ndarray], np.ndarray],
                   route_override: Optional[Callable] = None,
-                  canvas_keys: bool = True) -> Tuple[np.ndarray, dict]:
+                  canvas_keys: bool = True, causal: bool = False) -> Tuple[np.ndarray, dict]:
     """One decoder layer over every canvas position at once.
 
     ``x [B*N, H]`` residual stream; ``prompt_kv[b] = (K, V)``, each
@@ -440,11 +455,14 @@ def layer_forward(x: np.ndarray, lw: Dict[str, np.ndarray], cfg, layer: int,
       5. f = RMSNorm(x) (pre_feedforward_layernorm);
       6. m = routed top-k MoE + shared expert;
       7. x += RMSNorm(m) (post-FFN norm; plain x += m when disabled).
+
+    ``causal`` masks later canvas keys (block commit).  The returned info
+    carries the canvas ``k, v [B, N, Hkv, D]`` as stored (after RoPE).
     """
     eps = cfg.rms_eps
     a = rnd(rmsnorm(x, lw["norm_in"], eps))
     q, k, v = qkv_rope(a, lw, cfg, layer, prompt_lens, rnd)
-    o = canvas_attention(q, k, v, prompt_kv, rnd, canvas_keys)
+    o = canvas_attention(q, k, v, prompt_kv, rnd, canvas_keys, causal)
     x = x + rmsnorm(o @ lw["wo"], lw["norm_pa"], eps)
     f = rnd(rmsnorm(x, lw["norm_pf"], eps))
     m, r, idx, gates = moe_block(f, lw, cfg.top_k, rnd, route_override)
@@ -452,7 +470,7 @@ def layer_forward(x: np.ndarray, lw: Dict[str, np.ndarray], cfg, layer: int,
         x = x + rmsnorm(m, lw["norm_pf2"], eps)
     else:
         x = x + m
-    return x, {"router_logits": r, "route_idx": idx, "gates": gates}
+    return x, {"router_logits": r, "route_idx": idx, "gates": gates, "k": k, "v": v}
 
 
 def _rounder(cfg):
@@ -555,3 +573,46 @@ def generate_block(tokens: np.ndarray, locked: np.ndarray, n_steps: int,
         if history is not None:
             history.append((tokens.copy(), locked.copy(), pred, conf))
     return tokens, locked
+
+
+# --------------------------------------------------------------------------
+# block continuation
+# --------------------------------------------------------------------------
+
+
+def commit_block(tokens: np.ndarray, weights: OracleWeights, cfg, prompt_kv_fn,
+                 prompt_lens: Sequence[int], shadow: Optional[Shadow] = None,
+                 trace: Optional[list] = None):
+    """K/V of a finished block, to be appended to the prompt cache.
+
+    After a block is resolved the model builds the context for the next
+    canvas the way a causal model would ([HandsOn] "How Is This Different from
+    Previous Models?", Figure 3): the decoder stack runs once over the block's
+    tokens at positions ``prompt_len + i`` with the cached context visible and
+    causal attention inside the block.  Returns, per layer, the block's
+    ``(k, v)``, each ``[B, N, Hkv, D]`` as stored (k after RoPE)."""
+    B, N = tokens.shape
+    rnd = _rounder(cfg)
+    x = weights.embed_rows(tokens.reshape(-1).astype(np.int64)).copy()
+    out = []
+    for l in range(cfg.n_layers):
+        kv = [prompt_kv_fn(l, b) for b in range(B)]
+        # layers whose GPU routing record is None keep the oracle's own routing
+        shadowed = shadow is not None and shadow.route_idx is not None and shadow.route_idx[l] is not None
+        ov = _shadow_route(shadow, l) if shadowed else None
+        x, info = layer_forward(x, weights.layer(l), cfg, l, kv, prompt_lens, rnd, ov, causal=True)
+        if trace is not None:
+            trace.append(info)
+        out.append((info["k"], info["v"]))
+    return out
+
+
+def append_kv(K_old: np.ndarray, V_old: np.ndarray, k_blk: np.ndarray, v_blk: np.ndarray,
+              visible: int) -> Tuple[np.ndarray, np.ndarray]:
+    """A layer's cache after a block: ``[old ; block]`` along positions
+    (``[len, Hkv, D]``), of which the last ``visible`` positions stay (all of
+    them on global layers, the last ``window`` on sliding-window layers,
+    [HandsOn] "Detailed Specs")."""
+    K = np.concatenate([K_old, k_blk], axis=0)
+    V = np.concatenate([V_old, v_blk], axis=0)
+    return K[K.shape[0] - visible:], V[V.shape[0] - visible:]
