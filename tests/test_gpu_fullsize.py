@@ -43,9 +43,9 @@ def dg():
     return _dg
 
 
-def _context(dg, w):
+def _context(dg, w, extra_positions=0):
     say("load", w.name)
-    ctx = dg.Context(w.model, max_batch=w.batch, max_prompt_len=w.prompt_len)
+    ctx = dg.Context(w.model, max_batch=w.batch, max_prompt_len=w.prompt_len + extra_positions)
     upload.load_context(ctx, w)
     return ctx
 
@@ -85,7 +85,8 @@ def _check_schedule(w, tok0, lk0, passes):
 
 @pytest.fixture(scope="module")
 def c3ctx(torch, dg):
-    ctx = _context(dg, C3)
+    # room for one block commit (the last test on this context)
+    ctx = _context(dg, C3, extra_positions=C3.model.canvas_len)
     yield ctx
     ctx.close()
     torch.cuda.empty_cache()
@@ -238,6 +239,55 @@ def test_c3_moe_sampled_tokens(torch, c3ctx):
 
 
 # ------------------------------------------ 256 canvas, 131072 prompt ----
+
+def test_c3_block_commit_sampled_layers(torch, c3ctx):
+    # block continuation at full size, last on this context (it grows the
+    # caches): the copied part of each cache is bit-exact, the block's K/V
+    # meet the one-layer tolerance on layer 0 and the stack's end-to-end
+    # tolerance deeper in
+    w = C3
+    m = w.model
+    N, L = m.canvas_len, m.n_layers
+    tok0, _ = gen.canvas(w)
+    layers = [0, 5, 11, 29]
+    before = {}
+    for l in layers:
+        n = c3ctx.prompt_kv_len(0, l)
+        k = torch.empty((n, m.n_kv_heads, m.head_dim), dtype=torch.bfloat16, device="cuda")
+        v = torch.empty_like(k)
+        c3ctx.get_prompt_kv(0, l, k, v)
+        before[l] = (host64(k), host64(v))
+    trace = torch.zeros((L, N, m.top_k), dtype=torch.int32, device="cuda")
+    c3ctx.set_trace(trace)
+    say("C3 block commit")
+    c3ctx.commit_block(torch.from_numpy(tok0).cuda())
+    torch.cuda.synchronize()
+    c3ctx.set_trace(None)
+    tr = trace.cpu().numpy()
+    tol = _stack_tolerance()
+    W = _oracle_weights(w, cache_layers=True)
+    kvf = prompt_kv_fn(w)
+    sh = om.Shadow(route_idx=[tr[l] for l in range(L - 1)] + [None], delta_route=tol)
+    blk = om.commit_block(tok0, W, m, kvf, [w.prompt_len], shadow=sh)
+    assert not sh.failures, sh.failures[:5]
+    print(f"C3 commit: routing adopted {sh.adopted}, max margin {sh.max_margin}")
+    for l in layers:
+        vis = w.prompt_len + N if m.is_global(l) else min(w.prompt_len + N, m.window)
+        n = c3ctx.prompt_kv_len(0, l)
+        assert n == vis, (l, n, vis)
+        k = torch.empty((n, m.n_kv_heads, m.head_dim), dtype=torch.bfloat16, device="cuda")
+        v = torch.empty_like(k)
+        c3ctx.get_prompt_kv(0, l, k, v)
+        torch.cuda.synchronize()
+        gk, gv = host64(k), host64(v)
+        old = vis - N
+        bk, bv = before[l]
+        assert np.array_equal(gk[:old], bk[len(bk) - old:]) and np.array_equal(gv[:old], bv[len(bv) - old:]), l
+        ek, ev = rel_err(gk[old:], blk[l][0][0]), rel_err(gv[old:], blk[l][1][0])
+        lim = TOL["bf16"] if l == 0 else tol
+        print(f"C3 commit layer {l}: len {vis}, block K rel err {ek:.3e}, V {ev:.3e} (tolerance {lim:.3e})")
+        assert ek <= lim and ev <= lim, (l, ek, ev)
+
 
 def test_c4_long_prompt_attention_and_schedule(torch, dg):
     w = C4
