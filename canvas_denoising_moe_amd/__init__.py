@@ -9,5 +9,6 @@ marshals torch tensors (device memory, streams) into the C ABI.
 """
 from .binding import (  # noqa: F401
     DG_BF16, DG_EHIP, DG_EINVAL, DG_ENOMEM, DG_ESTATE, DG_EUNSUPPORTED, DG_F32, DG_OK, LIB_PATH,
-    Context, DGError, exported_symbols, k_argmax_conf, k_lock_select, k_moe_route, lib, make_config,
+    Context, DGError, exported_symbols, k_argmax_conf, k_eb_noise, k_eb_rows, k_eb_select, k_lock_select,
+    k_moe_route, lib, make_config,
 )

@@ -58,6 +58,10 @@ _SIGS = {
     "dg_denoise_step": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, POINTER(c_int32), c_void_p, c_void_p]),
     "dg_generate_block": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
     "dg_commit_block": (c_int32, [c_void_p, c_int32, c_void_p]),
+    "dg_eb_step": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_int32, POINTER(ctypes.c_uint32),
+                             ctypes.c_uint32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "dg_generate_block_eb": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, POINTER(ctypes.c_uint32),
+                                       ctypes.c_uint32, c_int32, POINTER(c_int32)]),
     "dg_get_prompt_kv": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
     "dg_forward_hidden": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p]),
     "dg_forward_layers": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
@@ -65,6 +69,12 @@ _SIGS = {
     "dg_k_argmax_conf": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
     "dg_k_lock_select": (c_int32, [c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                    POINTER(c_int32), c_void_p]),
+    "dg_k_eb_rows": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32, POINTER(ctypes.c_uint32),
+                               ctypes.c_uint32, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "dg_k_eb_noise": (c_int32, [c_int32, c_int32, c_int32, c_int32, POINTER(ctypes.c_uint32), ctypes.c_uint32,
+                                c_void_p, c_void_p]),
+    "dg_k_eb_select": (c_int32, [c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                 c_void_p, c_int32, c_int32, c_void_p]),
     "dg_k_moe_route": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                  c_void_p, c_void_p, c_void_p]),
     "dg_k_qkv": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
@@ -73,6 +83,8 @@ _SIGS = {
     "dg_k_moe_ffn": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
     "dg_k_lm_head": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p]),
     "dg_k_lm_argmax": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p]),
+    "dg_k_lm_sample": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, POINTER(ctypes.c_uint32),
+                                 ctypes.c_uint32, c_void_p, c_void_p, c_void_p]),
     "dg_profile": (c_int32, [c_void_p, c_int32]),
     "dg_profile_read": (c_int32, [c_void_p, c_int32, POINTER(c_int32), POINTER(ctypes.c_double)]),
 }
@@ -239,6 +251,30 @@ class Context:
         self._c(lib().dg_generate_block(self._h, tokens.shape[0], n_steps, _ptr(tokens, torch.int32, "tokens"),
                                         _ptr(locked, torch.uint8, "locked")))
 
+    # -- entropy-bounded denoising ------------------------------------------------
+    def eb_step(self, tokens, locked, t: int, t_max: int, seeds: Sequence[int], block: int, prev_pred, status,
+                entropy=None, sample=None, pred=None):
+        """One EB pass (dg_eb_step); ``prev_pred [B, N]`` and ``status [B]``
+        (int32, device) carry the per-canvas state between passes."""
+        import torch
+        B = tokens.shape[0]
+        sd = _seeds(seeds, B)
+        self._c(lib().dg_eb_step(self._h, B, _ptr(tokens, torch.int32, "tokens"), _ptr(locked, torch.uint8, "locked"),
+                                 t, t_max, sd, block, _ptr(prev_pred, torch.int32, "prev_pred"),
+                                 _ptr(status, torch.int32, "status"), _ptr(entropy, torch.float32, "entropy"),
+                                 _ptr(sample, torch.int32, "sample"), _ptr(pred, torch.int32, "pred")))
+
+    def generate_block_eb(self, tokens, locked, seeds: Sequence[int], block: int = 0, t_max: int = 48):
+        """EB passes until every canvas is done (dg_generate_block_eb); returns
+        the number of passes after which each canvas was done."""
+        import torch
+        B = tokens.shape[0]
+        sd = _seeds(seeds, B)
+        passes = (c_int32 * B)()
+        self._c(lib().dg_generate_block_eb(self._h, B, _ptr(tokens, torch.int32, "tokens"),
+                                           _ptr(locked, torch.uint8, "locked"), sd, block, t_max, passes))
+        return [int(p) for p in passes]
+
     def commit_block(self, tokens):
         """Commit the canvases ``tokens [batch, N]`` (int32, device) to the
         prompt KV caches (dg_commit_block): every slot's prompt_len grows by N."""
@@ -316,6 +352,45 @@ class Context:
         import torch
         self._c(lib().dg_k_lm_argmax(self._h, batch, _ptr(h, self.wdtype, "h"),
                                      _ptr(pred, torch.int32, "pred"), _ptr(conf, torch.float32, "conf")))
+
+    def k_lm_sample(self, batch: int, h, t: int, t_max: int, seeds: Sequence[int], block: int, pred, entropy, sample):
+        import torch
+        sd = _seeds(seeds, batch)
+        self._c(lib().dg_k_lm_sample(self._h, batch, _ptr(h, self.wdtype, "h"), t, t_max, sd, block,
+                                     _ptr(pred, torch.int32, "pred"), _ptr(entropy, torch.float32, "entropy"),
+                                     _ptr(sample, torch.int32, "sample")))
+
+
+def _seeds(seeds: Sequence[int], n: int):
+    if len(seeds) != n:
+        raise ValueError(f"{n} seeds expected, got {len(seeds)}")
+    return (ctypes.c_uint32 * max(1, n))(*[int(x) & 0xFFFFFFFF for x in seeds])
+
+
+def k_eb_rows(logits, canvas_len: int, t: int, t_max: int, seeds: Sequence[int], block: int, pred, entropy, sample,
+              stream=None):
+    import torch
+    rows, V = logits.shape
+    sd = _seeds(seeds, rows // canvas_len)
+    _check(lib().dg_k_eb_rows(_ptr(logits, torch.float32, "logits"), rows, V, canvas_len, t, t_max, sd, block,
+                              _ptr(pred, torch.int32, "pred"), _ptr(entropy, torch.float32, "entropy"),
+                              _ptr(sample, torch.int32, "sample"), _stream(stream)))
+
+
+def k_eb_noise(rows: int, vocab: int, canvas_len: int, t: int, seeds: Sequence[int], block: int, noise, stream=None):
+    import torch
+    sd = _seeds(seeds, rows // canvas_len)
+    _check(lib().dg_k_eb_noise(rows, vocab, canvas_len, t, sd, block, _ptr(noise, torch.float32, "noise"),
+                               _stream(stream)))
+
+
+def k_eb_select(entropy, sample, pred, tokens, locked, prev_pred, status, t: int, t_max: int, stream=None):
+    import torch
+    B, N = tokens.shape
+    _check(lib().dg_k_eb_select(B, N, _ptr(entropy, torch.float32, "entropy"), _ptr(sample, torch.int32, "sample"),
+                                _ptr(pred, torch.int32, "pred"), _ptr(tokens, torch.int32, "tokens"),
+                                _ptr(locked, torch.uint8, "locked"), _ptr(prev_pred, torch.int32, "prev_pred"),
+                                _ptr(status, torch.int32, "status"), t, t_max, _stream(stream)))
 
 
 def k_argmax_conf(logits, pred, conf, stream=None):

@@ -30,6 +30,9 @@ HIPCC_FLAGS = [
     # head's 128 accumulators were shuffled between register files on every
     # loop iteration
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    # loops marked for full unrolling stay unrolled even when large (the LM
+    # head's sampler epilogue indexes its accumulators with the loop counters)
+    "-mllvm", "-pragma-unroll-threshold=65536",
     "-Wno-unused-result",
 ]
 

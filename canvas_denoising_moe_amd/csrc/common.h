@@ -198,19 +198,114 @@ hipError_t launch_embed(int is_bf16, const int32_t* tokens, int rows, int H, int
                         const void* packed_embed, float* x, hipStream_t s);
 hipError_t launch_rope_table(float2* cs, int N, int D, int prompt_len, double theta, hipStream_t s);
 
+// ----------------------------------------------------------------------------
+// Entropy-bounded sampling: counter-based noise and per-row statistics
+// ----------------------------------------------------------------------------
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy
+// as 1, 2, 3", SC 2011): ten rounds of two 32x32 -> 64-bit products with a
+// Weyl sequence of round keys.
+DG_DEV uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c.x, p1 = (uint64_t)0xCD9E8D57u * c.z;
+    const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+// Gumbel noise from a 32-bit word: u = (2n + 1) 2^-24 from the top 23 bits
+// (exact, strictly inside (0, 1)), g = -log(-log u), written with the
+// hardware base-2 logarithm: -log(-log u) = -ln2 log2(-log2 u) - log(ln 2).
+// Both arguments are normal floats (-log2 u lies in [8.6e-8, 24]).
+DG_DEV float gumbel_from_bits(uint32_t w) {
+  const float u = (float)(((w >> 9) << 1) | 1u) * 0x1p-24f;
+  const float e2 = -__builtin_amdgcn_logf(u);
+  return fmaf(-0.693147180559945309f, __builtin_amdgcn_logf(e2), 0.366512920581664327f);
+}
+
+// Sampling score l * (1/tau) + g with the product and the sum rounded apart,
+// so the sampled id is the same wherever the same float logit is scored.
+DG_DEV float eb_score(float l, float inv_tau, float g) {
+#pragma clang fp contract(off)
+  const float z = l * inv_tau;
+  return z + g;
+}
+
+// Per-pass sampler parameters: canvas b of a row is row / N, its position row
+// % N; its noise key is (seed[b], block) and the counter's third word the pass.
+struct EbArg {
+  float inv_tau;
+  uint32_t t, block;
+  int32_t N;
+  uint32_t seed[64];
+};
+
+// Per-row statistics of softmax(l / tau) over a vocabulary range: greedy max m
+// and its id, S = sum exp(z - m z_), U = sum exp(z - m_z) (z - m_z) with z =
+// l / tau and m_z = m / tau, and the best sampling score with its id.
+struct EbPart { float m; int i; float S, U, gs; int gi; };
+
+// Merge of two vocabulary ranges; equal maxima and scores keep the lower id.
+DG_DEV EbPart eb_merge(EbPart a, EbPart b, float inv_tau) {
+  EbPart r;
+  if (a.m > b.m || (a.m == b.m && a.i < b.i)) { r.m = a.m; r.i = a.i; } else { r.m = b.m; r.i = b.i; }
+  if (a.gs > b.gs || (a.gs == b.gs && a.gi < b.gi)) { r.gs = a.gs; r.gi = a.gi; } else { r.gs = b.gs; r.gi = b.gi; }
+  const float mz = r.m * inv_tau;
+  float S = 0.f, U = 0.f;
+  if (a.S > 0.f) {
+    const float d = a.m * inv_tau - mz, f = expf(d);
+    S += a.S * f;
+    U += (a.U + d * a.S) * f;
+  }
+  if (b.S > 0.f) {
+    const float d = b.m * inv_tau - mz, f = expf(d);
+    S += b.S * f;
+    U += (b.U + d * b.S) * f;
+  }
+  r.S = S;
+  r.U = U;
+  return r;
+}
+
+// Entropy (nats) of the merged statistics, log S - U / S, never below 0.
+DG_DEV float eb_entropy(const EbPart& p) { return fmaxf(logf(p.S) - p.U / p.S, 0.f); }
+
 // Tied LM head for bf16 contexts (lmhead.hip): h bf16 [M, K] @ E^T with E packed
 // as the B operand ([V/16][K/32][64][8]).  Store mode writes logits fp32 [M, V];
 // argmax mode writes pred/conf [M] through per-(vocabulary tile, row) partials
-// part_* [(V/256 rounded up) * M].  Needs K % 256 == 0 and V % 16 == 0.
+// part_* [(V/256 rounded up) * M]; sampler mode writes pred, the entropy ent
+// and the sample samp [M] through the partials part_m/s/i and part_u/g/gi.
+// Needs K % 128 == 0, M % 16 == 0 and V % 16 == 0.
+enum LmMode { LM_STORE = 0, LM_ARGMAX = 1, LM_SAMPLE = 2 };
 struct LmArgs {
   const void* h; int M, K, V;
   const void* E;
   float* logits;
   float* part_m; float* part_s; int32_t* part_i;
+  float* part_u; float* part_g; int32_t* part_gi;
   int32_t* pred; float* conf;
+  float* ent; int32_t* samp;
+  EbArg eb;
 };
 bool lm_head_supported(int M, int K, int V);
-hipError_t launch_lm_head(const LmArgs& a, bool argmax, hipStream_t s, KTime t = {});
+hipError_t launch_lm_head(const LmArgs& a, int mode, hipStream_t s, KTime t = {});
+
+// Sampler statistics of fp32 logits [rows, V] (eb.hip): pred, ent, samp [rows].
+hipError_t launch_eb_rows(const float* logits, int rows, int V, const EbArg& eb, int32_t* pred, float* ent,
+                          int32_t* samp, hipStream_t s);
+// The Gumbel noise of rows [rows, V] as the sampler draws it (eb.hip).
+hipError_t launch_eb_noise(int rows, int V, const EbArg& eb, float* out, hipStream_t s);
+// The entropy-bounded lock step of B canvases of N positions (eb.hip).
+// status[b]: bit 0 done, bit 1 a previous pass's greedy tokens are in
+// prev_pred, bit 2 this pass stopped the canvas.
+hipError_t launch_eb_select(int B, int N, const float* ent, const int32_t* samp, const int32_t* pred,
+                            int32_t* tokens, uint8_t* locked, int32_t* prev_pred, int32_t* status, int t,
+                            int t_max, hipStream_t s);
 
 // Head: argmax / confidence and the lock step.
 hipError_t launch_argmax_conf(const float* logits, int rows, int V, int32_t* pred, float* conf,

@@ -22,6 +22,15 @@
 // waves are merged in column order through LDS, and one (max, sum, argmax)
 // partial per (row, vocabulary tile) is written.  k_lm_merge folds the
 // partials of a row in a fixed tree order.
+//
+// Sampler mode (entropy-bounded denoising, [4xFaster] "Recommended Inference
+// Settings"): the same tile also yields, per row, the statistics of
+// softmax(l / tau) -- S = sum exp(z - m_z) and U = sum exp(z - m_z)(z - m_z),
+// from which the entropy log S - U / S follows -- and the Gumbel-max sample,
+// the largest l / tau + g.  The noise is Philox4x32-10 keyed by the row's
+// canvas: one call per lane and row yields the four words of the lane's four
+// columns (ids v, v + 16, v + 32, v + 48 of a 64-id group), so the counter of
+// id v is ((v >> 6) * 16 + (v & 15), position, pass, 0) and its word (v >> 4) & 3.
 #include "common.h"
 
 namespace {
@@ -54,7 +63,7 @@ DG_DEV void mma_bf16(floatx4& c, const v4u& a, const v4u& b) {
                                               c, 0, 0, 0);
 }
 
-template <bool ARGMAX>
+template <int MODE>
 __global__ __launch_bounds__(256) void k_lm_head(LmArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   bf16_t* As = reinterpret_cast<bf16_t*>(smem);  // [2][KC][RT][64][8]
@@ -142,7 +151,7 @@ __global__ __launch_bounds__(256) void k_lm_head(LmArgs a) {
   mfma_drain();
 
   const int col_in = lane & 15, rq = (lane >> 4) * 4;
-  if constexpr (!ARGMAX) {
+  if constexpr (MODE == LM_STORE) {
 #pragma unroll
     for (int rt = 0; rt < kLmRT; ++rt)
 #pragma unroll
@@ -154,6 +163,69 @@ __global__ __launch_bounds__(256) void k_lm_head(LmArgs a) {
         for (int cc = 0; cc < 4; ++cc)
           if (nb0 + cc < NB) out[(nb0 + cc) * 16 + col_in] = acc[rt][cc][r];
       }
+  } else if constexpr (MODE == LM_SAMPLE) {
+    EbPart* red = reinterpret_cast<EbPart*>(smem);  // [4 waves][rows]; A chunks are done
+    const float inv = a.eb.inv_tau;
+    const uint32_t call = (uint32_t)(nb0 >> 2) * 16u + (uint32_t)col_in;
+#pragma unroll
+    for (int rt = 0; rt < kLmRT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        // rows past M repeat the last row's inputs; their results are dropped
+        const int row = min(rbase + rt * 16 + rq + r, a.M - 1);
+        const int cb = row / a.eb.N, pos = row - cb * a.eb.N;
+        const uint4 w = philox4x32_10(make_uint4(call, (uint32_t)pos, a.eb.t, 0u), a.eb.seed[cb], a.eb.block);
+        const float g[4] = {gumbel_from_bits(w.x), gumbel_from_bits(w.y), gumbel_from_bits(w.z),
+                            gumbel_from_bits(w.w)};
+        // this lane's 4 columns ascend with cc; columns past the vocabulary are skipped
+        float m = -INFINITY, gs = -INFINITY;
+        int mi = 0x7fffffff, gi = 0x7fffffff;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          if (nb0 + cc >= NB) continue;
+          const float v = acc[rt][cc][r];
+          const int id = (nb0 + cc) * 16 + col_in;
+          if (v > m) { m = v; mi = id; }
+          const float sc = eb_score(v, inv, g[cc]);
+          if (sc > gs) { gs = sc; gi = id; }
+        }
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) {  // the 16 lanes holding this row
+          const float om = __shfl_xor(m, o, 64), og = __shfl_xor(gs, o, 64);
+          const int oi = __shfl_xor(mi, o, 64), ogi = __shfl_xor(gi, o, 64);
+          if (om > m || (om == m && oi < mi)) { m = om; mi = oi; }
+          if (og > gs || (og == gs && ogi < gi)) { gs = og; gi = ogi; }
+        }
+        const float mz = m * inv;
+        float S = 0.f, U = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          if (nb0 + cc >= NB) continue;
+          const float d = acc[rt][cc][r] * inv - mz, e = expf(d);
+          S += e;
+          U += e * d;
+        }
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) {
+          S += __shfl_xor(S, o, 64);
+          U += __shfl_xor(U, o, 64);
+        }
+        if (col_in == 0) red[wave * kLmRows + rt * 16 + rq + r] = EbPart{m, mi, S, U, gs, gi};
+      }
+    __syncthreads();
+    const int row = rbase + tid;
+    if (tid < kLmRows && row < a.M) {
+      EbPart p = red[tid];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) p = eb_merge(p, red[w * kLmRows + tid], inv);  // column order
+      const long long o = (long long)vt * a.M + row;
+      a.part_m[o] = p.m;
+      a.part_i[o] = p.i;
+      a.part_s[o] = p.S;
+      a.part_u[o] = p.U;
+      a.part_g[o] = p.gs;
+      a.part_gi[o] = p.gi;
+    }
   } else {
     Part* red = reinterpret_cast<Part*>(smem);  // [4 waves][rows]; A chunks are done
 #pragma unroll
@@ -224,28 +296,67 @@ __global__ __launch_bounds__(256) void k_lm_merge(LmArgs a) {
   }
 }
 
+// Sampler mode: fold a row's (vocabulary tile) partials in a fixed tree
+// order into its greedy id, entropy and sample.
+__global__ __launch_bounds__(256) void k_lm_merge_eb(LmArgs a) {
+  __shared__ EbPart red[4];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int NVT = ((a.V >> 4) + 15) >> 4;
+  const float inv = a.eb.inv_tau;
+  EbPart p{-INFINITY, 0x7fffffff, 0.f, 0.f, -INFINITY, 0x7fffffff};
+  for (int t = tid; t < NVT; t += 256) {
+    const long long o = (long long)t * a.M + row;
+    p = eb_merge(p, EbPart{a.part_m[o], a.part_i[o], a.part_s[o], a.part_u[o], a.part_g[o], a.part_gi[o]}, inv);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    EbPart q;
+    q.m = __shfl_xor(p.m, o, 64);
+    q.i = __shfl_xor(p.i, o, 64);
+    q.S = __shfl_xor(p.S, o, 64);
+    q.U = __shfl_xor(p.U, o, 64);
+    q.gs = __shfl_xor(p.gs, o, 64);
+    q.gi = __shfl_xor(p.gi, o, 64);
+    p = eb_merge(p, q, inv);
+  }
+  if ((tid & 63) == 0) red[tid >> 6] = p;
+  __syncthreads();
+  if (tid == 0) {
+    EbPart r = red[0];
+    for (int w = 1; w < 4; ++w) r = eb_merge(r, red[w], inv);
+    a.pred[row] = r.i;
+    a.ent[row] = eb_entropy(r);
+    a.samp[row] = r.gi;
+  }
+}
+
 }  // namespace
 
 bool lm_head_supported(int M, int K, int V) {
   return M > 0 && M % 16 == 0 && K % (32 * kLmKC) == 0 && V % 16 == 0;
 }
 
-hipError_t launch_lm_head(const LmArgs& a, bool argmax, hipStream_t s, KTime t) {
+hipError_t launch_lm_head(const LmArgs& a, int mode, hipStream_t s, KTime t) {
   if (a.M <= 0) return hipSuccess;
-  if (!lm_head_supported(a.M, a.K, a.V)) return hipErrorInvalidValue;
+  if (!lm_head_supported(a.M, a.K, a.V) || mode < LM_STORE || mode > LM_SAMPLE) return hipErrorInvalidValue;
+  if (mode == LM_SAMPLE && (a.eb.N <= 0 || a.M % a.eb.N != 0 || a.M / a.eb.N > 64)) return hipErrorInvalidValue;
   const int NVT = ((a.V >> 4) + 15) >> 4, NRG = (a.M + kLmRows - 1) / kLmRows;
   const long long blocks = (((long long)NVT * NRG + 7) >> 3) << 3;
-  const void* fn = argmax ? reinterpret_cast<const void*>(&k_lm_head<true>)
-                          : reinterpret_cast<const void*>(&k_lm_head<false>);
-  static bool attr[2] = {false, false};
-  if (!attr[argmax]) {
-    hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLmLds);
+  static_assert(4 * kLmRows * sizeof(EbPart) <= kLmLds, "the wave merge fits the A staging area");
+  const void* fns[3] = {reinterpret_cast<const void*>(&k_lm_head<LM_STORE>),
+                        reinterpret_cast<const void*>(&k_lm_head<LM_ARGMAX>),
+                        reinterpret_cast<const void*>(&k_lm_head<LM_SAMPLE>)};
+  static bool attr[3] = {false, false, false};
+  if (!attr[mode]) {
+    hipError_t err = hipFuncSetAttribute(fns[mode], hipFuncAttributeMaxDynamicSharedMemorySize, kLmLds);
     if (err != hipSuccess) return err;
-    attr[argmax] = true;
+    attr[mode] = true;
   }
-  if (!argmax)
-    return launch_k(k_lm_head<false>, dim3((unsigned)blocks), dim3(256), kLmLds, s, t.start, t.stop, a);
-  hipError_t e = launch_k(k_lm_head<true>, dim3((unsigned)blocks), dim3(256), kLmLds, s, t.start, nullptr, a);
+  const dim3 grid((unsigned)blocks);
+  if (mode == LM_STORE) return launch_k(k_lm_head<LM_STORE>, grid, dim3(256), kLmLds, s, t.start, t.stop, a);
+  hipError_t e = mode == LM_ARGMAX ? launch_k(k_lm_head<LM_ARGMAX>, grid, dim3(256), kLmLds, s, t.start, nullptr, a)
+                                   : launch_k(k_lm_head<LM_SAMPLE>, grid, dim3(256), kLmLds, s, t.start, nullptr, a);
   if (e != hipSuccess) return e;
-  return launch_k(k_lm_merge, dim3((unsigned)a.M), dim3(256), 0, s, nullptr, t.stop, a);
+  if (mode == LM_ARGMAX) return launch_k(k_lm_merge, dim3((unsigned)a.M), dim3(256), 0, s, nullptr, t.stop, a);
+  return launch_k(k_lm_merge_eb, dim3((unsigned)a.M), dim3(256), 0, s, nullptr, t.stop, a);
 }

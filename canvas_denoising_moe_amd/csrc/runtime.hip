@@ -59,6 +59,13 @@ struct dg_ctx {
   // fused LM head + argmax (bf16): per-(vocabulary tile, row) partials
   float *lm_m = nullptr, *lm_s = nullptr;
   int32_t* lm_i = nullptr;
+  // sampler mode partials, per-row entropy / sample, and the state of the
+  // entropy-bounded loop (greedy tokens of the previous pass, status flags)
+  float *lm_u = nullptr, *lm_g = nullptr;
+  int32_t* lm_gi = nullptr;
+  float* eb_ent = nullptr;
+  int32_t *eb_samp = nullptr, *eb_prev = nullptr, *eb_status = nullptr;
+  int32_t* eb_status_host = nullptr;  // pinned
   bool lm_fused = false;
   long long part_cap = 0;
   int32_t* trace = nullptr;
@@ -256,11 +263,23 @@ dg_status alloc_workspaces(dg_ctx* ctx) {
     TRY(dalloc_t(ctx, &ctx->lm_m, parts * 4));
     TRY(dalloc_t(ctx, &ctx->lm_s, parts * 4));
     TRY(dalloc_t(ctx, &ctx->lm_i, parts * 4));
+    TRY(dalloc_t(ctx, &ctx->lm_u, parts * 4));
+    TRY(dalloc_t(ctx, &ctx->lm_g, parts * 4));
+    TRY(dalloc_t(ctx, &ctx->lm_gi, parts * 4));
   } else if (c.has_lm_head) {
     TRY(dalloc_t(ctx, &ctx->logits, M * (size_t)c.vocab * 4));
   }
   TRY(dalloc_t(ctx, &ctx->pred, M * 4));
   TRY(dalloc_t(ctx, &ctx->conf, M * 4));
+  if (c.has_lm_head) {
+    TRY(dalloc_t(ctx, &ctx->eb_ent, M * 4));
+    TRY(dalloc_t(ctx, &ctx->eb_samp, M * 4));
+    TRY(dalloc_t(ctx, &ctx->eb_prev, M * 4));
+    TRY(dalloc_t(ctx, &ctx->eb_status, (size_t)c.max_batch * 4));
+    void* hp = nullptr;
+    HIPX(hipHostMalloc(&hp, (size_t)c.max_batch * 4, hipHostMallocDefault));
+    ctx->eb_status_host = static_cast<int32_t*>(hp);
+  }
   TRY(dalloc_t(ctx, &ctx->rope, (size_t)c.max_batch * c.canvas_len * (D / 2) * sizeof(float2)));
   // attention split partials: up to 64 splits of every query row
   const long long qrows = (long long)M * c.n_heads;
@@ -517,7 +536,7 @@ dg_status enqueue_head(dg_ctx* ctx, const void* h, int M, int32_t* pred, float* 
   if (ctx->lm_fused) {
     LmArgs la = lm_args(ctx, h, M);
     la.pred = pred; la.conf = conf;
-    HIPX(launch_lm_head(la, true, ctx->st, t));
+    HIPX(launch_lm_head(la, LM_ARGMAX, ctx->st, t));
     return DG_OK;
   }
   TRY(enqueue_dense(ctx, h, c.hidden, ctx->embed, c.hidden, c.vocab, M, ctx->logits, c.vocab, false, t));
@@ -525,17 +544,66 @@ dg_status enqueue_head(dg_ctx* ctx, const void* h, int M, int32_t* pred, float* 
   return DG_OK;
 }
 
-dg_status enqueue_pass(dg_ctx* ctx, int B, int32_t* tokens, uint8_t* locked, const StepsArg& steps) {
+// Sampler statistics of h [M, H]: greedy id, entropy of softmax(l / tau) and
+// the Gumbel-max sample per row (fused on matrix cores for bf16, else logits
+// into the workspace and a row kernel).
+dg_status enqueue_head_eb(dg_ctx* ctx, const void* h, int M, const EbArg& eb, int32_t* pred, float* ent,
+                          int32_t* samp, KTime t = {}) {
   const dg_config& c = ctx->c;
-  const int N = c.canvas_len, M = B * N, H = c.hidden;
+  if (ctx->lm_fused) {
+    LmArgs la = lm_args(ctx, h, M);
+    la.part_u = ctx->lm_u; la.part_g = ctx->lm_g; la.part_gi = ctx->lm_gi;
+    la.pred = pred; la.ent = ent; la.samp = samp; la.eb = eb;
+    HIPX(launch_lm_head(la, LM_SAMPLE, ctx->st, t));
+    return DG_OK;
+  }
+  TRY(enqueue_dense(ctx, h, c.hidden, ctx->embed, c.hidden, c.vocab, M, ctx->logits, c.vocab, false, t));
+  HIPX(launch_eb_rows(ctx->logits, M, c.vocab, eb, pred, ent, samp, ctx->st));
+  return DG_OK;
+}
+
+// embed -> decoder stack -> final norm into ctx->a
+dg_status enqueue_trunk(dg_ctx* ctx, int B, const int32_t* tokens) {
+  const dg_config& c = ctx->c;
+  const int M = B * c.canvas_len, H = c.hidden;
   HIPX(launch_embed(ctx->bf16, tokens, M, H, c.vocab, ctx->embed, ctx->x, ctx->st));
   NormArgs n0{};
   n0.mode = 2; n0.rows = M; n0.H = H; n0.k = c.top_k; n0.eps = c.rms_eps;
   n0.x = ctx->x; n0.w_out = ctx->L[0].norm[0]; n0.out = ctx->a;
   HIPX(launch_residual_norm(ctx->bf16, n0, ctx->st));
   TRY(enqueue_layers(ctx, B, ctx->norm_final));
+  return DG_OK;
+}
+
+dg_status enqueue_pass(dg_ctx* ctx, int B, int32_t* tokens, uint8_t* locked, const StepsArg& steps) {
+  const int N = ctx->c.canvas_len, M = B * N;
+  TRY(enqueue_trunk(ctx, B, tokens));
   TRY(enqueue_head(ctx, ctx->a, M, ctx->pred, ctx->conf, prof_kernel(ctx, DG_PROF_LM_HEAD)));
   HIPX(launch_lock_select(B, N, ctx->conf, ctx->pred, tokens, locked, steps, ctx->st));
+  return DG_OK;
+}
+
+// Temperature of pass t of at most t_max: linear from 0.8 to 0.4
+// ([4xFaster] "Recommended Inference Settings").
+EbArg eb_arg(const dg_config& c, int t, int t_max, const uint32_t* seeds, int B, uint32_t block) {
+  EbArg e{};
+  const double tau = t_max > 1 ? 0.8 + (0.4 - 0.8) * t / (t_max - 1) : 0.8;
+  e.inv_tau = (float)(1.0 / tau);
+  e.t = (uint32_t)t;
+  e.block = block;
+  e.N = c.canvas_len;
+  for (int b = 0; b < B; ++b) e.seed[b] = seeds[b];
+  return e;
+}
+
+// One entropy-bounded pass: the stack, the sampler statistics and the lock step.
+dg_status enqueue_pass_eb(dg_ctx* ctx, int B, int32_t* tokens, uint8_t* locked, int t, int t_max,
+                          const EbArg& eb, int32_t* prev_pred, int32_t* status) {
+  const int N = ctx->c.canvas_len, M = B * N;
+  TRY(enqueue_trunk(ctx, B, tokens));
+  TRY(enqueue_head_eb(ctx, ctx->a, M, eb, ctx->pred, ctx->eb_ent, ctx->eb_samp, prof_kernel(ctx, DG_PROF_LM_HEAD)));
+  HIPX(launch_eb_select(B, N, ctx->eb_ent, ctx->eb_samp, ctx->pred, tokens, locked, prev_pred, status, t, t_max,
+                        ctx->st));
   return DG_OK;
 }
 
@@ -586,6 +654,7 @@ dg_status dg_destroy(dg_ctx* ctx) {
   for (hipEvent_t e : ctx->ev_pool) (void)hipEventDestroy(e);
   for (void* p : ctx->owned)
     if (p) (void)hipFree(p);
+  if (ctx->eb_status_host) (void)hipHostFree(ctx->eb_status_host);
   delete ctx;
   return DG_OK;
 }
@@ -809,6 +878,66 @@ dg_status dg_generate_block(dg_ctx* ctx, int32_t batch, int32_t n_steps, int32_t
   return DG_OK;
 }
 
+namespace {
+dg_status check_eb(dg_ctx* ctx, int32_t batch, int32_t t, int32_t t_max, const uint32_t* seeds) {
+  const dg_config& c = ctx->c;
+  if (!c.has_lm_head) return fail(ctx, DG_ESTATE, "context has no LM head");
+  if (batch < 1 || batch > c.max_batch) return fail(ctx, DG_EINVAL, "batch %d outside [1, %d]", batch, c.max_batch);
+  if (t_max < 1 || t_max > (1 << 20)) return fail(ctx, DG_EINVAL, "t_max %d outside [1, 2^20]", t_max);
+  if (t < 0 || t >= t_max) return fail(ctx, DG_EINVAL, "pass %d outside [0, t_max = %d)", t, t_max);
+  if (!seeds) return fail(ctx, DG_EINVAL, "seeds are required");
+  if (!weights_ready(ctx)) return fail(ctx, DG_ESTATE, "weights are not loaded");
+  return check_slots(ctx, batch);
+}
+}  // namespace
+
+dg_status dg_eb_step(dg_ctx* ctx, int32_t batch, int32_t* tokens, uint8_t* locked, int32_t t, int32_t t_max,
+                     const uint32_t* seeds_host, uint32_t block, int32_t* prev_pred, int32_t* status,
+                     float* entropy_out, int32_t* sample_out, int32_t* pred_out) {
+  TRY(enter(ctx));
+  TRY(check_eb(ctx, batch, t, t_max, seeds_host));
+  if (!tokens || !locked || !prev_pred || !status)
+    return fail(ctx, DG_EINVAL, "tokens, locked, prev_pred and status are required");
+  const dg_config& c = ctx->c;
+  const EbArg eb = eb_arg(c, t, t_max, seeds_host, batch, block);
+  hipEvent_t evp = prof_start(ctx, DG_PROF_PASS);
+  TRY(enqueue_pass_eb(ctx, batch, tokens, locked, t, t_max, eb, prev_pred, status));
+  prof_stop(ctx, DG_PROF_PASS, evp);
+  const size_t M = (size_t)batch * c.canvas_len;
+  if (entropy_out) HIPX(hipMemcpyAsync(entropy_out, ctx->eb_ent, M * 4, hipMemcpyDeviceToDevice, ctx->st));
+  if (sample_out) HIPX(hipMemcpyAsync(sample_out, ctx->eb_samp, M * 4, hipMemcpyDeviceToDevice, ctx->st));
+  if (pred_out) HIPX(hipMemcpyAsync(pred_out, ctx->pred, M * 4, hipMemcpyDeviceToDevice, ctx->st));
+  return DG_OK;
+}
+
+dg_status dg_generate_block_eb(dg_ctx* ctx, int32_t batch, int32_t* tokens, uint8_t* locked,
+                               const uint32_t* seeds_host, uint32_t block, int32_t t_max, int32_t* passes_out) {
+  TRY(enter(ctx));
+  TRY(check_eb(ctx, batch, 0, t_max, seeds_host));
+  if (!tokens || !locked) return fail(ctx, DG_EINVAL, "tokens and locked are required");
+  const dg_config& c = ctx->c;
+  std::vector<int32_t> passes(batch, 0);
+  HIPX(hipMemsetAsync(ctx->eb_status, 0, (size_t)batch * 4, ctx->st));
+  for (int t = 0; t < t_max; ++t) {
+    const EbArg eb = eb_arg(c, t, t_max, seeds_host, batch, block);
+    hipEvent_t evp = prof_start(ctx, DG_PROF_PASS);
+    TRY(enqueue_pass_eb(ctx, batch, tokens, locked, t, t_max, eb, ctx->eb_prev, ctx->eb_status));
+    prof_stop(ctx, DG_PROF_PASS, evp);
+    // the stop decision is the device's: read the canvases' status after each pass
+    HIPX(hipMemcpyAsync(ctx->eb_status_host, ctx->eb_status, (size_t)batch * 4, hipMemcpyDeviceToHost, ctx->st));
+    HIPX(hipStreamSynchronize(ctx->st));
+    bool all = true;
+    for (int b = 0; b < batch; ++b) {
+      if ((ctx->eb_status_host[b] & 1) && passes[b] == 0) passes[b] = t + 1;
+      all = all && passes[b] != 0;
+    }
+    if (all) break;
+  }
+  if (passes_out)
+    for (int b = 0; b < batch; ++b) passes_out[b] = passes[b];
+  return DG_OK;
+}
+
 dg_status dg_forward_layers(dg_ctx* ctx, int32_t batch, int32_t first, int32_t count, const float* x_in,
                             float* x_out) {
   TRY(enter(ctx));
@@ -867,6 +996,55 @@ dg_status dg_k_lock_select(int32_t batch, int32_t n, const float* conf, const in
     steps.v[b] = steps_left_host[b];
   }
   HIPX(launch_lock_select(batch, n, conf, pred, tokens, locked, steps, reinterpret_cast<hipStream_t>(stream)));
+  return DG_OK;
+}
+
+dg_status dg_k_eb_rows(const float* logits, int32_t rows, int32_t vocab, int32_t canvas_len, int32_t t,
+                       int32_t t_max, const uint32_t* seeds_host, uint32_t block, int32_t* pred, float* entropy,
+                       int32_t* sample, void* stream) {
+  dg_ctx* ctx = nullptr;
+  if (rows < 0 || vocab < 1 || canvas_len < 1) return fail(ctx, DG_EINVAL, "rows >= 0, vocab >= 1, canvas_len >= 1 required");
+  if (rows % canvas_len || rows / canvas_len > DG_MAX_BATCH)
+    return fail(ctx, DG_EINVAL, "rows must be a multiple of canvas_len, at most 64 canvases");
+  if (t_max < 1 || t < 0 || t >= t_max) return fail(ctx, DG_EINVAL, "pass %d outside [0, t_max = %d)", t, t_max);
+  if (rows == 0) return DG_OK;
+  if (!logits || !pred || !entropy || !sample || !seeds_host)
+    return fail(ctx, DG_EINVAL, "logits, pred, entropy, sample and seeds are required");
+  dg_config c{};
+  c.canvas_len = canvas_len;
+  const EbArg eb = eb_arg(c, t, t_max, seeds_host, rows / canvas_len, block);
+  HIPX(launch_eb_rows(logits, rows, vocab, eb, pred, entropy, sample, reinterpret_cast<hipStream_t>(stream)));
+  return DG_OK;
+}
+
+dg_status dg_k_eb_noise(int32_t rows, int32_t vocab, int32_t canvas_len, int32_t t, const uint32_t* seeds_host,
+                        uint32_t block, float* noise, void* stream) {
+  dg_ctx* ctx = nullptr;
+  if (rows < 0 || vocab < 1 || canvas_len < 1) return fail(ctx, DG_EINVAL, "rows >= 0, vocab >= 1, canvas_len >= 1 required");
+  if (rows % canvas_len || rows / canvas_len > DG_MAX_BATCH)
+    return fail(ctx, DG_EINVAL, "rows must be a multiple of canvas_len, at most 64 canvases");
+  if (t < 0) return fail(ctx, DG_EINVAL, "pass %d < 0", t);
+  if (rows == 0) return DG_OK;
+  if (!noise || !seeds_host) return fail(ctx, DG_EINVAL, "noise and seeds are required");
+  dg_config c{};
+  c.canvas_len = canvas_len;
+  const EbArg eb = eb_arg(c, t, t + 1, seeds_host, rows / canvas_len, block);
+  HIPX(launch_eb_noise(rows, vocab, eb, noise, reinterpret_cast<hipStream_t>(stream)));
+  return DG_OK;
+}
+
+dg_status dg_k_eb_select(int32_t batch, int32_t n, const float* entropy, const int32_t* sample,
+                         const int32_t* pred, int32_t* tokens, uint8_t* locked, int32_t* prev_pred,
+                         int32_t* status, int32_t t, int32_t t_max, void* stream) {
+  dg_ctx* ctx = nullptr;
+  if (batch < 0 || batch > DG_MAX_BATCH || n < 1 || n > 4096)
+    return fail(ctx, DG_EINVAL, "batch must be in [0, 64] and n in [1, 4096]");
+  if (t_max < 1 || t < 0 || t >= t_max) return fail(ctx, DG_EINVAL, "pass %d outside [0, t_max = %d)", t, t_max);
+  if (batch == 0) return DG_OK;
+  if (!entropy || !sample || !pred || !tokens || !locked || !prev_pred || !status)
+    return fail(ctx, DG_EINVAL, "entropy, sample, pred, tokens, locked, prev_pred and status are required");
+  HIPX(launch_eb_select(batch, n, entropy, sample, pred, tokens, locked, prev_pred, status, t, t_max,
+                        reinterpret_cast<hipStream_t>(stream)));
   return DG_OK;
 }
 
@@ -957,7 +1135,7 @@ dg_status dg_k_lm_head(dg_ctx* ctx, int32_t batch, const void* h, float* logits)
   if (ctx->lm_fused) {
     LmArgs la = lm_args(ctx, h, M);
     la.logits = logits;
-    HIPX(launch_lm_head(la, false, ctx->st));
+    HIPX(launch_lm_head(la, LM_STORE, ctx->st));
     return DG_OK;
   }
   return enqueue_dense(ctx, h, c.hidden, ctx->embed, c.hidden, c.vocab, M, logits, c.vocab, false);
@@ -970,6 +1148,20 @@ dg_status dg_k_lm_argmax(dg_ctx* ctx, int32_t batch, const void* h, int32_t* pre
   if (batch < 1 || batch > c.max_batch) return fail(ctx, DG_EINVAL, "batch out of range");
   if (!h || !pred || !conf) return fail(ctx, DG_EINVAL, "h, pred and conf are required");
   return enqueue_head(ctx, h, batch * c.canvas_len, pred, conf);
+}
+
+dg_status dg_k_lm_sample(dg_ctx* ctx, int32_t batch, const void* h, int32_t t, int32_t t_max,
+                         const uint32_t* seeds_host, uint32_t block, int32_t* pred, float* entropy,
+                         int32_t* sample) {
+  TRY(enter(ctx));
+  const dg_config& c = ctx->c;
+  if (!c.has_lm_head || !ctx->embed_set) return fail(ctx, DG_ESTATE, "embedding not loaded");
+  if (batch < 1 || batch > c.max_batch) return fail(ctx, DG_EINVAL, "batch out of range");
+  if (t_max < 1 || t < 0 || t >= t_max) return fail(ctx, DG_EINVAL, "pass %d outside [0, t_max = %d)", t, t_max);
+  if (!h || !pred || !entropy || !sample || !seeds_host)
+    return fail(ctx, DG_EINVAL, "h, pred, entropy, sample and seeds are required");
+  const EbArg eb = eb_arg(c, t, t_max, seeds_host, batch, block);
+  return enqueue_head_eb(ctx, h, batch * c.canvas_len, eb, pred, entropy, sample);
 }
 
 dg_status dg_profile(dg_ctx* ctx, int32_t mask) {

@@ -160,6 +160,54 @@ dg_status dg_denoise_step(dg_ctx* ctx, int32_t batch, int32_t* tokens, uint8_t* 
 dg_status dg_generate_block(dg_ctx* ctx, int32_t batch, int32_t n_steps, int32_t* tokens,
                             uint8_t* locked);
 
+/* ---- entropy-bounded (EB) denoising ---------------------------------------
+ * The sampler the pages recommend ([4xFaster] "Recommended Inference
+ * Settings": EB sampler, at most 48 steps, temperature decaying linearly from
+ * 0.8 to 0.4, entropy bound 0.1, adaptive stop once the mean canvas entropy is
+ * below 0.005 and the high-probability tokens hold for 2 consecutive steps;
+ * [ParadigmShift] "Serving in Production: The Role of vLLM": two consecutive
+ * passes in agreement halt the block).  Pass t of at most t_max runs at
+ * tau = 0.8 + (0.4 - 0.8) t / (t_max - 1) (0.8 when t_max == 1).  Per
+ * position: entropy H of softmax(l / tau) in nats; a sample, the id of the
+ * largest l * (float)(1/tau) + g (product and sum rounded apart, ties to the
+ * lower id) with Gumbel noise g = -log(-log u), u = (2n + 1) 2^-24 from the top
+ * 23 bits n of a Philox4x32-10 word (Salmon et al., SC 2011) with key
+ * (seeds[b], block), counter ((v >> 6) * 16 + (v & 15), position, t, 0) and
+ * word (v >> 4) & 3 for vocabulary id v; the greedy id (lowest among the
+ * largest logits).  Per canvas not yet done: the unlocked positions in order
+ * of increasing H (ties to the lower position) are locked with their sample
+ * while the float32 running sum of their H stays <= 0.1f, at least one (every
+ * unlocked one when t == t_max - 1); the canvas stops when a previous pass's
+ * greedy ids are recorded, equal this pass's at every position, and the
+ * float32 mean of H over the canvas (sum in position order, then / N) is
+ * < 0.005f: its remaining unlocked positions then take their greedy ids.  A
+ * canvas is done once it stops or has no unlocked position; done canvases are
+ * left untouched.
+ *
+ * Per-canvas state (device, caller-owned): prev_pred int32 [batch, N], the
+ * greedy ids of the previous pass; status int32 [batch], bit 0 done, bit 1
+ * prev_pred holds a previous pass, bit 2 this pass stopped the canvas.  Set
+ * status to 0 before a block's first pass. */
+
+/* One EB pass t of at most t_max over canvases 0..batch-1.
+ *   tokens int32 [batch, N], locked uint8 [batch, N] device, in/out
+ *   seeds_host uint32 [batch] host; block: the noise key's second word
+ *   prev_pred, status: the state above, in/out
+ *   entropy_out float, sample_out int32, pred_out int32 [batch, N] device or NULL
+ * Requires all weights and the prompt KV of slots 0..batch-1; 0 <= t < t_max. */
+dg_status dg_eb_step(dg_ctx* ctx, int32_t batch, int32_t* tokens, uint8_t* locked, int32_t t, int32_t t_max,
+                     const uint32_t* seeds_host, uint32_t block, int32_t* prev_pred, int32_t* status,
+                     float* entropy_out, int32_t* sample_out, int32_t* pred_out);
+
+/* EB passes 0, 1, ... until every canvas is done, at most t_max (the pages'
+ * setting is 48), with the state held by the context.  After each pass the
+ * host reads the canvases' status (one stream synchronisation per pass), so
+ * the call returns when the block is resolved.  passes_out int32 [batch]
+ * host or NULL: the number of passes after which each canvas was done. */
+dg_status dg_generate_block_eb(dg_ctx* ctx, int32_t batch, int32_t* tokens, uint8_t* locked,
+                               const uint32_t* seeds_host, uint32_t block, int32_t t_max,
+                               int32_t* passes_out);
+
 /* Block continuation: commits the resolved canvases (or N prompt tokens) to
  * the prompt KV cache.  The decoder stack runs once over tokens at positions
  * prompt_len + i with causal attention inside the block (position i sees the
@@ -217,6 +265,27 @@ dg_status dg_k_lock_select(int32_t batch, int32_t n, const float* conf, const in
                            int32_t* tokens, uint8_t* locked, const int32_t* steps_left_host,
                            void* stream);
 
+/* EB statistics of float logits [rows, vocab], rows a multiple of canvas_len
+ * (row r is position r % canvas_len of canvas r / canvas_len, at most 64
+ * canvases): pred int32, entropy float, sample int32 [rows] for pass t of at
+ * most t_max, noise key (seeds_host[canvas], block) (see the EB section). */
+dg_status dg_k_eb_rows(const float* logits, int32_t rows, int32_t vocab, int32_t canvas_len, int32_t t,
+                       int32_t t_max, const uint32_t* seeds_host, uint32_t block, int32_t* pred,
+                       float* entropy, int32_t* sample, void* stream);
+
+/* The EB sampler's Gumbel noise: noise float [rows, vocab] for pass t, row
+ * r being position r % canvas_len of canvas r / canvas_len (at most 64
+ * canvases), key (seeds_host[canvas], block) (see the EB section). */
+dg_status dg_k_eb_noise(int32_t rows, int32_t vocab, int32_t canvas_len, int32_t t, const uint32_t* seeds_host,
+                        uint32_t block, float* noise, void* stream);
+
+/* The EB lock step alone on given entropy float, sample int32, pred int32
+ * [batch, n]: updates tokens, locked, prev_pred [batch, n] and status [batch]
+ * as an EB pass t of at most t_max does; batch <= 64, n <= 4096. */
+dg_status dg_k_eb_select(int32_t batch, int32_t n, const float* entropy, const int32_t* sample,
+                         const int32_t* pred, int32_t* tokens, uint8_t* locked, int32_t* prev_pred,
+                         int32_t* status, int32_t t, int32_t t_max, void* stream);
+
 /* Top-k routing on float router logits [rows, E] ([4xFaster] "DiffusionGemma's
  * Technical Architecture": 8 of 128 experts active): idx int32 [rows, k]
  * ordered (logit desc, expert asc); gates float [rows, k] = softmax over the
@@ -263,6 +332,14 @@ dg_status dg_k_lm_head(dg_ctx* ctx, int32_t batch, const void* h, float* logits)
  * tied embedding and LM head; the output distribution judges which tokens
  * are final). */
 dg_status dg_k_lm_argmax(dg_ctx* ctx, int32_t batch, const void* h, int32_t* pred, float* conf);
+
+/* EB statistics of the tied LM head as an EB pass runs it (bf16 contexts:
+ * fused, the logits never reach memory): h T [batch*N, H] -> pred int32,
+ * entropy float, sample int32 [batch*N] for pass t of at most t_max with the
+ * noise key (seeds_host[b], block) (see the EB section above). */
+dg_status dg_k_lm_sample(dg_ctx* ctx, int32_t batch, const void* h, int32_t t, int32_t t_max,
+                         const uint32_t* seeds_host, uint32_t block, int32_t* pred, float* entropy,
+                         int32_t* sample);
 
 /* ---- kernel timing ----------------------------------------------------------
  * Per-launch device durations of selected kernel classes.  dg_profile(ctx,

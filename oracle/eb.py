@@ -261,14 +261,40 @@ def eb_set_plausible(H: np.ndarray, d: np.ndarray, free: np.ndarray, g: np.ndarr
     return True
 
 
+def eb_apply(H: np.ndarray, xs: np.ndarray, pred: np.ndarray, tokens: np.ndarray, locked: np.ndarray, t: int,
+             t_max: int, prev_pred: Optional[np.ndarray], sel: Optional[np.ndarray] = None,
+             stop: Optional[bool] = None):
+    """The lock step of one canvas that is not done, from its entropies ``H``,
+    samples ``xs`` and greedy tokens ``pred`` ``[N]``: the EB locks (every
+    unlocked position at the last pass), then the stop rule against the
+    previous pass's greedy tokens ``prev_pred`` (None before the first pass).
+    ``sel`` / ``stop`` replace the rule's own decisions (shadowed
+    comparison).  Returns new ``(tokens, locked)``, the positions the EB rule
+    locked, the stop flag and whether the canvas is done."""
+    tokens, locked = tokens.copy(), locked.copy()
+    free = np.nonzero(locked == 0)[0]
+    if stop is None:
+        stable = prev_pred is not None and bool(np.array_equal(prev_pred, pred))
+        stop = bool(stable and mean_entropy32(H) < np.float32(STOP_ENTROPY))
+    if sel is None:
+        sel = free if t >= t_max - 1 else eb_select(H, free)
+    tokens[sel] = xs[sel]
+    locked[sel] = 1
+    if stop:
+        rest = np.nonzero(locked == 0)[0]
+        tokens[rest] = pred[rest]
+        locked[rest] = 1
+    return tokens, locked, sel, stop, bool(stop or locked.all())
+
+
 def eb_update(logits: np.ndarray, tokens: np.ndarray, locked: np.ndarray, t: int, state: EBState,
               seeds: Sequence[int], block: int = 0, t_max: int = T_MAX, shadow: Optional[EBShadow] = None):
     """The sampler's step after the LM head, for ``B`` canvases.
 
     ``logits [B, N, V]``; ``tokens, locked [B, N]``.  Canvases already done
     are left as they are.  Returns new ``(tokens, locked)`` and a dict of the
-    pass's per-canvas values (H, sample, pred, the positions locked, the stop
-    flag)."""
+    pass's per-canvas values (H, sample, pred, the positions the EB rule
+    locked, the stop flag)."""
     B, N, V = logits.shape
     tau = temperature(t, t_max)
     tokens, locked = tokens.copy(), locked.copy()
@@ -284,7 +310,7 @@ def eb_update(logits: np.ndarray, tokens: np.ndarray, locked: np.ndarray, t: int
             d = entropy_slack(lb, tau, shadow.dlogit) + 1e-6 * (1.0 + H)
             if shadow.sample is not None:
                 score = sample_scores(lb, tau, noise).astype(np.float64)
-                slack = shadow.dlogit / tau + 4e-7 * (1.0 + float(np.abs(score).max()))
+                slack = shadow.dlogit / tau + 2e-6 * (1.0 + float(np.abs(score).max()))
                 xs = _adopt_argmax(score, xs, shadow.sample[b], slack, "sample", b, shadow)
             if shadow.pred is not None:
                 pred = _adopt_argmax(lb, pred, shadow.pred[b], shadow.dlogit, "pred", b, shadow)
@@ -295,9 +321,9 @@ def eb_update(logits: np.ndarray, tokens: np.ndarray, locked: np.ndarray, t: int
             info["selected"].append(np.zeros(0, dtype=np.int64))
             info["stopped"].append(False)
             continue
-        free = np.nonzero(locked[b] == 0)[0]
         prev = state.prev_pred[b]
         state.prev_pred[b] = pred
+        free = np.nonzero(locked[b] == 0)[0]
         stable = prev is not None and bool(np.array_equal(prev, pred))
         stop = bool(stable and mean_entropy32(H) < np.float32(STOP_ENTROPY))
         if shadow is not None and shadow.stopped is not None and bool(shadow.stopped[b]) != stop:
@@ -307,26 +333,18 @@ def eb_update(logits: np.ndarray, tokens: np.ndarray, locked: np.ndarray, t: int
                 stop = bool(shadow.stopped[b])
             else:
                 shadow.failures.append(f"stop canvas {b} pass {t}: gpu {bool(shadow.stopped[b])} oracle {stop}")
-        if t >= t_max - 1:
-            sel = free
-        else:
-            sel = eb_select(H, free)
-            if shadow is not None and shadow.locked_after is not None and not stop:
-                g = np.nonzero((shadow.locked_after[b] == 1) & (locked[b] == 0))[0]
-                if set(g.tolist()) != set(sel.tolist()):
-                    if eb_set_plausible(H, d, free, g):
-                        shadow.adopted["lock"] += 1
-                        sel = g
-                    else:
-                        shadow.failures.append(f"EB lock set canvas {b} pass {t}")
-        tokens[b, sel] = xs[sel]
-        locked[b, sel] = 1
-        if stop:
-            rest = np.nonzero(locked[b] == 0)[0]
-            tokens[b, rest] = pred[rest]
-            locked[b, rest] = 1
-        if stop or bool(locked[b].all()):
-            state.done[b] = True
+        sel = free if t >= t_max - 1 else eb_select(H, free)
+        if shadow is not None and shadow.locked_after is not None and not stop and t < t_max - 1:
+            g = np.nonzero((shadow.locked_after[b] == 1) & (locked[b] == 0))[0]
+            if set(g.tolist()) != set(sel.tolist()):
+                if eb_set_plausible(H, d, free, g):
+                    shadow.adopted["lock"] += 1
+                    sel = g
+                else:
+                    shadow.failures.append(f"EB lock set canvas {b} pass {t}")
+        tokens[b], locked[b], sel, stop, done = eb_apply(H, xs, pred, tokens[b], locked[b], t, t_max, prev,
+                                                         sel=sel, stop=stop)
+        state.done[b] = done
         info["selected"].append(sel)
         info["stopped"].append(stop)
     return tokens, locked, info

@@ -107,6 +107,10 @@ class Workload:
     # std close to router_std * sqrt(hidden)
     router_std: float = 0.02
     kv_std: float = 1.0
+    # added to every final-norm weight w (the norm scales by 1 + w): a value
+    # of g - 1 scales the logits by about g, sharpening the output
+    # distribution (low-entropy workloads for the entropy-bounded sampler)
+    final_norm_shift: float = 0.0
     # number of positions pre-locked per canvas (len == batch)
     prelock: Tuple[int, ...] = field(default=())
     description: str = ""

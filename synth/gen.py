@@ -25,7 +25,7 @@ from typing import Dict, Tuple
 
 import numpy as np
 
-from .configs import BF16, Workload
+from .configs import BF16, F32, Workload
 
 CHUNK = 1 << 22
 
@@ -130,7 +130,10 @@ def embed(w: Workload) -> np.ndarray:
 
 def norm_final(w: Workload) -> np.ndarray:
     m = w.model
-    return normal(w.seed, 0, NORM_FINAL, 0, (m.hidden,), w.weight_std, m.dtype)
+    if not w.final_norm_shift:
+        return normal(w.seed, 0, NORM_FINAL, 0, (m.hidden,), w.weight_std, m.dtype)
+    x = normal(w.seed, 0, NORM_FINAL, 0, (m.hidden,), w.weight_std, F32) + np.float32(w.final_norm_shift)
+    return f32_to_bf16_bits(x) if m.dtype == BF16 else x
 
 
 def prompt_kv(w: Workload, layer: int, canvas: int) -> Tuple[np.ndarray, np.ndarray]:

@@ -101,3 +101,33 @@ def test_context_calls_reject_null_context():
     assert L.dg_denoise_step(None, 1, None, None, None, None, None) == dg.DG_EINVAL
     assert L.dg_generate_block(None, 1, 8, None, None) == dg.DG_EINVAL
     assert L.dg_destroy(None) == dg.DG_OK
+
+
+def test_eb_entry_points_validate_on_the_host():
+    L = dg.lib()
+    fake = ctypes.c_void_p(16)
+    seeds = (ctypes.c_uint32 * 2)(1, 2)
+    # missing outputs / seeds, pass outside [0, t_max), rows not a multiple of the canvas
+    assert L.dg_k_eb_rows(fake, 64, 128, 32, 0, 48, seeds, 0, None, fake, fake, None) == dg.DG_EINVAL
+    assert L.dg_k_eb_rows(fake, 64, 128, 32, 0, 48, None, 0, fake, fake, fake, None) == dg.DG_EINVAL
+    assert L.dg_k_eb_rows(fake, 64, 128, 32, 48, 48, seeds, 0, fake, fake, fake, None) == dg.DG_EINVAL
+    assert L.dg_k_eb_rows(fake, 65, 128, 32, 0, 48, seeds, 0, fake, fake, fake, None) == dg.DG_EINVAL
+    assert L.dg_k_eb_rows(fake, 65 * 32, 128, 32, 0, 48, seeds, 0, fake, fake, fake, None) == dg.DG_EINVAL
+    assert L.dg_k_eb_noise(64, 128, 32, 0, seeds, 0, None, None) == dg.DG_EINVAL
+    assert L.dg_k_eb_noise(64, 128, 32, -1, seeds, 0, fake, None) == dg.DG_EINVAL
+    assert L.dg_k_eb_select(1, 8, fake, fake, fake, fake, fake, None, fake, 0, 48, None) == dg.DG_EINVAL
+    assert L.dg_k_eb_select(1, 8, fake, fake, fake, fake, fake, fake, fake, -1, 48, None) == dg.DG_EINVAL
+    assert L.dg_k_eb_select(1, 8, fake, fake, fake, fake, fake, fake, fake, 0, 0, None) == dg.DG_EINVAL
+    assert L.dg_k_eb_select(65, 8, fake, fake, fake, fake, fake, fake, fake, 0, 48, None) == dg.DG_EINVAL
+    # empty work is a no-op with NULL pointers
+    assert L.dg_k_eb_rows(None, 0, 128, 32, 0, 48, None, 0, None, None, None, None) == dg.DG_OK
+    assert L.dg_k_eb_select(0, 8, None, None, None, None, None, None, None, 0, 48, None) == dg.DG_OK
+
+
+def test_eb_context_calls_reject_null_context():
+    L = dg.lib()
+    seeds = (ctypes.c_uint32 * 1)(1)
+    passes = (ctypes.c_int32 * 1)()
+    assert L.dg_eb_step(None, 1, None, None, 0, 48, seeds, 0, None, None, None, None, None) == dg.DG_EINVAL
+    assert L.dg_generate_block_eb(None, 1, None, None, seeds, 0, 48, passes) == dg.DG_EINVAL
+    assert L.dg_k_lm_sample(None, 1, None, 0, 48, seeds, 0, None, None, None) == dg.DG_EINVAL
