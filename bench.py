@@ -12,7 +12,10 @@ passes, so every lock count of a block is exercised.
 Prints one JSON line: canvas tokens/s per pass as ``value``, the resolved
 tokens/s of whole blocks, the roofline of the dominant kernel (the grouped
 gate|up expert GEMM, timed with HIP events on the library's stream) and the
-CPU oracle's rate on a bounded sample of the same workload.
+CPU oracle's rate on a bounded sample of the same workload.  ``eb_sampler``
+adds the entropy-bounded variant of the same workload: the pass time with
+the sampler head (temperature, entropy, Gumbel-max sample) and the EB lock
+step, and whole blocks that stop adaptively within 48 passes.
 """
 from __future__ import annotations
 
@@ -188,6 +191,8 @@ def main():
     ap.add_argument("--blocks", type=int, default=2, help="whole blocks timed for resolved tok/s")
     ap.add_argument("--breakdown-steps", type=int, default=4,
                     help="extra passes after the timed region with every kernel class timed")
+    ap.add_argument("--eb-blocks", type=int, default=1,
+                    help="whole entropy-bounded blocks timed (at most 48 passes each)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe-copy-mib", type=int, default=0,
                     help="only run 4 device copies of this many MiB (calibrates HBM byte counters) and exit")
@@ -310,6 +315,50 @@ def main():
     block_med = float(np.median(block_ms)) if block_ms else float("nan")
     resolved = newly / (block_med / 1e3) if block_ms else float("nan")
 
+    # entropy-bounded sampler: passes with the sampler head and the EB lock
+    # step (timed alone, then with the LM head's launches timed), and whole
+    # blocks that stop adaptively (one host read of the canvases' status per pass)
+    eb_res = None
+    if args.eb_blocks > 0:
+        seeds = [1000 + b for b in range(B)]
+        prev = torch.zeros((B, N), dtype=torch.int32, device=dev)
+        status = torch.zeros(B, dtype=torch.int32, device=dev)
+        eb_steps = min(args.steps, 8)
+
+        def eb_run(k):
+            tokens.copy_(tok0_d)
+            locked.copy_(lk0_d)
+            status.zero_()
+            for t in range(k):
+                ctx.eb_step(tokens, locked, t, 48, seeds, 0, prev, status)
+
+        eb_run(2)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        eb_run(eb_steps)
+        torch.cuda.synchronize()
+        eb_pass_ms = (time.perf_counter() - t0) * 1e3 / eb_steps
+        ctx.profile([bd.PROF_LM_HEAD])
+        eb_run(eb_steps)
+        torch.cuda.synchronize()
+        ctx.profile(())
+        n_lm, ms_lm = ctx.profile_read(bd.PROF_LM_HEAD)
+        eb_block_ms, eb_passes = [], None
+        for _ in range(args.eb_blocks):
+            tokens.copy_(tok0_d)
+            locked.copy_(lk0_d)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            eb_passes = ctx.generate_block_eb(tokens, locked, seeds, 0, 48)
+            torch.cuda.synchronize()
+            eb_block_ms.append((time.perf_counter() - t0) * 1e3)
+            assert bool(locked.all()), "EB block left unlocked positions"
+        eb_med = float(np.median(eb_block_ms))
+        eb_res = {"t_max": 48, "passes": eb_passes, "pass_ms": round(eb_pass_ms, 4),
+                  "canvas_tok_s": round(M / (eb_pass_ms / 1e3), 1),
+                  "lm_head_sampler_us": round(ms_lm / max(n_lm, 1) * 1e3, 2),
+                  "block_ms": round(eb_med, 3), "resolved_tok_s": round(newly / (eb_med / 1e3), 1)}
+
     # block continuation: commit the resolved canvases to the prompt caches
     # (causal pass over the block + K/V append).  The first commit also sets
     # up the buffers the caches move between; the second is timed.  Last, as
@@ -370,6 +419,7 @@ def main():
                           "hbm_frac": round(byts / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                           "mfma_frac": round(flops / (ms_per_step / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
         "kernels_breakdown": kern,
+        "eb_sampler": eb_res,
         "experts_touched_min": min(touched),
         "init_s": round(init_s, 1),
     }

@@ -113,15 +113,20 @@ def gumbel_noise(seed: int, block: int, t: int, positions: Sequence[int], V: int
     v = np.arange(V, dtype=np.uint64)
     call = (v >> np.uint64(6)) * np.uint64(16) + (v & np.uint64(15))
     word = ((v >> np.uint64(4)) & np.uint64(3)).astype(np.int64)
-    pos = np.asarray(positions, dtype=np.uint64)
-    ctr = np.zeros((pos.size, V, 4), dtype=np.uint64)
-    ctr[..., 0] = call[None, :]
-    ctr[..., 1] = pos[:, None]
-    ctr[..., 2] = np.uint64(t)
-    out = philox4(ctr, (seed, block), bits=32)
-    bits = np.take_along_axis(out, word[None, :, None], axis=2)[..., 0]
-    u = uniform_from_bits(bits).astype(np.float64)
-    return (-np.log(-np.log(u))).astype(np.float32)
+    pos = np.asarray(positions, dtype=np.uint64).reshape(-1)
+    g = np.empty((pos.size, V), dtype=np.float32)
+    step = max(1, (1 << 22) // max(V, 1))  # positions per chunk, to bound the memory
+    for p0 in range(0, pos.size, step):
+        pc = pos[p0:p0 + step]
+        ctr = np.zeros((pc.size, V, 4), dtype=np.uint64)
+        ctr[..., 0] = call[None, :]
+        ctr[..., 1] = pc[:, None]
+        ctr[..., 2] = np.uint64(t)
+        out = philox4(ctr, (seed, block), bits=32)
+        bits = np.take_along_axis(out, word[None, :, None], axis=2)[..., 0]
+        u = uniform_from_bits(bits).astype(np.float64)
+        g[p0:p0 + step] = -np.log(-np.log(u))
+    return g
 
 
 # --------------------------------------------------------------------------

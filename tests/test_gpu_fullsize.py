@@ -21,6 +21,7 @@ import numpy as np
 import pytest
 
 from gpu_util import DELTA_REL, TOL, host64, needs_gpu, rel_err, run_block_stepwise, say, shadow_compare
+from oracle import eb
 from oracle import model as om
 from oracle.inputs import prompt_kv_fn, weights_for
 from synth import C3, C4, C5, gen, upload
@@ -206,6 +207,86 @@ def test_c3_fused_argmax_equals_row_reduction(torch, c3ctx):
     e = float(np.max(np.abs(c - c2) / c2))
     print(f"C3 fused argmax: pred equal, conf rel diff {e:.3e}")
     assert e <= 1e-6
+
+
+def test_c3_fused_sampler_on_its_own_logits(torch, c3ctx):
+    # the fused LM head's sampler statistics over the 262144-entry vocabulary
+    # against the oracle's on the same kernel's logits: greedy ids exactly,
+    # entropies of every row, samples of sampled rows
+    w = C3
+    m = w.model
+    M = w.batch * m.canvas_len
+    say("C3 fused sampler")
+    h = upload.to_device(gen.activations(27, 1, (M, m.hidden), std=1.0, dtype="bf16"), "bf16")
+    logits = torch.empty((M, m.vocab), dtype=torch.float32, device="cuda")
+    pred = torch.empty(M, dtype=torch.int32, device="cuda")
+    ent = torch.empty(M, dtype=torch.float32, device="cuda")
+    samp = torch.empty(M, dtype=torch.int32, device="cuda")
+    t, t_max, seeds = 5, eb.T_MAX, [2024]
+    c3ctx.k_lm_head(w.batch, h, logits)
+    c3ctx.k_lm_sample(w.batch, h, t, t_max, seeds, 1, pred, ent, samp)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    assert np.array_equal(pred.cpu().numpy(), np.argmax(lg, axis=1))
+    tau = eb.temperature(t, t_max)
+    H = eb.entropy(lg.astype(np.float64), tau)
+    herr = np.abs(ent.cpu().numpy().astype(np.float64) - H)
+    print(f"C3 fused sampler: entropy max |err| {herr.max():.3e} (H {H.min():.3f}..{H.max():.3f})")
+    assert np.all(herr <= 2e-5 * (1.0 + H))
+    rows = np.array([0, 3, 64, 100, 129, 200, 254, 255])
+    noise = eb.gumbel_noise(seeds[0], 1, t, rows, m.vocab)
+    score = eb.sample_scores(lg[rows].astype(np.float64), tau, noise).astype(np.float64)
+    got = samp.cpu().numpy()[rows]
+    mine = np.argmax(score, axis=1)
+    for j in np.nonzero(mine != got)[0]:
+        assert score[j, mine[j]] - score[j, got[j]] <= 4e-6 * (1.0 + abs(score[j, mine[j]])), (rows[j],)
+    print(f"C3 fused sampler: {int((mine == got).sum())}/{rows.size} sampled rows identical")
+
+
+def test_c3_eb_pass_matches_oracle(torch, c3ctx):
+    # one entropy-bounded pass of the full stack against the oracle, decisions shadowed
+    w = C3
+    m = w.model
+    B, N, L = w.batch, m.canvas_len, m.n_layers
+    say("C3 EB pass")
+    tok0, lk0 = gen.canvas(w)
+    tokens = torch.from_numpy(tok0).cuda()
+    locked = torch.from_numpy(lk0).cuda()
+    prev = torch.zeros((B, N), dtype=torch.int32, device="cuda")
+    status = torch.zeros(B, dtype=torch.int32, device="cuda")
+    ent = torch.empty((B, N), dtype=torch.float32, device="cuda")
+    samp = torch.empty((B, N), dtype=torch.int32, device="cuda")
+    pred = torch.empty((B, N), dtype=torch.int32, device="cuda")
+    trace = torch.empty((L, B * N, m.top_k), dtype=torch.int32, device="cuda")
+    seeds = [99]
+    c3ctx.set_trace(trace)
+    c3ctx.eb_step(tokens, locked, 0, eb.T_MAX, seeds, 0, prev, status, ent, samp, pred)
+    torch.cuda.synchronize()
+    c3ctx.set_trace(None)
+    tol = _stack_tolerance()
+    tr = trace.cpu().numpy()
+    W = _oracle_weights(w, cache_layers=True)
+    kvf = prompt_kv_fn(w)
+    sh = om.Shadow(route_idx=[tr[l] for l in range(L)], delta_route=tol)
+    x = W.embed_rows(tok0.reshape(-1).astype(np.int64)).copy()
+    x = om.forward_hidden(x, W, m, kvf, [w.prompt_len], shadow=sh)
+    hh = om.bf16_round(om.rmsnorm(x, W.norm_final(), m.rms_eps))
+    lg = om.lm_logits(hh, W.embed()).reshape(B, N, -1)
+    assert not sh.failures, sh.failures[:5]
+    H = eb.entropy(lg[0], eb.temperature(0))
+    g_ent = ent.cpu().numpy()[0].astype(np.float64)
+    herr = float(np.max(np.abs(g_ent - H) / H))
+    rms = float(np.sqrt(np.mean(lg ** 2)))
+    esh = eb.EBShadow(sample=samp.cpu().numpy(), pred=pred.cpu().numpy(), locked_after=locked.cpu().numpy(),
+                      stopped=(status.cpu().numpy() & 4) != 0, dlogit=tol * max(1.0, rms))
+    state = eb.EBState(B)
+    t_o, l_o, info = eb.eb_update(lg, tok0, lk0, 0, state, seeds, 0, eb.T_MAX, shadow=esh)
+    print(f"C3 EB pass: entropy rel err {herr:.3e}, routing adopted {sh.adopted['route']}, "
+          f"decisions adopted {esh.adopted}, locked {[len(s) for s in info['selected']]}")
+    assert not esh.failures, esh.failures[:5]
+    assert herr <= tol
+    assert np.array_equal(tokens.cpu().numpy(), t_o)
+    assert np.array_equal(locked.cpu().numpy(), l_o)
 
 
 def test_c3_moe_sampled_tokens(torch, c3ctx):
