@@ -20,6 +20,7 @@ def weights_for(w, cache_layers: bool = False) -> OracleWeights:
         embed_raw=gen.embed(w) if m.has_lm_head else None,
         norm_final_raw=gen.norm_final(w) if m.has_lm_head else None,
         cache_layers=cache_layers,
+        expert_format=getattr(m, "expert_format", "native"),
     )
 
 

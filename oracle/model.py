@@ -258,18 +258,30 @@ def _to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
 _EXPERT_STACKS = ("w_gate", "w_up", "w_down")
 
 
+_SHARED = ("sh_gate", "sh_up", "sh_down")
+
+
+def _expert_values(a: np.ndarray, expert_format: str) -> np.ndarray:
+    """The values an expert matrix ``[in, out]`` stands for in its stored
+    format: itself, or its MXFP4 quantisation along ``in``."""
+    if expert_format == "mxfp4":
+        from .quant import mxfp4_weight
+        return mxfp4_weight(a)
+    return a
+
+
 class _ExpertStack:
     """``[E, in, out]`` expert weights kept in their stored form; indexing one
     expert returns its float64 matrix."""
 
-    def __init__(self, raw: np.ndarray, dtype: str):
-        self.raw, self.dtype, self.shape = raw, dtype, raw.shape
+    def __init__(self, raw: np.ndarray, dtype: str, expert_format: str = "native"):
+        self.raw, self.dtype, self.shape, self.fmt = raw, dtype, raw.shape, expert_format
 
     def __getitem__(self, e: int) -> np.ndarray:
-        return _to_f64(self.raw[e], self.dtype)
+        return _expert_values(_to_f64(self.raw[e], self.dtype), self.fmt)
 
     def __array__(self, dtype=None, copy=None):
-        a = _to_f64(self.raw, self.dtype)
+        a = np.stack([self[e] for e in range(self.shape[0])])
         return a if dtype is None else a.astype(dtype)
 
 
@@ -288,14 +300,23 @@ class OracleWeights:
     _embed: Optional[np.ndarray] = None
     _cache: Dict[int, Dict[str, np.ndarray]] = field(default_factory=dict)
     cache_layers: bool = False
+    # storage of the routed and shared experts' matrices: "native" (dtype) or
+    # "mxfp4" (quantised along the input dimension, see quant.py)
+    expert_format: str = "native"
 
     def layer(self, l: int) -> Dict[str, np.ndarray]:
         if l in self._cache:
             return self._cache[l]
         raw = self.layer_fn(l)
         # per-expert stacks are widened one expert at a time, when an expert is used
-        out = {k: (_ExpertStack(v, self.dtype) if k in _EXPERT_STACKS else _to_f64(v, self.dtype))
-               for k, v in raw.items()}
+        out = {}
+        for k, v in raw.items():
+            if k in _EXPERT_STACKS:
+                out[k] = _ExpertStack(v, self.dtype, self.expert_format)
+            elif k in _SHARED:
+                out[k] = _expert_values(_to_f64(v, self.dtype), self.expert_format)
+            else:
+                out[k] = _to_f64(v, self.dtype)
         if self.cache_layers:
             self._cache[l] = out
         return out

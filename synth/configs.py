@@ -53,6 +53,9 @@ class ModelConfig:
     # norm of the MoE output before the residual add (symmetric with the
     # post-attention norm)
     post_ffn_norm: bool = True
+    # storage of the routed and shared experts' matrices: "native" (dtype) or
+    # "mxfp4" (4-bit blocks of 32 along the input dimension, bf16 only)
+    expert_format: str = "native"
 
     def is_global(self, layer: int) -> bool:
         return bool((self.global_layer_mask >> layer) & 1)
