@@ -27,7 +27,7 @@ class DGConfig(ctypes.Structure):
         ("expert_ffn", c_int32), ("vocab", c_int32), ("canvas_len", c_int32), ("window", c_int32),
         ("max_batch", c_int32), ("max_prompt_len", c_int32), ("global_layer_mask", c_uint64),
         ("rope_theta", c_float), ("prope_frac", c_float), ("rms_eps", c_float), ("dtype", c_int32),
-        ("has_lm_head", c_int32), ("post_ffn_norm", c_int32),
+        ("has_lm_head", c_int32), ("post_ffn_norm", c_int32), ("expert_format", c_int32),
     ]
 
 
@@ -63,6 +63,7 @@ _SIGS = {
     "dg_generate_block_eb": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, POINTER(ctypes.c_uint32),
                                        ctypes.c_uint32, c_int32, POINTER(c_int32)]),
     "dg_get_prompt_kv": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
+    "dg_get_expert_weight": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
     "dg_forward_hidden": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p]),
     "dg_forward_layers": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_void_p, c_void_p]),
     "dg_set_trace": (c_int32, [c_void_p, c_void_p]),
@@ -90,6 +91,7 @@ _SIGS = {
 }
 
 PROF_GATE_UP, PROF_DOWN, PROF_ATTN, PROF_LM_HEAD, PROF_PASS, PROF_COUNT = range(6)
+EXPERT_FORMATS = {"native": 0, "mxfp4": 1}
 PROF_KEEP = 1 << 30
 
 
@@ -162,6 +164,10 @@ def make_config(model, max_batch: int, max_prompt_len: int) -> DGConfig:
     c.dtype = DG_BF16 if model.dtype == "bf16" else DG_F32
     c.has_lm_head = int(bool(model.has_lm_head))
     c.post_ffn_norm = int(bool(model.post_ffn_norm))
+    fmt = getattr(model, "expert_format", "native")
+    if fmt not in EXPERT_FORMATS:
+        raise ValueError(f"expert_format {fmt!r} is not one of {sorted(EXPERT_FORMATS)}")
+    c.expert_format = EXPERT_FORMATS[fmt]
     return c
 
 
@@ -290,6 +296,13 @@ class Context:
         """Copy the slot's cache of one layer into ``k, v [len, Hkv, D]``."""
         self._c(lib().dg_get_prompt_kv(self._h, slot, layer, _ptr(k, self.wdtype, "k"),
                                        _ptr(v, self.wdtype, "v"), None))
+
+    def get_expert_weight(self, layer: int, expert: int, which: int, values=None, codes=None, scales=None):
+        """One expert matrix as the GEMMs use it (dg_get_expert_weight): which
+        0 gate [H, F], 1 up [H, F], 2 down [F, H]; MXFP4 codes / scales too."""
+        import torch
+        self._c(lib().dg_get_expert_weight(self._h, layer, expert, which, _ptr(values, self.wdtype, "values"),
+                                           _ptr(codes, torch.uint8, "codes"), _ptr(scales, torch.uint8, "scales")))
 
     def forward_hidden(self, x_in, x_out):
         import torch

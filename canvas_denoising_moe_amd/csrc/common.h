@@ -98,6 +98,27 @@ hipError_t launch_pack(int is_bf16, const PackArgs& a, hipStream_t s);
 hipError_t launch_pack_batched(int is_bf16, const PackArgs& a, int nbatch, long long src_bs,
                                long long dst_bs, hipStream_t s);
 
+// MXFP4 (OCP microscaling, 4-bit E2M1 elements, one E8M0 scale per 32
+// consecutive k of a column) from packed bf16 fragments [NB][KB][64][8]
+// (batch stride src_bs elements).  With KG = ceil(KB / 4):
+//   codes  uint32 [batch][NB][KG][64 lanes][4]: word j of a lane holds the 8
+//          codes of k-step 4 kg + j in the lane's fragment order, element e in
+//          bits 4e..4e+3 (so one 16-byte load feeds four k-steps);
+//   scales uint8  [batch][NB][KG][16 columns][4]: byte j = s + 127 of k-step
+//          4 kg + j of that column.
+// k-steps past KB hold zero codes and scale 2^0.
+hipError_t launch_quant_mxfp4(const void* packed, int nbatch, long long src_bs, int NB, int KB, uint4* codes,
+                              uint8_t* scales, hipStream_t s);
+// The weights a packed expert operand stands for, back in math layout
+// [K, N] (T): packed bf16/fp32 fragments (codes == NULL) or MXFP4 codes and
+// scales decoded with the streaming GEMM's own conversion (codes_out [K, N]
+// and scales_out [K/32, N] receive the raw codes and scale bytes).  colmap 2:
+// the gate|up interleave, half selects up (1) or gate (0) and N is F.  Any
+// output may be NULL.
+hipError_t launch_unpack_weight(int is_bf16, const void* packed, const uint4* codes, const uint8_t* scales, int K,
+                                int N, int colmap, int half, void* out, uint8_t* codes_out, uint8_t* scales_out,
+                                hipStream_t s);
+
 // Generic skinny GEMM on matrix cores; see gemm.hip for the arguments.
 struct GemmArgs {
   const void* A; long long lda;
@@ -140,6 +161,11 @@ struct StreamArgs {
   // split-K (fp32-store epilogue only): K/32 % ksplit == 0; split s writes its
   // partial sums at out + s * split_stride
   int ksplit; long long split_stride;
+  // qb = 1: B in MXFP4 (bf16 contexts): codes Bq and scales Bs in the layout
+  // of launch_quant_mxfp4, group strides in uint4 / uint32 units
+  int qb;
+  const uint4* Bq; long long bq_group_stride;
+  const uint32_t* Bs; long long bs_group_stride;
 };
 hipError_t launch_stream(int is_bf16, const StreamArgs& g, const EpiArgs& e, hipStream_t s,
                          KTime t = {});

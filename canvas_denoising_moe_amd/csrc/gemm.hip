@@ -27,6 +27,15 @@
 // fp32 workloads use the same packing and loop with 16x16x4 fp32 MFMAs (8 per
 // 32-wide k-step); lanes feed matching k indices to A and B, so the sum is the
 // plain dot product.
+//
+// Expert weights may instead be stored as MXFP4 (OCP microscaling: 4-bit E2M1
+// elements sharing one E8M0 scale per 32 consecutive k of a column), the
+// gfx950-native analogue of the 4-bit builds the pages list ([Experimental]
+// and [ParadigmShift] "Serving in Production": GGUF Q4_K_M, NVFP4).  The
+// stream then moves a quarter of the bytes: one 16-byte load per lane carries
+// the fragments of four k-steps, and v_cvt_scalef32_pk_bf16_fp4 turns them back
+// into exact bf16 fragments (every E2M1 value times a power of two is a bf16)
+// for the same bf16 MFMAs, activations staying bf16.
 #include "common.h"
 
 namespace {
@@ -75,6 +84,20 @@ DG_DEV void mma(floatx4& c, const Frag<float>& a, const Frag<float>& b) {
   c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.z, b.b.z, c, 0, 0, 0);
   c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.w, b.b.w, c, 0, 0, 0);
 }
+
+// One k-step's B fragment from MXFP4: the lane's 8 codes (element e in bits
+// 4e..4e+3) times 2^(sbyte - 127), converted two at a time.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+DG_DEV Frag<bf16_t> dq_fp4(uint32_t w, uint32_t sbyte) {
+  const float sc = __uint_as_float(sbyte << 23);
+  Frag<bf16_t> f;
+  f.v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
+  f.v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1));
+  f.v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2));
+  f.v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
+  return f;
+}
+DG_DEV uint32_t u4_at(const uint4& v, int j) { return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w; }
 
 DG_DEV float gelu_tanh(float z) {
   const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
@@ -345,11 +368,13 @@ constexpr int kStreamLdsKB = 32, kStreamLdsWideKB = 128;
 template <typename T, int MT, int R, int LK>
 constexpr int stream_kc() { return (LK * 1024 / (16 * MT * 32 * (int)sizeof(T))) / R * R; }  // k-steps per chunk
 
-template <typename T, int MT, int WN, int EPI, int R, int LK>
+template <typename T, int MT, int WN, int EPI, int R, int LK, int QB = 0>
 __global__ __launch_bounds__(256) void k_stream(StreamArgs g, EpiArgs e) {
   constexpr int ROWS = 16 * MT;
   constexpr int KC = stream_kc<T, MT, R, LK>();
   static_assert(KC % R == 0, "the register ring must tile an A chunk");
+  // MXFP4: every ring slot holds four k-steps, so chunks hold whole rounds of the ring
+  static_assert(QB == 0 || (sizeof(T) == 2 && KC % (4 * R) == 0), "MXFP4 ring rounds must tile an A chunk");
   static_assert(EPI != EPI_DOWN || sizeof(T) != 2 || 4 * ROWS * 16 * WN * 4 <= LK * 1024,
                 "the down output tiles must fit the LDS budget");
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -439,11 +464,37 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs g, EpiArgs e) {
     const int nb = min(nb0 + w, g.NB - 1);
     bptr[w] = Bg + ((long long)nb * KBall + kbase) * 512 + lane * 8;
   }
-  Frag<T> b[R][WN];
+  Frag<T> b[QB ? 1 : R][WN];
+  // MXFP4: slot i of the ring holds k-steps 4i..4i+3 of its round (codes, scales)
+  constexpr int RQ = QB ? R : 1;
+  const int KG = (KBall + 3) >> 2;
+  const uint4* qptr[WN];
+  const uint32_t* sptr[WN];
+  uint4 bq[RQ][WN];
+  uint32_t bsc[RQ][WN];
+  if constexpr (QB == 0) {
 #pragma unroll
-  for (int i = 0; i < R; ++i)
+    for (int i = 0; i < R; ++i)
 #pragma unroll
-    for (int w = 0; w < WN; ++w) b[i][w] = ld_frag<T>(bptr[w] + (long long)min(i, KB - 1) * 512);
+      for (int w = 0; w < WN; ++w) b[i][w] = ld_frag<T>(bptr[w] + (long long)min(i, KB - 1) * 512);
+  } else {
+    const uint4* Bq = g.Bq + (long long)group * g.bq_group_stride;
+    const uint32_t* Bs = g.Bs + (long long)group * g.bs_group_stride;
+#pragma unroll
+    for (int w = 0; w < WN; ++w) {
+      const int nb = min(nb0 + w, g.NB - 1);
+      qptr[w] = Bq + (long long)nb * KG * 64 + lane;
+      sptr[w] = Bs + (long long)nb * KG * 16 + (lane & 15);
+    }
+#pragma unroll
+    for (int i = 0; i < RQ; ++i)
+#pragma unroll
+      for (int w = 0; w < WN; ++w) {
+        const int kg = min(i, KG - 1);
+        bq[i][w] = qptr[w][(long long)kg * 64];
+        bsc[i][w] = sptr[w][(long long)kg * 16];
+      }
+  }
 
   if (tid < ROWS) {
     ar = ar < 0 ? 0 : (ar >= a_max ? a_max - 1 : ar);
@@ -541,24 +592,58 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs g, EpiArgs e) {
     // registers right behind the last MFMA, and those reads returned values
     // the MFMA had not yet written.
     const T* Ap = As + lane * 8;
-    for (int kb0 = kc0; kb0 < kc0 + nk; kb0 += R) {
+    if constexpr (QB == 0) {
+      for (int kb0 = kc0; kb0 < kc0 + nk; kb0 += R) {
 #pragma unroll
-      for (int i = 0; i < R; ++i) {
-        const int kb = kb0 + i;
-        const int kl = min(kb - kc0, nk - 1);
-        Frag<T> a[MT];
+        for (int i = 0; i < R; ++i) {
+          const int kb = kb0 + i;
+          const int kl = min(kb - kc0, nk - 1);
+          Frag<T> a[MT];
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          a[m] = ld_frag<T>(Ap + (kl * MT + m) * 512);
-          if (kb >= kc0 + nk) a[m] = zero_frag<T>();
+          for (int m = 0; m < MT; ++m) {
+            a[m] = ld_frag<T>(Ap + (kl * MT + m) * 512);
+            if (kb >= kc0 + nk) a[m] = zero_frag<T>();
+          }
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int w = 0; w < WN; ++w) mma(acc[m][w], a[m], b[i][w]);
+          const int kn = min(kb + R, KB - 1);
+#pragma unroll
+          for (int w = 0; w < WN; ++w) b[i][w] = ld_frag<T>(bptr[w] + (long long)kn * 512);
         }
+      }
+    } else {
+      // rounds of R slots x 4 k-steps; chunk starts are multiples of 4R, so slot
+      // i always holds k-group (kb0 / 4) + i; k-steps past K meet a zero A
+      // fragment (and zero codes in the padded k-group)
+      for (int kb0 = kc0; kb0 < kc0 + nk; kb0 += 4 * RQ) {
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
+        for (int i = 0; i < RQ; ++i) {
 #pragma unroll
-          for (int w = 0; w < WN; ++w) mma(acc[m][w], a[m], b[i][w]);
-        const int kn = min(kb + R, KB - 1);
+          for (int j = 0; j < 4; ++j) {
+            const int kb = kb0 + 4 * i + j;
+            const int kl = min(kb - kc0, nk - 1);
+            Frag<T> a[MT];
 #pragma unroll
-        for (int w = 0; w < WN; ++w) b[i][w] = ld_frag<T>(bptr[w] + (long long)kn * 512);
+            for (int m = 0; m < MT; ++m) {
+              a[m] = ld_frag<T>(Ap + (kl * MT + m) * 512);
+              if (kb >= kc0 + nk) a[m] = zero_frag<T>();
+            }
+#pragma unroll
+            for (int w = 0; w < WN; ++w) {
+              const Frag<bf16_t> bw = dq_fp4(u4_at(bq[i][w], j), (bsc[i][w] >> (8 * j)) & 0xFFu);
+#pragma unroll
+              for (int m = 0; m < MT; ++m) mma(acc[m][w], a[m], bw);
+            }
+          }
+          const int kgn = min((kb0 >> 2) + i + RQ, KG - 1);
+#pragma unroll
+          for (int w = 0; w < WN; ++w) {
+            bq[i][w] = qptr[w][(long long)kgn * 64];
+            bsc[i][w] = sptr[w][(long long)kgn * 16];
+          }
+        }
       }
     }
   }
@@ -636,10 +721,11 @@ int device_cus() {
   return cus[dev];
 }
 
-template <typename T, int MT, int WN, int EPI, int R, int LK>
+template <typename T, int MT, int WN, int EPI, int R, int LK, int QB = 0>
 hipError_t run_stream(const StreamArgs& g, const EpiArgs& e, hipStream_t s, KTime t) {
   const int ksplit = g.ksplit > 1 ? g.ksplit : 1;
   if (((g.K >> 5) % ksplit) != 0 || (ksplit > 1 && EPI != EPI_STORE_F32)) return hipErrorInvalidValue;
+  if (QB && (ksplit > 1 || !g.Bq || !g.Bs)) return hipErrorInvalidValue;
   if (g.ent_off && (ksplit > 1 || g.n_dense > 0 || g.n_groups < 1)) return hipErrorInvalidValue;
   const long long blocks = stream_blocks<WN>(g);
   if (blocks <= 0) return hipSuccess;
@@ -650,12 +736,12 @@ hipError_t run_stream(const StreamArgs& g, const EpiArgs& e, hipStream_t s, KTim
   static bool attr_set = false;  // one attribute call per instantiation
   if (!attr_set) {
     // the chunk plus the kernel's static LDS
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_stream<T, MT, WN, EPI, R, LK>),
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_stream<T, MT, WN, EPI, R, LK, QB>),
                                          hipFuncAttributeMaxDynamicSharedMemorySize, LK * 1024);
     if (err != hipSuccess) return err;
     attr_set = true;
   }
-  return launch_k(k_stream<T, MT, WN, EPI, R, LK>, dim3((unsigned)blocks), dim3(256), lds, s, t.start, t.stop,
+  return launch_k(k_stream<T, MT, WN, EPI, R, LK, QB>, dim3((unsigned)blocks), dim3(256), lds, s, t.start, t.stop,
                   g, e);
 }
 
@@ -671,6 +757,16 @@ hipError_t run_stream_dense(const StreamArgs& g, const EpiArgs& e, hipStream_t s
 
 template <typename T, int MT>
 hipError_t run_stream_mt(const StreamArgs& g, const EpiArgs& e, hipStream_t s, KTime t) {
+  if (g.qb) {
+    // MXFP4 experts: a ring slot holds four k-steps in a quarter of the bytes;
+    // 4 slots (16 k-steps, 8 KB per wave in flight) for gate|up, 2 for down
+    if constexpr (sizeof(T) == 2) {
+      if (e.kind == EPI_GEGLU) return run_stream<T, MT, 2, EPI_GEGLU, 4, kStreamLdsKB, 1>(g, e, s, t);
+      if (e.kind == EPI_DOWN)
+        return run_stream<T, MT, (MT == 2 ? 4 : 2), EPI_DOWN, (MT == 2 ? 2 : 4), kStreamLdsKB, 1>(g, e, s, t);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (e.kind) {
     case EPI_STORE_F32: return run_stream_dense<T, MT, EPI_STORE_F32>(g, e, s, t);
     case EPI_GEGLU: return run_stream<T, MT, 2, EPI_GEGLU, 8, kStreamLdsKB>(g, e, s, t);
@@ -723,6 +819,94 @@ __global__ void k_pack(PackArgs a, int nbatch, long long src_bs, long long dst_b
   }
 }
 
+// ----------------------------------------------------------------------------
+// MXFP4 quantisation of packed bf16 fragments (OCP Microscaling Formats v1.0
+// conversion: s = floor(log2 max|x|) - 2, clamped to [-126, 127]; each element
+// the E2M1 value nearest to x / 2^s, ties to the even mantissa, saturating at
+// 6).  One thread per (batch, n-block, k-group, k-step of the group, column):
+// the column's 32 values of that k-step sit in lanes c, c+16, c+32, c+48 of
+// the bf16 fragment, 8 each.
+// ----------------------------------------------------------------------------
+DG_DEV uint32_t e2m1_code(float v, int s) {
+  const float a = fabsf(ldexpf(v, -s));  // exact: a power-of-two scaling of a bf16
+  const uint32_t idx = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+                     : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
+  return idx | ((__float_as_uint(v) >> 31) << 3);
+}
+
+__global__ __launch_bounds__(256) void k_quant_mxfp4(const bf16_t* __restrict__ src, int nbatch, long long src_bs,
+                                                     int NB, int KB, uint32_t* codes, uint8_t* scales) {
+  const int KG = (KB + 3) >> 2;
+  const long long per = (long long)NB * KG * 64;  // threads per batch
+  const long long total = per * nbatch;
+  for (long long idx = blockIdx.x * (long long)blockDim.x + threadIdx.x; idx < total;
+       idx += (long long)gridDim.x * blockDim.x) {
+    const long long bi = idx / per;
+    long long o = idx - bi * per;
+    const int c = (int)(o & 15), j = (int)((o >> 4) & 3);
+    const long long nbkg = o >> 6;  // nb * KG + kg
+    const int kg = (int)(nbkg % KG), nb = (int)(nbkg / KG);
+    const int kb = kg * 4 + j;
+    uint32_t* cw = codes + (bi * per + nbkg * 64) * 4;  // [64 lanes][4]
+    uint8_t* sb = scales + bi * per + nbkg * 64;        // [16 columns][4]
+    if (kb >= KB) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) cw[(c + 16 * gq) * 4 + j] = 0u;
+      sb[c * 4 + j] = 127;
+      continue;
+    }
+    const bf16_t* f = src + bi * src_bs + ((long long)nb * KB + kb) * 512;
+    float v[4][8];
+    float amax = 0.f;
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[gq][e] = bf2f(f[(c + 16 * gq) * 8 + e]);
+        amax = fmaxf(amax, fabsf(v[gq][e]));
+      }
+    const int ex = (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127;  // floor(log2 amax) for normal amax
+    const int s = amax > 0.f ? min(max(ex - 2, -126), 127) : -126;
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      uint32_t wv = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wv |= e2m1_code(v[gq][e], s) << (4 * e);
+      cw[(c + 16 * gq) * 4 + j] = wv;
+    }
+    sb[c * 4 + j] = (uint8_t)(s + 127);
+  }
+}
+
+// Weight element (k, n) of a packed operand back in math layout.
+template <typename T>
+__global__ __launch_bounds__(256) void k_unpack_weight(const T* __restrict__ packed, const uint32_t* __restrict__ codes,
+                                                       const uint8_t* __restrict__ scales, int K, int N, int colmap,
+                                                       int half, T* out, uint8_t* codes_out, uint8_t* scales_out) {
+  const long long total = (long long)K * N;
+  const int KB = K >> 5, KG = (KB + 3) >> 2;
+  for (long long idx = blockIdx.x * (long long)blockDim.x + threadIdx.x; idx < total;
+       idx += (long long)gridDim.x * blockDim.x) {
+    const int k = (int)(idx / N), n = (int)(idx - (long long)k * N);
+    const int nb = colmap == 2 ? 2 * (n >> 4) + half : (n >> 4);
+    const int kb = k >> 5, lane = (n & 15) + 16 * ((k & 31) >> 3), e = k & 7;
+    float v;
+    if (codes) {
+      const int kg = kb >> 2, j = kb & 3;
+      const uint32_t w = codes[(((long long)nb * KG + kg) * 64 + lane) * 4 + j];
+      const uint32_t sbyte = scales[(((long long)nb * KG + kg) * 16 + (n & 15)) * 4 + j];
+      const Frag<bf16_t> f = dq_fp4(w, sbyte);
+      const uint32_t pair = u4_at(f.v, e >> 1);
+      v = bf2f((bf16_t)((e & 1) ? (pair >> 16) : (pair & 0xFFFF)));
+      if (codes_out) codes_out[idx] = (uint8_t)((w >> (4 * e)) & 15u);
+      if (scales_out && (k & 31) == 0) scales_out[(long long)kb * N + n] = (uint8_t)sbyte;
+    } else {
+      v = to_f<T>(packed[(((long long)nb * KB + kb) * 64 + lane) * 8 + e]);
+    }
+    if (out) out[idx] = from_f<T>(v);
+  }
+}
+
 template <typename T, int MT, int WN, int EPI>
 hipError_t run_gemm(const GemmArgs& g, const EpiArgs& e, hipStream_t s, KTime t) {
   constexpr int ROWS = MT * 16;
@@ -761,6 +945,35 @@ hipError_t launch_gemm(int is_bf16, const GemmArgs& g, const EpiArgs& e, int mt,
 
 hipError_t launch_stream(int is_bf16, const StreamArgs& g, const EpiArgs& e, hipStream_t s, KTime t) {
   return is_bf16 ? run_stream_t<bf16_t>(g, e, s, t) : run_stream_t<float>(g, e, s, t);
+}
+
+hipError_t launch_quant_mxfp4(const void* packed, int nbatch, long long src_bs, int NB, int KB, uint4* codes,
+                              uint8_t* scales, hipStream_t s) {
+  const long long total = (long long)NB * ((KB + 3) / 4) * 64 * nbatch;
+  if (total <= 0) return hipSuccess;
+  const long long want = (total + 255) / 256;
+  const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(k_quant_mxfp4, dim3(blocks), dim3(256), 0, s, reinterpret_cast<const bf16_t*>(packed), nbatch,
+                     src_bs, NB, KB, reinterpret_cast<uint32_t*>(codes), scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack_weight(int is_bf16, const void* packed, const uint4* codes, const uint8_t* scales, int K,
+                                int N, int colmap, int half, void* out, uint8_t* codes_out, uint8_t* scales_out,
+                                hipStream_t s) {
+  const long long total = (long long)K * N;
+  if (total <= 0) return hipSuccess;
+  if (codes && !is_bf16) return hipErrorInvalidValue;
+  const long long want = (total + 255) / 256;
+  const unsigned blocks = (unsigned)(want < 65536 ? want : 65536);
+  const uint32_t* cw = reinterpret_cast<const uint32_t*>(codes);
+  if (is_bf16)
+    hipLaunchKernelGGL(k_unpack_weight<bf16_t>, dim3(blocks), dim3(256), 0, s, reinterpret_cast<const bf16_t*>(packed),
+                       cw, scales, K, N, colmap, half, reinterpret_cast<bf16_t*>(out), codes_out, scales_out);
+  else
+    hipLaunchKernelGGL(k_unpack_weight<float>, dim3(blocks), dim3(256), 0, s, reinterpret_cast<const float*>(packed),
+                       cw, scales, K, N, colmap, half, reinterpret_cast<float*>(out), codes_out, scales_out);
+  return hipGetLastError();
 }
 
 hipError_t launch_pack(int is_bf16, const PackArgs& a, hipStream_t s) {

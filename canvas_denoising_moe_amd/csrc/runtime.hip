@@ -22,6 +22,9 @@ struct LayerW {
   void* router = nullptr;    // packed [E/16][H/32][64][8]
   void* gu = nullptr;   // (E+1) experts, packed gate|up interleave [2F/16][H/32][64][8]
   void* down = nullptr;  // (E+1) experts, packed [H/16][F/32][64][8]
+  // MXFP4 experts: gu / down hold the codes, these the scales (launch_quant_mxfp4 layout)
+  void* gu_s = nullptr;
+  void* down_s = nullptr;
   void* norm[4] = {nullptr, nullptr, nullptr, nullptr};  // in, pa, pf, pf2
   bool set = false;
 };
@@ -184,6 +187,15 @@ int work_cap(const dg_config& c, int M) {
 // range is cut into kRouterSplit slices to spread the stream over many
 // workgroups; the routing kernel adds the partial logits in slice order
 constexpr int kRouterSplit = 8;
+// MXFP4 expert storage: per expert, codes (bytes) and scales (bytes) of an
+// operand with NB n-blocks and K / 32 k-steps (k-groups of four, padded)
+struct QSize { long long codes, scales; };
+QSize mxfp4_size(long long NB, long long K) {
+  const long long KG = ((K >> 5) + 3) >> 2;
+  return QSize{NB * KG * 1024, NB * KG * 64};
+}
+bool mxfp4(const dg_config& c) { return c.expert_format == DG_EXPERT_MXFP4; }
+
 int router_split(const dg_config& c) { return ((c.hidden / 32) % kRouterSplit) == 0 ? kRouterSplit : 1; }
 int kv_len(const dg_config& c, int l, int prompt_len) {
   return is_global(c, l) ? prompt_len : (prompt_len < c.window ? prompt_len : c.window);
@@ -221,6 +233,10 @@ dg_status check_config(const dg_config* c) {
     return fail(ctx, DG_EUNSUPPORTED, "n_experts * ceil(max_batch*canvas_len/32) must be <= 16384");
   if (c->window < 0 || c->max_prompt_len < 0) return fail(ctx, DG_EINVAL, "window and max_prompt_len must be >= 0");
   if (c->dtype != DG_F32 && c->dtype != DG_BF16) return fail(ctx, DG_EINVAL, "dtype must be DG_F32 or DG_BF16");
+  if (c->expert_format != DG_EXPERT_NATIVE && c->expert_format != DG_EXPERT_MXFP4)
+    return fail(ctx, DG_EINVAL, "expert_format must be DG_EXPERT_NATIVE or DG_EXPERT_MXFP4");
+  if (c->expert_format == DG_EXPERT_MXFP4 && c->dtype != DG_BF16)
+    return fail(ctx, DG_EUNSUPPORTED, "MXFP4 experts need a DG_BF16 context");
   if (!(c->rope_theta > 0.f) || !(c->prope_frac >= 0.f && c->prope_frac <= 1.f) || !(c->rms_eps >= 0.f))
     return fail(ctx, DG_EINVAL, "rope_theta > 0, prope_frac in [0, 1] and rms_eps >= 0 required");
   return DG_OK;
@@ -388,6 +404,12 @@ dg_status enqueue_experts(dg_ctx* ctx, int l, int M, const void* f) {
   g.A = f; g.lda = H; g.a_rows = ctx->arows; g.a_rows_max = M;
   g.B = ctx->L[l].gu; g.b_group_stride = 2LL * F * H;
   g.K = H; g.NB = 2 * F / 16; g.mt = kStreamMT;
+  if (mxfp4(c)) {
+    const QSize q = mxfp4_size(g.NB, H);
+    g.qb = 1;
+    g.Bq = reinterpret_cast<const uint4*>(ctx->L[l].gu); g.bq_group_stride = q.codes / 16;
+    g.Bs = reinterpret_cast<const uint32_t*>(ctx->L[l].gu_s); g.bs_group_stride = q.scales / 4;
+  }
   g.work = ctx->work; g.work_count = ctx->work_count; g.work_cap = work_cap(c, M);
   g.ent_off = ctx->work_count + 1; g.n_groups = c.n_experts + 1;
   EpiArgs e{};
@@ -398,6 +420,12 @@ dg_status enqueue_experts(dg_ctx* ctx, int l, int M, const void* f) {
   d.A = ctx->u; d.lda = F; d.a_rows = nullptr;
   d.B = ctx->L[l].down; d.b_group_stride = (long long)F * H;
   d.K = F; d.NB = H / 16; d.mt = kStreamMT;
+  if (mxfp4(c)) {
+    const QSize q = mxfp4_size(d.NB, F);
+    d.qb = 1;
+    d.Bq = reinterpret_cast<const uint4*>(ctx->L[l].down); d.bq_group_stride = q.codes / 16;
+    d.Bs = reinterpret_cast<const uint32_t*>(ctx->L[l].down_s); d.bs_group_stride = q.scales / 4;
+  }
   // down keeps the tile-major order: its A rows (u) are few, and spreading the
   // concurrent weight reads over many experts streams faster here
   d.work = ctx->work; d.work_count = ctx->work_count; d.work_cap = work_cap(c, M);
@@ -677,8 +705,16 @@ dg_status dg_set_layer_weights(dg_ctx* ctx, int32_t layer, const dg_layer_weight
     TRY(dalloc(ctx, &L.qkv, bytes_of(ctx, (qd + 2 * kvd) * H)));
     TRY(dalloc(ctx, &L.wo, bytes_of(ctx, qd * H)));
     TRY(dalloc(ctx, &L.router, bytes_of(ctx, H * E)));
-    TRY(dalloc(ctx, &L.gu, bytes_of(ctx, (E + 1) * 2 * F * H)));
-    TRY(dalloc(ctx, &L.down, bytes_of(ctx, (E + 1) * F * H)));
+    if (mxfp4(c)) {
+      const QSize gq = mxfp4_size(2 * F / 16, H), dq = mxfp4_size(H / 16, F);
+      TRY(dalloc(ctx, &L.gu, (size_t)((E + 1) * gq.codes)));
+      TRY(dalloc(ctx, &L.gu_s, (size_t)((E + 1) * gq.scales)));
+      TRY(dalloc(ctx, &L.down, (size_t)((E + 1) * dq.codes)));
+      TRY(dalloc(ctx, &L.down_s, (size_t)((E + 1) * dq.scales)));
+    } else {
+      TRY(dalloc(ctx, &L.gu, bytes_of(ctx, (E + 1) * 2 * F * H)));
+      TRY(dalloc(ctx, &L.down, bytes_of(ctx, (E + 1) * F * H)));
+    }
     for (int i = 0; i < 4; ++i) TRY(dalloc(ctx, &L.norm[i], bytes_of(ctx, H)));
   }
   const int KB = (int)(H / 32);
@@ -697,17 +733,31 @@ dg_status dg_set_layer_weights(dg_ctx* ctx, int32_t layer, const dg_layer_weight
   HIPX(launch_pack(ctx->bf16, p, ctx->st));
   p = PackArgs{w->router, nullptr, E, (int)H, (int)E, 1, 0, 0, 0, L.router};
   HIPX(launch_pack(ctx->bf16, p, ctx->st));
-  // routed experts 0..E-1 then the shared expert at index E
-  p = PackArgs{w->w_gate, w->w_up, F, (int)H, (int)(2 * F), 1, 2, 0, 0, L.gu};
+  // routed experts 0..E-1 then the shared expert at index E; MXFP4 experts are
+  // packed as bf16 into a scratch buffer first and quantised from there
+  void* tmp = nullptr;
+  if (mxfp4(c)) TRY(dalloc(ctx, &tmp, bytes_of(ctx, (E + 1) * 2 * F * H)));
+  void* gu_dst = mxfp4(c) ? tmp : L.gu;
+  p = PackArgs{w->w_gate, w->w_up, F, (int)H, (int)(2 * F), 1, 2, 0, 0, gu_dst};
   HIPX(launch_pack_batched(ctx->bf16, p, (int)E, H * F, 2 * F * H, ctx->st));
   p = PackArgs{w->sh_gate, w->sh_up, F, (int)H, (int)(2 * F), 1, 2, 0, 0,
-               reinterpret_cast<char*>(L.gu) + bytes_of(ctx, E * 2 * F * H)};
+               reinterpret_cast<char*>(gu_dst) + bytes_of(ctx, E * 2 * F * H)};
   HIPX(launch_pack(ctx->bf16, p, ctx->st));
-  p = PackArgs{w->w_down, nullptr, H, (int)F, (int)H, 1, 0, 0, 0, L.down};
+  if (mxfp4(c))
+    HIPX(launch_quant_mxfp4(tmp, (int)E + 1, 2 * F * H, (int)(2 * F / 16), (int)(H / 32),
+                            reinterpret_cast<uint4*>(L.gu), reinterpret_cast<uint8_t*>(L.gu_s), ctx->st));
+  void* dn_dst = mxfp4(c) ? tmp : L.down;
+  p = PackArgs{w->w_down, nullptr, H, (int)F, (int)H, 1, 0, 0, 0, dn_dst};
   HIPX(launch_pack_batched(ctx->bf16, p, (int)E, F * H, F * H, ctx->st));
   p = PackArgs{w->sh_down, nullptr, H, (int)F, (int)H, 1, 0, 0, 0,
-               reinterpret_cast<char*>(L.down) + bytes_of(ctx, E * F * H)};
+               reinterpret_cast<char*>(dn_dst) + bytes_of(ctx, E * F * H)};
   HIPX(launch_pack(ctx->bf16, p, ctx->st));
+  if (mxfp4(c)) {
+    HIPX(launch_quant_mxfp4(tmp, (int)E + 1, F * H, (int)(H / 16), (int)(F / 32),
+                            reinterpret_cast<uint4*>(L.down), reinterpret_cast<uint8_t*>(L.down_s), ctx->st));
+    HIPX(hipStreamSynchronize(ctx->st));  // the scratch is read before it is freed
+    dfree(ctx, tmp);
+  }
   const void* norms[4] = {w->norm_in, w->norm_pa, w->norm_pf, w->norm_pf2};
   for (int i = 0; i < 4; ++i)
     HIPX(hipMemcpyAsync(L.norm[i], norms[i], bytes_of(ctx, H), hipMemcpyDeviceToDevice, ctx->st));
@@ -833,6 +883,34 @@ dg_status dg_commit_block(dg_ctx* ctx, int32_t batch, const int32_t* tokens) {
     S.prompt_len += N;
     HIPX(launch_rope_table(ctx->rope + (size_t)b * N * (D / 2), N, D, S.prompt_len, (double)c.rope_theta, ctx->st));
   }
+  return DG_OK;
+}
+
+dg_status dg_get_expert_weight(dg_ctx* ctx, int32_t layer, int32_t expert, int32_t which, void* values,
+                               uint8_t* codes, uint8_t* scales) {
+  TRY(enter(ctx));
+  const dg_config& c = ctx->c;
+  if (layer < 0 || layer >= c.n_layers || !ctx->L[layer].set) return fail(ctx, DG_ESTATE, "layer %d not loaded", layer);
+  if (expert < 0 || expert > c.n_experts) return fail(ctx, DG_EINVAL, "expert %d outside [0, %d]", expert, c.n_experts);
+  if (which < 0 || which > 2) return fail(ctx, DG_EINVAL, "which must be 0 (gate), 1 (up) or 2 (down)");
+  if ((codes || scales) && !mxfp4(c)) return fail(ctx, DG_EINVAL, "codes and scales exist only for MXFP4 experts");
+  const long long H = c.hidden, F = c.expert_ffn;
+  const LayerW& L = ctx->L[layer];
+  const bool down = which == 2;
+  const int K = (int)(down ? F : H), N = (int)(down ? H : F);
+  const long long NB = down ? H / 16 : 2 * F / 16;
+  const void* packed = nullptr;
+  const uint4* q = nullptr;
+  const uint8_t* sc = nullptr;
+  if (mxfp4(c)) {
+    const QSize qs = mxfp4_size(NB, K);
+    q = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(down ? L.down : L.gu) + expert * qs.codes);
+    sc = reinterpret_cast<const uint8_t*>(down ? L.down_s : L.gu_s) + expert * qs.scales;
+  } else {
+    packed = reinterpret_cast<const char*>(down ? L.down : L.gu) + bytes_of(ctx, expert * NB * 16 * K);
+  }
+  HIPX(launch_unpack_weight(ctx->bf16, packed, q, sc, K, N, down ? 0 : 2, which == 1 ? 1 : 0, values, codes, scales,
+                            ctx->st));
   return DG_OK;
 }
 

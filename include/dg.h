@@ -87,7 +87,20 @@ typedef struct dg_config {
   int32_t dtype;          /* dg_dtype of weights, KV and stored activations */
   int32_t has_lm_head;    /* 0: decoder layers only (dg_forward_hidden) */
   int32_t post_ffn_norm;  /* 1: normalise the MoE output before the residual add */
+  int32_t expert_format;  /* dg_expert_format of the routed and shared experts' matrices */
 } dg_config;
+
+/* Storage of the expert matrices (w_gate, w_up, w_down, sh_*).  MXFP4 (OCP
+ * Microscaling Formats v1.0: 4-bit E2M1 elements, one E8M0 scale per 32
+ * consecutive input-dimension entries of a column) is the gfx950-native
+ * analogue of the 4-bit builds the pages list ([Experimental] "DiffusionGemma:
+ * Google's Experimental Diffusion LLM"; [ParadigmShift] "Serving in
+ * Production": GGUF Q4_K_M, NVFP4).  Weights are still given as T; the
+ * library quantises them when they are set (scale s = floor(log2 max|x|) - 2
+ * clamped to [-126, 127]; each element the nearest E2M1 value of x / 2^s, ties
+ * to the even mantissa, saturating at 6) and the expert GEMMs multiply bf16
+ * activations by the exact dequantised values.  DG_BF16 contexts only. */
+typedef enum dg_expert_format { DG_EXPERT_NATIVE = 0, DG_EXPERT_MXFP4 = 1 } dg_expert_format;
 
 /* One decoder layer's weights (caller-owned device pointers, dtype T).
  * Shapes: wq [H, Hq*D]; wk, wv [H, Hkv*D]; wo [Hq*D, H]; router [H, E];
@@ -226,6 +239,15 @@ dg_status dg_generate_block_eb(dg_ctx* ctx, int32_t batch, int32_t* tokens, uint
  * caches move between (synchronising the stream); later commits only enqueue
  * work. */
 dg_status dg_commit_block(dg_ctx* ctx, int32_t batch, const int32_t* tokens);
+
+/* Test export: one expert matrix as the expert GEMMs multiply by it, in math
+ * layout.  expert in [0, E] (E = the shared expert); which 0 = gate [H, F],
+ * 1 = up [H, F], 2 = down [F, H].  values T [K, N] device (the dequantised
+ * weights for MXFP4); for MXFP4 contexts codes uint8 [K, N] (one E2M1 code per
+ * byte, sign in bit 3) and scales uint8 [K / 32, N] (s + 127) device, or NULL.
+ * Any output may be NULL. */
+dg_status dg_get_expert_weight(dg_ctx* ctx, int32_t layer, int32_t expert, int32_t which, void* values,
+                               uint8_t* codes, uint8_t* scales);
 
 /* Test export: the prompt KV cache of one slot and layer as
  * [len, Hkv, D] (k after RoPE, v) into caller buffers k, v (device, the

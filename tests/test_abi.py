@@ -67,6 +67,7 @@ def _create(cfg):
     ("max_batch", 65, dg.DG_EINVAL),
     ("canvas_len", 20, dg.DG_EUNSUPPORTED),
     ("dtype", 7, dg.DG_EINVAL),
+    ("expert_format", 2, dg.DG_EINVAL),
 ])
 def test_create_rejects_bad_configs_before_any_device_call(field, value, status):
     cfg = dg.make_config(C3.model, 1, 4096)
@@ -131,3 +132,14 @@ def test_eb_context_calls_reject_null_context():
     assert L.dg_eb_step(None, 1, None, None, 0, 48, seeds, 0, None, None, None, None, None) == dg.DG_EINVAL
     assert L.dg_generate_block_eb(None, 1, None, None, seeds, 0, 48, passes) == dg.DG_EINVAL
     assert L.dg_k_lm_sample(None, 1, None, 0, 48, seeds, 0, None, None, None) == dg.DG_EINVAL
+
+
+def test_mxfp4_experts_need_a_bf16_context():
+    import dataclasses
+
+    from synth import C1
+    cfg = dg.make_config(dataclasses.replace(C1.model, expert_format="mxfp4"), 1, 64)  # C1 is fp32
+    st, h = _create(cfg)
+    assert st == dg.DG_EUNSUPPORTED and not h.value
+    with pytest.raises(ValueError):
+        dg.make_config(dataclasses.replace(C1.model, expert_format="int3"), 1, 64)
