@@ -15,7 +15,8 @@ gate|up expert GEMM, timed with HIP events on the library's stream) and the
 CPU oracle's rate on a bounded sample of the same workload.  ``eb_sampler``
 adds the entropy-bounded variant of the same workload: the pass time with
 the sampler head (temperature, entropy, Gumbel-max sample) and the EB lock
-step, and whole blocks that stop adaptively within 48 passes.
+step, and whole blocks that stop adaptively within 48 passes.  ``mxfp4_experts``
+measures the same workload again with the expert matrices stored as MXFP4.
 """
 from __future__ import annotations
 
@@ -39,7 +40,7 @@ METRIC = "canvas tokens/sec per denoise pass; resolved tok/s (30-layer bf16, 1 M
 # they were taken with
 COUNTERS = os.path.join(ROOT, "profiles", "moe_gate_up_C3_counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "canvas_denoising_moe_amd", "csrc", f) for f in ("gemm.hip", "common.h")]
-GATE_UP_KERNEL = r"k_stream<unsigned short, \d+, \d+, 1, \d+, \d+>"   # <T, MT, WN, EPI_GEGLU, R, LDS KB>
+GATE_UP_KERNEL = r"k_stream<unsigned short, \d+, \d+, 1, \d+, \d+, 0>"   # <T, MT, WN, EPI_GEGLU, R, LDS KB, bf16 W>
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -120,16 +121,18 @@ def algorithmic(w, touched):
     H, D, F, E, K, V = m.hidden, m.head_dim, m.expert_ffn, m.n_experts, m.top_k, m.vocab
     qd, kvd = m.n_heads * D, m.n_kv_heads * D
     es = 2 if m.dtype == "bf16" else 4
+    # expert matrices: MXFP4 stores 4 bits per weight plus one scale byte per 32
+    ees = 0.5 + 1.0 / 32 if getattr(m, "expert_format", "native") == "mxfp4" else es
     byts = flops = 0.0
     gu_bytes = []
     for l in range(m.n_layers):
         Lw = m.kv_len(l, w.prompt_len)
         attn_w = (H * (qd + 2 * kvd) + qd * H + H * E) * es
-        ex = (touched[l] + 1) * 3 * H * F * es
+        ex = (touched[l] + 1) * 3 * H * F * ees
         kv = w.batch * Lw * kvd * 2 * es
         norms = 4 * H * es
         byts += attn_w + ex + kv + norms
-        gu_bytes.append((touched[l] + 1) * 2 * H * F * es + M * H * es + (M * K + M) * F * es)
+        gu_bytes.append((touched[l] + 1) * 2 * H * F * ees + M * H * es + (M * K + M) * F * es)
         flops += 2.0 * M * (H * (qd + 2 * kvd) + qd * H + H * E + (K + 1) * 3 * H * F)
         flops += 4.0 * M * m.n_heads * D * (Lw + m.canvas_len)
     if m.has_lm_head:
@@ -182,6 +185,76 @@ def cpu_baseline(w):
             "sample": sample}
 
 
+def measure_mxfp4(w0, steps, warmup):
+    """The same workload with MXFP4 expert weights: pass time, the expert
+    GEMMs' launch times and the gate|up roofline on its (4.25-bit) bytes."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    import canvas_denoising_moe_amd as dg
+    from canvas_denoising_moe_amd import binding as bd
+    from synth import gen, upload
+
+    w = dataclasses.replace(w0, name=w0.name + "-mxfp4", model=dataclasses.replace(w0.model, expert_format="mxfp4"))
+    m = w.model
+    B, N, T = w.batch, m.canvas_len, w.n_steps
+    M = B * N
+    dev = torch.device("cuda", 0)
+    t0 = time.perf_counter()
+    ctx = dg.Context(m, max_batch=B, max_prompt_len=w.prompt_len, device=0)
+    try:
+        upload.load_context(ctx, w)
+        torch.cuda.synchronize()
+        load_s = time.perf_counter() - t0
+        print(f"[bench] {w.name}: loaded and quantised in {load_s:.1f} s", file=sys.stderr, flush=True)
+        tok0, lk0 = gen.canvas(w)
+        tok0_d = torch.from_numpy(tok0).to(dev)
+        lk0_d = torch.from_numpy(lk0).to(dev)
+        tokens, locked = tok0_d.clone(), lk0_d.clone()
+        trace = torch.empty((m.n_layers, M, m.top_k), dtype=torch.int32, device=dev)
+        ctx.set_trace(trace)
+        ctx.denoise_step(tokens, locked, [T] * B)
+        torch.cuda.synchronize()
+        ctx.set_trace(None)
+        tr = trace.cpu().numpy()
+        touched = [int(np.unique(tr[l]).size) for l in range(m.n_layers)]
+
+        def step(i):
+            s = i % T
+            if s == 0:
+                tokens.copy_(tok0_d)
+                locked.copy_(lk0_d)
+            ctx.denoise_step(tokens, locked, [T - s] * B)
+
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        ctx.profile([bd.PROF_GATE_UP, bd.PROF_DOWN])
+        for i in range(4):
+            step(steps + i)
+        torch.cuda.synchronize()
+        ctx.profile(())
+        n_gu, ms_gu = ctx.profile_read(bd.PROF_GATE_UP)
+        n_dn, ms_dn = ctx.profile_read(bd.PROF_DOWN)
+    finally:
+        ctx.close()
+    _, _, gu_bytes, _ = algorithmic(w, touched)
+    gu_s = ms_gu / max(n_gu, 1) / 1e3
+    ach = gu_bytes / gu_s / 1e9
+    return {"workload": w.name, "ms_per_step": round(ms, 4), "canvas_tok_s": round(M / (ms / 1e3), 1),
+            "gate_up_us": round(gu_s * 1e6, 2), "down_us": round(ms_dn / max(n_dn, 1) * 1e3, 2),
+            "gate_up_roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": round(ach / HBM_PEAK_GBS, 4), "bytes_per_launch": int(gu_bytes)},
+            "experts_touched_min": min(touched), "load_s": round(load_s, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -193,6 +266,8 @@ def main():
                     help="extra passes after the timed region with every kernel class timed")
     ap.add_argument("--eb-blocks", type=int, default=1,
                     help="whole entropy-bounded blocks timed (at most 48 passes each)")
+    ap.add_argument("--no-mxfp4", action="store_true",
+                    help="skip the variant with MXFP4 expert weights (a second context)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--probe-copy-mib", type=int, default=0,
                     help="only run 4 device copies of this many MiB (calibrates HBM byte counters) and exit")
@@ -424,6 +499,9 @@ def main():
         "init_s": round(init_s, 1),
     }
     ctx.close()
+    if not args.no_mxfp4 and m.dtype == "bf16":
+        torch.cuda.empty_cache()
+        line["mxfp4_experts"] = measure_mxfp4(w, args.steps, args.warmup)
     print(json.dumps(line), flush=True)
 
 
