@@ -58,6 +58,7 @@ _SIGS = {
     "dg_denoise_step": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, POINTER(c_int32), c_void_p, c_void_p]),
     "dg_generate_block": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
     "dg_commit_block": (c_int32, [c_void_p, c_int32, c_void_p]),
+    "dg_commit_tokens": (c_int32, [c_void_p, c_int32, c_void_p, c_int32]),
     "dg_eb_step": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_int32, POINTER(ctypes.c_uint32),
                              ctypes.c_uint32, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
     "dg_generate_block_eb": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, POINTER(ctypes.c_uint32),
@@ -286,6 +287,25 @@ class Context:
         prompt KV caches (dg_commit_block): every slot's prompt_len grows by N."""
         import torch
         self._c(lib().dg_commit_block(self._h, tokens.shape[0], _ptr(tokens, torch.int32, "tokens")))
+
+    def commit_tokens(self, tokens, n: int):
+        """Commit the first ``n`` tokens of each row of ``tokens [batch, N]``
+        (dg_commit_tokens): every slot's prompt_len grows by n."""
+        import torch
+        self._c(lib().dg_commit_tokens(self._h, tokens.shape[0], _ptr(tokens, torch.int32, "tokens"), int(n)))
+
+    def prefill(self, tokens):
+        """Build the prompt KV from prompt ids ``tokens [batch, L]`` (int32,
+        device) by successive commits of N tokens and a shorter last one."""
+        import torch
+        B, L = tokens.shape
+        N = self.model.canvas_len
+        with torch.cuda.stream(self.stream):  # the copies are ordered with the commits that read them
+            buf = torch.zeros((B, N), dtype=torch.int32, device=tokens.device)
+            for p0 in range(0, L, N):
+                n = min(N, L - p0)
+                buf[:, :n].copy_(tokens[:, p0:p0 + n])
+                self.commit_tokens(buf, n)
 
     def prompt_kv_len(self, slot: int, layer: int) -> int:
         n = c_int32()

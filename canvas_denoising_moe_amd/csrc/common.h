@@ -343,11 +343,12 @@ hipError_t launch_lock_select(int B, int N, const float* conf, const int32_t* pr
 // Layout helpers.
 hipError_t launch_kv_repack(int is_bf16, const void* src, int L, int Hkv, int D, void* k_dst,
                             int transpose, hipStream_t s);
-// K [Hkv][new_len][D] / V^T [Hkv][D][new_len] of one layer after appending a
-// block of N positions (k [Hkv][N][D], v^T [Hkv][D][N]) to the old cache;
-// positions are absolute, the new range a suffix of [old ; block] (layout.hip)
+// K [Hkv][new_len][D] / V^T [Hkv][D][new_len] of one layer after appending the
+// first n of a block's N positions (k [Hkv][N][D], v^T [Hkv][D][N]) to the old
+// cache; positions are absolute, the new range a suffix of [old ; block
+// positions < n] (layout.hip)
 hipError_t launch_kv_append(int is_bf16, const void* kold, const void* vold, int old_len, long long old_first,
-                            const void* kblk, const void* vblk, int N, long long blk_first, int new_len,
+                            const void* kblk, const void* vblk, int N, int n, long long blk_first, int new_len,
                             long long first, int Hkv, int D, void* knew, void* vnew, hipStream_t s);
 // generic 4-d permute copy: dst[(i0,i1,i2,i3) strides ds] = src[(i0,i1,i2,i3) strides ss]
 hipError_t launch_permute4(int is_bf16, const void* src, void* dst, const int* dims,

@@ -108,16 +108,21 @@ __global__ __launch_bounds__(256) void k_eb_noise(int V, EbArg eb, float* out) {
 }
 
 // One workgroup per canvas.  Canvases marked done are left as they are.
+// Locked positions rank as +inf, which no entropy (finite, >= 0) exceeds or
+// equals; LDS rows are read four values at a time.  The running sum (thread
+// 0) and the mean (a thread of the second wave) are sequential float32 sums
+// in the stated orders.
 __global__ __launch_bounds__(1024) void k_eb_select(int N, const float* __restrict__ ent,
                                                     const int32_t* __restrict__ samp,
                                                     const int32_t* __restrict__ pred, int32_t* tokens,
                                                     uint8_t* locked, int32_t* prev_pred, int32_t* status,
                                                     int t, int t_max) {
   extern __shared__ float lds[];
-  float* H = lds;             // [N] entropies by position
-  float* sorted = lds + N;    // [N] unlocked entropies in lock order
-  int* rank = reinterpret_cast<int*>(lds + 2 * N);  // [N] lock order of each unlocked position, -1 locked
-  int* is_free = rank + N;    // [N]
+  const int N4 = (N + 3) & ~3;
+  float* H = lds;              // [N4] entropies by position (0 past N)
+  float* Hr = lds + N4;        // [N4] the same, +inf where locked or past N
+  float* sorted = lds + 2 * N4;  // [N4] unlocked entropies in lock order
+  int* rank = reinterpret_cast<int*>(lds + 3 * N4);  // [N4] lock order, -1 locked
   __shared__ int changed_s, nfree_s, k_s, stop_s;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int st = status[b];
@@ -129,10 +134,16 @@ __global__ __launch_bounds__(1024) void k_eb_select(int N, const float* __restri
   if (tid == 0) { changed_s = 0; nfree_s = 0; }
   __syncthreads();
   int nf = 0, changed = 0;
-  for (int i = tid; i < N; i += blockDim.x) {
-    H[i] = ent[base + i];
-    const int lk = locked[base + i];
-    is_free[i] = lk ? 0 : 1;
+  for (int i = tid; i < N4; i += blockDim.x) {
+    if (i >= N) {
+      H[i] = 0.f;
+      Hr[i] = INFINITY;
+      continue;
+    }
+    const float h = ent[base + i];
+    const bool lk = locked[base + i] != 0;
+    H[i] = h;
+    Hr[i] = lk ? INFINITY : h;
     nf += lk ? 0 : 1;
     const int pr = pred[base + i];
     changed |= pr != prev_pred[base + i];
@@ -142,20 +153,25 @@ __global__ __launch_bounds__(1024) void k_eb_select(int N, const float* __restri
   atomicAdd(&nfree_s, nf);
   __syncthreads();
   // lock order: increasing entropy, then increasing position
+  const float4* h4 = reinterpret_cast<const float4*>(Hr);
   for (int i = tid; i < N; i += blockDim.x) {
-    if (!is_free[i]) { rank[i] = -1; continue; }
-    const float hi = H[i];
+    const float hi = Hr[i];
+    if (hi == INFINITY) { rank[i] = -1; continue; }
     int r = 0;
-    for (int j = 0; j < N; ++j) {
-      const float hj = H[j];
-      r += (is_free[j] && (hj < hi || (hj == hi && j < i))) ? 1 : 0;
+#pragma unroll 8
+    for (int j4 = 0; j4 < (N4 >> 2); ++j4) {
+      const float4 v = h4[j4];
+      const int j = j4 * 4;
+      r += (v.x < hi || (v.x == hi && j < i)) ? 1 : 0;
+      r += (v.y < hi || (v.y == hi && j + 1 < i)) ? 1 : 0;
+      r += (v.z < hi || (v.z == hi && j + 2 < i)) ? 1 : 0;
+      r += (v.w < hi || (v.w == hi && j + 3 < i)) ? 1 : 0;
     }
     rank[i] = r;
+    sorted[r] = hi;
   }
   __syncthreads();
-  for (int i = tid; i < N; i += blockDim.x)
-    if (rank[i] >= 0) sorted[rank[i]] = H[i];
-  __syncthreads();
+  const int mean_tid = blockDim.x > 64 ? 64 : 0;
   if (tid == 0) {
     const int nfree = nfree_s;
     int k = 0;
@@ -163,16 +179,34 @@ __global__ __launch_bounds__(1024) void k_eb_select(int N, const float* __restri
       k = nfree;
     } else {
       float run = 0.f;
-      for (int r = 0; r < nfree; ++r) {
-        run += sorted[r];
-        if (r > 0 && run > kEntropyBound) break;
-        k = r + 1;
+      const float4* s4 = reinterpret_cast<const float4*>(sorted);
+      bool done = false;
+      for (int r4 = 0; r4 < ((nfree + 3) >> 2) && !done; ++r4) {
+        const float4 v = s4[r4];
+        const float vals[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = r4 * 4 + q;
+          if (done || r >= nfree) { done = true; break; }
+          run += vals[q];
+          if (r > 0 && run > kEntropyBound) { done = true; break; }
+          k = r + 1;
+        }
       }
     }
-    float sum = 0.f;
-    for (int i = 0; i < N; ++i) sum += H[i];
-    const float mean = sum / (float)N;
     k_s = k;
+  }
+  if (tid == mean_tid) {
+    float sum = 0.f;
+    const float4* m4 = reinterpret_cast<const float4*>(H);
+    for (int i4 = 0; i4 < (N4 >> 2); ++i4) {  // position order; entries past N are 0
+      const float4 v = m4[i4];
+      sum += v.x;
+      sum += v.y;
+      sum += v.z;
+      sum += v.w;
+    }
+    const float mean = sum / (float)N;
     stop_s = ((st & 2) && !changed_s && mean < kStopEntropy) ? 1 : 0;
   }
   __syncthreads();
@@ -214,7 +248,7 @@ hipError_t launch_eb_select(int B, int N, const float* ent, const int32_t* samp,
                             int t_max, hipStream_t s) {
   if (B <= 0) return hipSuccess;
   if (N <= 0 || N > 4096) return hipErrorInvalidValue;
-  const size_t lds = (size_t)N * 16;
+  const size_t lds = (size_t)((N + 3) & ~3) * 16;
   static bool attr = false;
   if (!attr) {
     hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_eb_select),

@@ -758,10 +758,13 @@ hipError_t run_stream_dense(const StreamArgs& g, const EpiArgs& e, hipStream_t s
 template <typename T, int MT>
 hipError_t run_stream_mt(const StreamArgs& g, const EpiArgs& e, hipStream_t s, KTime t) {
   if (g.qb) {
-    // MXFP4 experts: a ring slot holds four k-steps in a quarter of the bytes;
-    // 4 slots (16 k-steps, 8 KB per wave in flight) for gate|up, 2 for down
+    // MXFP4 experts: a ring slot holds four k-steps in a quarter of the bytes.
+    // gate|up: 4 n-blocks per wave (half the tiles, so each entry's A rows are
+    // re-staged half as often) and 2 slots (8 KB per wave in flight); measured
+    // on the 30-layer workload: 43.9 us against 46.3 (2 n-blocks, 4 slots),
+    // 52-57 us with deeper rings or 64 KB A chunks.  down: 2 slots of 4 n-blocks.
     if constexpr (sizeof(T) == 2) {
-      if (e.kind == EPI_GEGLU) return run_stream<T, MT, 2, EPI_GEGLU, 4, kStreamLdsKB, 1>(g, e, s, t);
+      if (e.kind == EPI_GEGLU) return run_stream<T, MT, 4, EPI_GEGLU, 2, kStreamLdsKB, 1>(g, e, s, t);
       if (e.kind == EPI_DOWN)
         return run_stream<T, MT, (MT == 2 ? 4 : 2), EPI_DOWN, (MT == 2 ? 2 : 4), kStreamLdsKB, 1>(g, e, s, t);
     }

@@ -82,34 +82,41 @@ __global__ __launch_bounds__(256) void k_argmax_conf(const float* __restrict__ l
 
 // One workgroup per canvas.  rank_i = #{unlocked j : conf_j > conf_i or
 // (conf_j == conf_i and j < i)}; position i is selected iff rank_i < k.
+// Locked positions enter the comparison as -inf, which no confidence (in
+// (0, 1]) falls below or equals; the LDS row is read four values at a time.
 __global__ __launch_bounds__(1024) void k_lock_select(int N, const float* __restrict__ conf,
                                                       const int32_t* __restrict__ pred, int32_t* tokens,
                                                       uint8_t* locked, StepsArg steps) {
-  extern __shared__ float cs[];  // [N] conf, then [N] locked flags
-  uint8_t* lk = reinterpret_cast<uint8_t*>(cs + N);
+  extern __shared__ float cs[];  // [N rounded up to 4] conf, -inf where locked
   __shared__ int rem_s;
   const int b = blockIdx.x, tid = threadIdx.x;
   const long long base = (long long)b * N;
+  const int N4 = (N + 3) & ~3;
   if (tid == 0) rem_s = 0;
   __syncthreads();
   int rem = 0;
-  for (int i = tid; i < N; i += blockDim.x) {
-    cs[i] = conf[base + i];
-    lk[i] = locked[base + i];
-    rem += lk[i] ? 0 : 1;
+  for (int i = tid; i < N4; i += blockDim.x) {
+    const bool lk = i >= N || locked[base + i];
+    cs[i] = lk ? -INFINITY : conf[base + i];
+    rem += lk ? 0 : 1;
   }
   atomicAdd(&rem_s, rem);
   __syncthreads();
   const int sl = steps.v[b];
   const int kk = (rem_s + sl - 1) / sl;
+  const float4* c4 = reinterpret_cast<const float4*>(cs);
   for (int i = tid; i < N; i += blockDim.x) {
-    if (lk[i]) continue;
     const float ci = cs[i];
+    if (ci == -INFINITY) continue;
     int rank = 0;
-    for (int j = 0; j < N; ++j) {
-      if (lk[j]) continue;
-      const float cj = cs[j];
-      rank += (cj > ci || (cj == ci && j < i)) ? 1 : 0;
+#pragma unroll 8
+    for (int j4 = 0; j4 < (N4 >> 2); ++j4) {
+      const float4 v = c4[j4];
+      const int j = j4 * 4;
+      rank += (v.x > ci || (v.x == ci && j < i)) ? 1 : 0;
+      rank += (v.y > ci || (v.y == ci && j + 1 < i)) ? 1 : 0;
+      rank += (v.z > ci || (v.z == ci && j + 2 < i)) ? 1 : 0;
+      rank += (v.w > ci || (v.w == ci && j + 3 < i)) ? 1 : 0;
     }
     if (rank < kk) {
       tokens[base + i] = pred[base + i];
@@ -130,7 +137,7 @@ hipError_t launch_argmax_conf(const float* logits, int rows, int V, int32_t* pre
 hipError_t launch_lock_select(int B, int N, const float* conf, const int32_t* pred, int32_t* tokens,
                               uint8_t* locked, StepsArg steps, hipStream_t s) {
   if (B <= 0) return hipSuccess;
-  const size_t lds = (size_t)N * 4 + (size_t)N;
+  const size_t lds = (size_t)((N + 3) & ~3) * 4;
   const int threads = N >= 1024 ? 1024 : ((N + 63) / 64) * 64;
   hipLaunchKernelGGL(k_lock_select, dim3(B), dim3(threads), lds, s, N, conf, pred, tokens, locked, steps);
   return hipGetLastError();

@@ -22,10 +22,10 @@ __global__ void k_kv_repack(const T* __restrict__ src, int L, int Hkv, int D, T*
   }
 }
 
-// Cache of one layer after a block of N positions is appended: the new
-// visible range is the last new_len positions of [old visible ; block].
-// K is [Hkv][len][D] and V^T [Hkv][D][len]; the block's k is [Hkv][N][D] and
-// its v^T [Hkv][D][N] (one canvas of the canvas buffers).  Destination
+// Cache of one layer after the first n positions of a block are appended: the
+// new visible range is the last new_len positions of [old visible ; block
+// positions 0..n-1].  K is [Hkv][len][D] and V^T [Hkv][D][len]; the block's k
+// is [Hkv][N][D] and its v^T [Hkv][D][N] (one canvas of the canvas buffers).  Destination
 // position p holds absolute position first + p with first = total - new_len;
 // positions below the block's start come from the old cache, whose first
 // visible position is old_first.
@@ -86,13 +86,13 @@ hipError_t launch_kv_repack(int is_bf16, const void* src, int L, int Hkv, int D,
 }
 
 hipError_t launch_kv_append(int is_bf16, const void* kold, const void* vold, int old_len, long long old_first,
-                            const void* kblk, const void* vblk, int N, long long blk_first, int new_len,
+                            const void* kblk, const void* vblk, int N, int n, long long blk_first, int new_len,
                             long long first, int Hkv, int D, void* knew, void* vnew, hipStream_t s) {
   const long long total = (long long)new_len * Hkv * D;
   if (total <= 0) return hipSuccess;
-  if (first < old_first || blk_first + N != first + new_len || old_first + old_len != blk_first ||
+  if (n < 1 || n > N || first < old_first || blk_first + n != first + new_len || old_first + old_len != blk_first ||
       total >= (1LL << 31) || blk_first + N >= (1LL << 31))
-    return hipErrorInvalidValue;  // the new range must be a suffix of [old ; block]
+    return hipErrorInvalidValue;  // the new range must be a suffix of [old ; first n of the block]
   if (is_bf16)
     hipLaunchKernelGGL(k_kv_append<bf16_t>, dim3(grid_for(total)), dim3(256), 0, s,
                        reinterpret_cast<const bf16_t*>(kold), reinterpret_cast<const bf16_t*>(vold), old_len,

@@ -463,11 +463,11 @@ dg_status enqueue_dense(dg_ctx* ctx, const void* A, int lda, const void* Bp, int
 // cache of that layer: the grown visible range goes into the spare buffers,
 // which then become the cache (stream order keeps the layer's attention on
 // the old ones).  The slot's prompt_len moves on after the last layer.
-dg_status append_block_kv(dg_ctx* ctx, int l, int b) {
+dg_status append_block_kv(dg_ctx* ctx, int l, int b, int n) {
   const dg_config& c = ctx->c;
   SlotKV& S = ctx->slots[b];
   const int N = c.canvas_len, Hkv = c.n_kv_heads, D = c.head_dim;
-  const int old_len = S.len[l], new_len = kv_len(c, l, S.prompt_len + N);
+  const int old_len = S.len[l], new_len = kv_len(c, l, S.prompt_len + n);
   if (S.k2.empty()) {
     S.k2.assign(c.n_layers, nullptr);
     S.v2.assign(c.n_layers, nullptr);
@@ -485,10 +485,10 @@ dg_status append_block_kv(dg_ctx* ctx, int l, int b) {
     S.cap2[l] = cap;
   }
   const long long blk_first = S.prompt_len, old_first = blk_first - old_len;
-  const long long first = blk_first + N - new_len;
+  const long long first = blk_first + n - new_len;
   const size_t kb = (size_t)b * Hkv * N * D;  // canvas b in the canvas K / V^T buffers
   HIPX(launch_kv_append(ctx->bf16, S.k[l], S.v[l], old_len, old_first,
-                        static_cast<char*>(ctx->kc) + kb * ctx->es, static_cast<char*>(ctx->vc) + kb * ctx->es, N,
+                        static_cast<char*>(ctx->kc) + kb * ctx->es, static_cast<char*>(ctx->vc) + kb * ctx->es, N, n,
                         blk_first, new_len, first, Hkv, D, S.k2[l], S.v2[l], ctx->st));
   std::swap(S.k[l], S.k2[l]);
   std::swap(S.v[l], S.v2[l]);
@@ -514,8 +514,11 @@ dg_status append_block_kv(dg_ctx* ctx, int l, int b) {
 // w_last_out is given (the final norm before the LM head).  commit: causal
 // canvas attention, each layer's canvas K/V appended to the caches right after
 // its attention, and nothing after the last layer's attention.
-dg_status enqueue_layers(dg_ctx* ctx, int B, const void* w_last_out, int l0 = 0, int l1 = -1, bool commit = false) {
+// commit_n > 0: the causal context-building pass of a block commit; after
+// each layer's attention the first commit_n positions' K/V join the caches
+dg_status enqueue_layers(dg_ctx* ctx, int B, const void* w_last_out, int l0 = 0, int l1 = -1, int commit_n = 0) {
   const dg_config& c = ctx->c;
+  const bool commit = commit_n > 0;
   if (l1 < 0) l1 = c.n_layers;
   const int N = c.canvas_len, M = B * N, H = c.hidden, D = c.head_dim;
   const int Hq = c.n_heads, Hkv = c.n_kv_heads, E = c.n_experts, K = c.top_k;
@@ -527,7 +530,7 @@ dg_status enqueue_layers(dg_ctx* ctx, int B, const void* w_last_out, int l0 = 0,
     TRY(enqueue_qkv(ctx, l, B, ctx->a, ctx->q, ctx->kc, ctx->vc, qs, ks, vs));
     TRY(enqueue_attention(ctx, l, B, ctx->o, 1, commit ? 1 : 0));
     if (commit) {
-      for (int b = 0; b < B; ++b) TRY(append_block_kv(ctx, l, b));
+      for (int b = 0; b < B; ++b) TRY(append_block_kv(ctx, l, b, commit_n));
       if (l + 1 == l1) break;  // later layers' inputs are not needed
     }
     TRY(enqueue_dense(ctx, ctx->o, Hq * D, W.wo, Hq * D, H, M, ctx->ao, H));
@@ -857,33 +860,48 @@ dg_status dg_denoise_step(dg_ctx* ctx, int32_t batch, int32_t* tokens, uint8_t* 
   return DG_OK;
 }
 
-dg_status dg_commit_block(dg_ctx* ctx, int32_t batch, const int32_t* tokens) {
-  TRY(enter(ctx));
+namespace {
+// The first n of each canvas's N tokens join the prompt caches.  The block
+// runs at full width: by the causal mask the positions past n influence none
+// before them, and their K/V are not appended.
+dg_status commit_tokens(dg_ctx* ctx, int32_t batch, const int32_t* tokens, int n) {
   const dg_config& c = ctx->c;
   if (!c.has_lm_head || !ctx->embed_set) return fail(ctx, DG_ESTATE, "the embedding is not loaded");
   if (batch < 1 || batch > c.max_batch) return fail(ctx, DG_EINVAL, "batch %d outside [1, %d]", batch, c.max_batch);
   if (!tokens) return fail(ctx, DG_EINVAL, "tokens is required");
+  if (n < 1 || n > c.canvas_len) return fail(ctx, DG_EINVAL, "n = %d outside [1, %d]", n, c.canvas_len);
   if (!weights_ready(ctx)) return fail(ctx, DG_ESTATE, "weights are not loaded");
   TRY(check_slots(ctx, batch));
   const int N = c.canvas_len, M = batch * N, H = c.hidden;
   for (int b = 0; b < batch; ++b)
-    if (ctx->slots[b].prompt_len + N > c.max_prompt_len)
+    if (ctx->slots[b].prompt_len + n > c.max_prompt_len)
       return fail(ctx, DG_EINVAL, "slot %d: prompt_len %d + %d exceeds max_prompt_len %d", b,
-                  ctx->slots[b].prompt_len, N, c.max_prompt_len);
+                  ctx->slots[b].prompt_len, n, c.max_prompt_len);
   // the block at positions prompt_len + i, causal within the block
   HIPX(launch_embed(ctx->bf16, tokens, M, H, c.vocab, ctx->embed, ctx->x, ctx->st));
   NormArgs n0{};
   n0.mode = 2; n0.rows = M; n0.H = H; n0.k = c.top_k; n0.eps = c.rms_eps;
   n0.x = ctx->x; n0.w_out = ctx->L[0].norm[0]; n0.out = ctx->a;
   HIPX(launch_residual_norm(ctx->bf16, n0, ctx->st));
-  TRY(enqueue_layers(ctx, batch, nullptr, 0, c.n_layers, true));
+  TRY(enqueue_layers(ctx, batch, nullptr, 0, c.n_layers, n));
   const int D = c.head_dim;
   for (int b = 0; b < batch; ++b) {
     SlotKV& S = ctx->slots[b];
-    S.prompt_len += N;
+    S.prompt_len += n;
     HIPX(launch_rope_table(ctx->rope + (size_t)b * N * (D / 2), N, D, S.prompt_len, (double)c.rope_theta, ctx->st));
   }
   return DG_OK;
+}
+}  // namespace
+
+dg_status dg_commit_block(dg_ctx* ctx, int32_t batch, const int32_t* tokens) {
+  TRY(enter(ctx));
+  return commit_tokens(ctx, batch, tokens, ctx->c.canvas_len);
+}
+
+dg_status dg_commit_tokens(dg_ctx* ctx, int32_t batch, const int32_t* tokens, int32_t n) {
+  TRY(enter(ctx));
+  return commit_tokens(ctx, batch, tokens, n);
 }
 
 dg_status dg_get_expert_weight(dg_ctx* ctx, int32_t layer, int32_t expert, int32_t which, void* values,

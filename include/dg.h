@@ -240,6 +240,15 @@ dg_status dg_generate_block_eb(dg_ctx* ctx, int32_t batch, int32_t* tokens, uint
  * work. */
 dg_status dg_commit_block(dg_ctx* ctx, int32_t batch, const int32_t* tokens);
 
+/* dg_commit_block for the first n (1 <= n <= N) tokens of each canvas row:
+ * positions prompt_len + i, i < n, join the caches and prompt_len grows by n.
+ * tokens int32 [batch, N] device; entries past n are ignored (any value).  By
+ * the causal mask the block's positions past n influence none before them,
+ * so this equals a causal pass over the n tokens alone: successive calls
+ * build the prompt KV of a prompt of any length from its token ids (the
+ * encoder prefill), N tokens at a time and a shorter last chunk. */
+dg_status dg_commit_tokens(dg_ctx* ctx, int32_t batch, const int32_t* tokens, int32_t n);
+
 /* Test export: one expert matrix as the expert GEMMs multiply by it, in math
  * layout.  expert in [0, E] (E = the shared expert); which 0 = gate [H, F],
  * 1 = up [H, F], 2 = down [F, H].  values T [K, N] device (the dequantised
@@ -282,7 +291,8 @@ dg_status dg_k_argmax_conf(const float* logits, int32_t rows, int32_t vocab, int
                            float* conf, void* stream);
 
 /* Lock-and-remask step alone (see dg_denoise_step) on given conf/pred
- * [batch, n]; steps_left_host host [batch] (>= 1); batch <= 64, n <= 4096. */
+ * [batch, n] (conf finite, as a probability is); steps_left_host host [batch]
+ * (>= 1); batch <= 64, n <= 4096. */
 dg_status dg_k_lock_select(int32_t batch, int32_t n, const float* conf, const int32_t* pred,
                            int32_t* tokens, uint8_t* locked, const int32_t* steps_left_host,
                            void* stream);
@@ -301,9 +311,10 @@ dg_status dg_k_eb_rows(const float* logits, int32_t rows, int32_t vocab, int32_t
 dg_status dg_k_eb_noise(int32_t rows, int32_t vocab, int32_t canvas_len, int32_t t, const uint32_t* seeds_host,
                         uint32_t block, float* noise, void* stream);
 
-/* The EB lock step alone on given entropy float, sample int32, pred int32
- * [batch, n]: updates tokens, locked, prev_pred [batch, n] and status [batch]
- * as an EB pass t of at most t_max does; batch <= 64, n <= 4096. */
+/* The EB lock step alone on given entropy float (finite, >= 0), sample int32,
+ * pred int32 [batch, n]: updates tokens, locked, prev_pred [batch, n] and
+ * status [batch] as an EB pass t of at most t_max does; batch <= 64,
+ * n <= 4096. */
 dg_status dg_k_eb_select(int32_t batch, int32_t n, const float* entropy, const int32_t* sample,
                          const int32_t* pred, int32_t* tokens, uint8_t* locked, int32_t* prev_pred,
                          int32_t* status, int32_t t, int32_t t_max, void* stream);

@@ -55,28 +55,35 @@ def _visible(m, l, total):
     return total if m.is_global(l) else min(total, m.window)
 
 
-def _commit_and_compare(torch, ctx, w, W, cache, pos, tokens_np, tol, tag):
-    """One GPU commit against the oracle's; returns the oracle's new caches."""
+def _commit_and_compare(torch, ctx, w, W, cache, pos, tokens_np, tol, tag, n=None):
+    """One GPU commit (of the first n tokens of each row; all N when n is
+    None) against the oracle's; returns the oracle's new caches."""
     m = w.model
     L, N = m.n_layers, m.canvas_len
+    n = N if n is None else n
     trace = torch.empty((L, N, m.top_k), dtype=torch.int32, device="cuda")
     ctx.set_trace(trace)
-    say(tag, "commit at", pos)
-    ctx.commit_block(torch.from_numpy(tokens_np.astype(np.int32)).cuda())
+    say(tag, "commit at", pos, "of", n)
+    if n == N:
+        ctx.commit_block(torch.from_numpy(tokens_np.astype(np.int32)).cuda())
+    else:
+        ctx.commit_tokens(torch.from_numpy(tokens_np.astype(np.int32)).cuda(), n)
     torch.cuda.synchronize()
     ctx.set_trace(None)
     tr = trace.cpu().numpy()
-    # the last layer's FFN is not run by the commit: its routing is not compared
-    sh = om.Shadow(route_idx=[tr[l] for l in range(L - 1)] + [None], delta_route=DELTA_REL[m.dtype])
-    blk = om.commit_block(tokens_np, W, m, lambda l, b: cache[l], [pos], shadow=sh)
+    # the last layer's FFN is not run by the commit: its routing is not compared;
+    # the oracle commits the n tokens alone, so only their routing is compared
+    sh = om.Shadow(route_idx=[tr[l][:n] for l in range(L - 1)] + [None], delta_route=DELTA_REL[m.dtype])
+    mn = dataclasses.replace(m, canvas_len=n)
+    blk = om.commit_block(tokens_np[:, :n], W, mn, lambda l, b: cache[l], [pos], shadow=sh)
     assert not sh.failures, sh.failures[:5]
     new = []
     for l in range(L):
-        vis = _visible(m, l, pos + N)
+        vis = _visible(m, l, pos + n)
         K, V = om.append_kv(cache[l][0], cache[l][1], blk[l][0][0], blk[l][1][0], vis)
         gk, gv = _gpu_cache(torch, ctx, m, l)
         assert gk.shape == K.shape, (l, gk.shape, K.shape)
-        old = vis - N  # positions copied from the previous cache
+        old = vis - n  # positions copied from the previous cache
         if old > 0:
             assert np.array_equal(gk[:old], _gpu_prev[l][0][len(_gpu_prev[l][0]) - old:]), (tag, l)
             assert np.array_equal(gv[:old], _gpu_prev[l][1][len(_gpu_prev[l][1]) - old:]), (tag, l)
@@ -92,11 +99,12 @@ def _commit_and_compare(torch, ctx, w, W, cache, pos, tokens_np, tol, tag):
 _gpu_prev = {}
 
 
-def _run_commits(torch, dg, w, n_commits, prefill_from_empty=False):
+def _run_commits(torch, dg, w, n_commits, prefill_from_empty=False, counts=None):
     m = w.model
     L, N = m.n_layers, m.canvas_len
     p0 = 0 if prefill_from_empty else w.prompt_len
-    ctx = dg.Context(m, max_batch=1, max_prompt_len=p0 + n_commits * N)
+    counts = counts if counts is not None else [N] * n_commits
+    ctx = dg.Context(m, max_batch=1, max_prompt_len=p0 + sum(counts))
     try:
         say("load", w.name, "prompt", p0)
         ww = dataclasses.replace(w, prompt_len=p0)
@@ -110,10 +118,12 @@ def _run_commits(torch, dg, w, n_commits, prefill_from_empty=False):
             assert np.array_equal(_gpu_prev[l][0], cache[l][0]) and np.array_equal(_gpu_prev[l][1], cache[l][1])
         rng = np.random.default_rng(w.seed + 1000)
         pos = p0
-        for c in range(n_commits):
+        for c, n in enumerate(counts):
             toks = rng.integers(0, m.vocab, size=(1, N))
-            cache = _commit_and_compare(torch, ctx, ww, W, cache, pos, toks, TOL[m.dtype], f"{w.name} #{c}")
-            pos += N
+            if n < N:
+                toks[:, n:] = rng.integers(-5, 2 * m.vocab, size=(1, N - n))  # ignored, may be anything
+            cache = _commit_and_compare(torch, ctx, ww, W, cache, pos, toks, TOL[m.dtype], f"{w.name} #{c}", n)
+            pos += n
         return ctx, W, cache, pos
     except Exception:
         ctx.close()
@@ -177,6 +187,51 @@ def test_prefill_from_empty_cache_bf16(torch, dg):
     ctx.close()
 
 
+def test_prefill_ragged_prompt_then_pass_bf16(torch, dg):
+    # a 107-token prompt from an empty cache: chunks of 32, 32, 32 and 11
+    # (the window of 64 truncates the local layer's cache along the way),
+    # then a denoise pass at positions 107 + i
+    ctx, W, cache, pos = _run_commits(torch, dg, COMMIT_BF16, 4, prefill_from_empty=True, counts=[32, 32, 32, 11])
+    try:
+        assert pos == 107
+        _pass_after(torch, ctx, dataclasses.replace(COMMIT_BF16, prompt_len=0), W, cache, pos)
+    finally:
+        ctx.close()
+
+
+def test_commit_one_token_at_a_time_f32(torch, dg):
+    w = dataclasses.replace(C1, prompt_len=64)
+    ctx, W, cache, pos = _run_commits(torch, dg, w, 3, counts=[1, 5, 1])
+    try:
+        _pass_after(torch, ctx, w, W, cache, pos)
+    finally:
+        ctx.close()
+
+
+def test_prefill_helper_equals_commits(torch, dg):
+    # Context.prefill (chunked dg_commit_tokens) gives the same caches as the
+    # explicit commits of the test above, bit for bit
+    w = COMMIT_BF16
+    m = w.model
+    rng = np.random.default_rng(w.seed + 1000)
+    toks = [rng.integers(0, m.vocab, size=(1, m.canvas_len)) for _ in range(4)]
+    counts = [32, 32, 32, 11]
+    prompt = np.concatenate([t[:, :n] for t, n in zip(toks, counts)], axis=1).astype(np.int32)
+    caches = []
+    for mode in ("prefill", "commits"):
+        with dg.Context(m, max_batch=1, max_prompt_len=107) as ctx:
+            upload.load_context(ctx, dataclasses.replace(w, prompt_len=0))
+            if mode == "prefill":
+                ctx.prefill(torch.from_numpy(prompt).cuda())
+            else:
+                for t, n in zip(toks, counts):
+                    ctx.commit_tokens(torch.from_numpy(t.astype(np.int32)).cuda(), n)
+            torch.cuda.synchronize()
+            caches.append([_gpu_cache(torch, ctx, m, l) for l in range(m.n_layers)])
+    for l in range(m.n_layers):
+        assert np.array_equal(caches[0][l][0], caches[1][l][0]) and np.array_equal(caches[0][l][1], caches[1][l][1])
+
+
 def test_commit_rejects_overflow(torch, dg):
     w = COMMIT_BF16
     m = w.model
@@ -186,3 +241,8 @@ def test_commit_rejects_overflow(torch, dg):
         with pytest.raises(Exception, match="exceeds max_prompt_len"):
             ctx.commit_block(toks)
         assert ctx.prompt_kv_len(0, 1) == w.prompt_len  # nothing changed
+        for bad in (0, m.canvas_len + 1):
+            with pytest.raises(Exception, match="outside"):
+                ctx.commit_tokens(toks, bad)
+        ctx.commit_tokens(toks, 16)  # fits
+        assert ctx.prompt_kv_len(0, 1) == w.prompt_len + 16

@@ -101,20 +101,23 @@ TINY = dataclasses.replace(
 
 
 def _commit_chain(w, tokens, chunk):
-    """Commit ``tokens`` in chunks of ``chunk`` from an empty cache; returns
-    the per-layer caches."""
-    m = dataclasses.replace(w.model, canvas_len=chunk)
-    W = weights_for(dataclasses.replace(w, model=m))
-    L = m.n_layers
-    Hkv, D = m.n_kv_heads, m.head_dim
+    """Commit ``tokens`` in chunks of ``chunk`` (the last one shorter when the
+    length is not a multiple) from an empty cache; returns the per-layer
+    caches."""
+    W = weights_for(w)
+    L = w.model.n_layers
+    Hkv, D = w.model.n_kv_heads, w.model.head_dim
     cache = [(np.zeros((0, Hkv, D)), np.zeros((0, Hkv, D))) for _ in range(L)]
     pos = 0
     for c0 in range(0, tokens.shape[1], chunk):
-        blk = om.commit_block(tokens[:, c0:c0 + chunk], W, m, lambda l, b: cache[l], [pos])
+        part = tokens[:, c0:c0 + chunk]
+        n = part.shape[1]
+        m = dataclasses.replace(w.model, canvas_len=n)
+        blk = om.commit_block(part, W, m, lambda l, b: cache[l], [pos])
         for l in range(L):
-            vis = pos + chunk if m.is_global(l) else min(pos + chunk, m.window)
+            vis = pos + n if m.is_global(l) else min(pos + n, m.window)
             cache[l] = om.append_kv(cache[l][0], cache[l][1], blk[l][0][0], blk[l][1][0], vis)
-        pos += chunk
+        pos += n
     return cache
 
 
@@ -124,7 +127,7 @@ def test_chunked_commits_equal_one_causal_pass():
     # block give the same cache at every layer
     tokens = _rng(9).integers(0, TINY.model.vocab, size=(1, 24))
     whole = _commit_chain(TINY, tokens, 24)
-    for chunk in (8, 12):
+    for chunk in (8, 12, 7, 5):  # 7 and 5 leave a shorter last chunk (3 and 4)
         got = _commit_chain(TINY, tokens, chunk)
         for l in range(TINY.model.n_layers):
             assert np.allclose(got[l][0], whole[l][0], rtol=0, atol=1e-10), (chunk, l)
