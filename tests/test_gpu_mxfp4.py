@@ -136,3 +136,43 @@ def test_block_mxfp4_tiny(torch, dg):
     report, worst = shadow_compare(w, tok0, lk0, passes, DELTA_REL["bf16"], TOL["bf16"])
     print(f"mxfp4 tiny block: adopted {report}, worst conf rel err {worst:.3e}")
     assert passes[-1]["locked"].all()
+
+
+def test_c3_mxfp4_sampled_layers(torch, dg):
+    # the benchmark's MXFP4 configuration (30-layer stack, 4096-position prompt
+    # KV): layers 0 and 29, each from the GPU's own input to it, against the
+    # oracle with the dequantised experts; routing shadowed
+    from synth import C3
+    w = dataclasses.replace(C3, name="C3-mxfp4", model=dataclasses.replace(C3.model, expert_format="mxfp4"))
+    m = w.model
+    M = w.batch * m.canvas_len
+    tok0, _ = gen.canvas(w)
+    x_np = om.bf16_bits_to_f64(gen.embed(w)[tok0.reshape(-1)])
+    with dg.Context(m, max_batch=1, max_prompt_len=w.prompt_len) as ctx:
+        say("C3 mxfp4 load")
+        upload.load_context(ctx, w)
+        x0 = torch.from_numpy(x_np.astype(np.float32)).cuda()
+        x28 = torch.empty_like(x0)
+        x29 = torch.empty_like(x0)
+        x1 = torch.empty_like(x0)
+        trace = torch.zeros((m.n_layers, M, m.top_k), dtype=torch.int32, device="cuda")
+        ctx.set_trace(trace)
+        say("C3 mxfp4 layers")
+        ctx.forward_layers(0, 1, x0, x1)
+        ctx.forward_layers(0, 29, x0, x28)
+        ctx.forward_layers(29, 1, x28, x29)
+        torch.cuda.synchronize()
+        tr = trace.cpu().numpy()
+        ctx.set_trace(None)
+        got = {0: (x_np, host64(x1)), 29: (host64(x28), host64(x29))}
+    W = weights_for(w)
+    kvf = prompt_kv_fn(w)
+    for l, (xin, xout) in got.items():
+        route = [None] * m.n_layers
+        route[l] = tr[l]
+        sh = om.Shadow(route_idx=route, delta_route=DELTA_REL["bf16"])
+        ref = om.forward_hidden(xin, W, m, kvf, [w.prompt_len], layers=[l], shadow=sh)
+        e = rel_err(xout, ref)
+        print(f"C3 mxfp4 layer {l}: rel err {e:.3e}, routing adopted {sh.adopted['route']}", flush=True)
+        assert not sh.failures, sh.failures[:5]
+        assert e <= TOL["bf16"], (l, e)
