@@ -5,6 +5,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+#include <set>
+#include <utility>
+
 typedef uint16_t bf16_t;  // raw bf16 bits
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_v __attribute__((ext_vector_type(8)));
@@ -71,6 +75,22 @@ DG_DEV float block_sum(float v, float* red) {
 // first kernel and `stop` the end time of its last one.  The events are bound
 // to the kernel dispatches themselves, so timing adds no packets to the stream.
 struct KTime { hipEvent_t start = nullptr, stop = nullptr; };
+
+// Raises a kernel's dynamic LDS limit to `bytes` on the current device, once
+// per (kernel, device): the attribute belongs to the kernel's code object on
+// each device, so a process driving two GPUs sets it on both.
+inline hipError_t ensure_lds_limit(const void* fn, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::set<std::pair<const void*, int>> done;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count({fn, dev})) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.insert({fn, dev});
+  return e;
+}
 
 template <typename F, typename... Args>
 inline hipError_t launch_k(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s,

@@ -249,13 +249,8 @@ hipError_t launch_eb_select(int B, int N, const float* ent, const int32_t* samp,
   if (B <= 0) return hipSuccess;
   if (N <= 0 || N > 4096) return hipErrorInvalidValue;
   const size_t lds = (size_t)((N + 3) & ~3) * 16;
-  static bool attr = false;
-  if (!attr) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_eb_select),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, 4096 * 16);
-    if (err != hipSuccess) return err;
-    attr = true;
-  }
+  hipError_t err = ensure_lds_limit(reinterpret_cast<const void*>(&k_eb_select), 4096 * 16);
+  if (err != hipSuccess) return err;
   const int threads = N >= 1024 ? 1024 : ((N + 63) / 64) * 64;
   hipLaunchKernelGGL(k_eb_select, dim3(B), dim3(threads), lds, s, N, ent, samp, pred, tokens, locked, prev_pred,
                      status, t, t_max);

@@ -733,14 +733,9 @@ hipError_t run_stream(const StreamArgs& g, const EpiArgs& e, hipStream_t s, KTim
   size_t lds = (size_t)16 * MT * min(KB, stream_kc<T, MT, R, LK>()) * 32 * sizeof(T);
   // bf16 down: the 4 waves' fp32 output tiles reuse the A chunk's LDS
   if (EPI == EPI_DOWN && sizeof(T) == 2) lds = max(lds, (size_t)4 * 16 * MT * 16 * WN * sizeof(float));
-  static bool attr_set = false;  // one attribute call per instantiation
-  if (!attr_set) {
-    // the chunk plus the kernel's static LDS
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_stream<T, MT, WN, EPI, R, LK, QB>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, LK * 1024);
-    if (err != hipSuccess) return err;
-    attr_set = true;
-  }
+  // the chunk plus the kernel's static LDS
+  hipError_t err = ensure_lds_limit(reinterpret_cast<const void*>(&k_stream<T, MT, WN, EPI, R, LK, QB>), LK * 1024);
+  if (err != hipSuccess) return err;
   return launch_k(k_stream<T, MT, WN, EPI, R, LK, QB>, dim3((unsigned)blocks), dim3(256), lds, s, t.start, t.stop,
                   g, e);
 }

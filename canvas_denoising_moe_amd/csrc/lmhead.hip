@@ -346,12 +346,8 @@ hipError_t launch_lm_head(const LmArgs& a, int mode, hipStream_t s, KTime t) {
   const void* fns[3] = {reinterpret_cast<const void*>(&k_lm_head<LM_STORE>),
                         reinterpret_cast<const void*>(&k_lm_head<LM_ARGMAX>),
                         reinterpret_cast<const void*>(&k_lm_head<LM_SAMPLE>)};
-  static bool attr[3] = {false, false, false};
-  if (!attr[mode]) {
-    hipError_t err = hipFuncSetAttribute(fns[mode], hipFuncAttributeMaxDynamicSharedMemorySize, kLmLds);
-    if (err != hipSuccess) return err;
-    attr[mode] = true;
-  }
+  hipError_t err = ensure_lds_limit(fns[mode], kLmLds);
+  if (err != hipSuccess) return err;
   const dim3 grid((unsigned)blocks);
   if (mode == LM_STORE) return launch_k(k_lm_head<LM_STORE>, grid, dim3(256), kLmLds, s, t.start, t.stop, a);
   hipError_t e = mode == LM_ARGMAX ? launch_k(k_lm_head<LM_ARGMAX>, grid, dim3(256), kLmLds, s, t.start, nullptr, a)

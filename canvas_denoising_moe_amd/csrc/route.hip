@@ -255,13 +255,8 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (a.E > 256 || a.k > 8 || (a.mode != ROUTE_LOGITS && a.mode != ROUTE_GIVEN)) return hipErrorInvalidValue;
   const size_t lds = (size_t)a.E * ((a.rows + 31) / 32) * 8;  // bitmap + prefix counts
   if (lds > kRouteMaxLds) return hipErrorInvalidValue;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_route_scatter),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, kRouteMaxLds);
-    if (err != hipSuccess) return err;
-    attr_set = true;
-  }
+  hipError_t err = ensure_lds_limit(reinterpret_cast<const void*>(&k_route_scatter), kRouteMaxLds);
+  if (err != hipSuccess) return err;
   if (a.mode == ROUTE_LOGITS) {
     hipLaunchKernelGGL(k_route_topk, dim3(a.rows), dim3(64), 0, s, a);
     hipError_t e = hipGetLastError();
