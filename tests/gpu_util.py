@@ -78,7 +78,7 @@ def run_block_stepwise(torch, ctx, w, steps=None):
     return tok0, lk0, passes
 
 
-def shadow_compare(w, tok0, lk0, passes, delta_rel, conf_tol, weights=None):
+def shadow_compare(w, tok0, lk0, passes, delta_rel, conf_tol, weights=None, route_delta=None):
     m = w.model
     W = weights if weights is not None else weights_for(w, cache_layers=True)
     kvf = prompt_kv_fn(w)
@@ -90,7 +90,9 @@ def shadow_compare(w, tok0, lk0, passes, delta_rel, conf_tol, weights=None):
         sh = om.Shadow(route_idx=[p["trace"][l] for l in range(m.n_layers)], pred=p["pred"],
                        locked_after=p["locked"])
         trace = []
-        sh.delta_route = delta_rel  # router logits have unit-order RMS in these workloads
+        # router logits have unit-order RMS in these workloads unless the caller
+        # scales the delta to its own logit RMS
+        sh.delta_route = delta_rel if route_delta is None else route_delta
         sh.delta_logit = delta_rel
         sh.delta_conf = delta_rel * float(np.sqrt(np.mean(p["conf"].astype(np.float64) ** 2)))
         t_o, l_o, pred_o, conf_o, _ = om.denoise_pass(t_o, l_o, [w.n_steps - t] * w.batch, W, m, kvf,

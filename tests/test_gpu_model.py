@@ -94,3 +94,45 @@ def test_c1_lock_schedule_and_invariants(torch, dg):
         prev_t, prev_l = p["tokens"], p["locked"]
     assert counts == [8, 8, 8, 8]
     assert passes[-1]["locked"].all()
+
+
+def test_max_capacity_batch(torch, dg):
+    # the largest batch a context takes: 64 canvases of 64 slots = 4096 rows,
+    # 128 experts (E * ceil(rows / 32) = 16384, the scatter's LDS bound), a
+    # sliding window shorter than the prompt, pre-lock counts 0..63
+    import dataclasses
+
+    from synth import configs
+    m = configs.ModelConfig(n_layers=2, hidden=256, n_heads=4, n_kv_heads=2, head_dim=64, n_experts=128, top_k=8,
+                            expert_ffn=128, vocab=1024, canvas_len=64, window=64, global_layer_mask=0b10,
+                            dtype="bf16")
+    w = dataclasses.replace(C1, name="max-capacity-bf16", model=m, batch=64, prompt_len=96, n_steps=3, seed=91,
+                            router_std=2.0 / 256 ** 0.5, prelock=tuple(range(64)))
+    N = m.canvas_len
+    say("max-capacity block, batch", w.batch)
+    with dg.Context(m, max_batch=w.batch, max_prompt_len=w.prompt_len) as ctx:
+        upload.load_context(ctx, w)
+        tok0, lk0, passes = run_block_stepwise(torch, ctx, w)
+        assert passes[-1]["locked"].all()
+        # a canvas of the batched first pass equals that canvas run alone
+        for b in (0, 37, 63):
+            say("max-capacity canvas", b, "alone")
+            ks, vs = upload.prompt_kv_to_device(w, b)
+            ctx.load_prompt_kv(0, w.prompt_len, ks, vs)
+            tokens = torch.from_numpy(tok0[b:b + 1].copy()).cuda()
+            locked = torch.from_numpy(lk0[b:b + 1].copy()).cuda()
+            conf = torch.empty((1, N), dtype=torch.float32, device="cuda")
+            pred = torch.empty((1, N), dtype=torch.int32, device="cuda")
+            ctx.denoise_step(tokens, locked, [w.n_steps], conf, pred)
+            torch.cuda.synchronize()
+            p0 = passes[0]
+            assert np.array_equal(conf.cpu().numpy()[0], p0["conf"][b]), b
+            assert np.array_equal(pred.cpu().numpy()[0], p0["pred"][b]), b
+            assert np.array_equal(tokens.cpu().numpy()[0], p0["tokens"][b]), b
+            assert np.array_equal(locked.cpu().numpy()[0], p0["locked"][b]), b
+    # router logits here have an RMS of about router_std * sqrt(hidden) = 2: a
+    # routing decision may follow the GPU where the oracle's margin lies within
+    # the bf16 tolerance of that scale
+    report, worst = shadow_compare(w, tok0, lk0, passes, DELTA_REL["bf16"], TOL["bf16"],
+                                   route_delta=TOL["bf16"] * 2.0)
+    print(f"max-capacity batch: adopted {report}, worst conf rel err {worst:.3e}")
