@@ -207,9 +207,11 @@ def test_fused_lm_head_sampler_mode(torch, dg, t, t_max):
 # whole EB blocks on small models
 # --------------------------------------------------------------------------
 
-def _eb_block(torch, dg, w, t_max, seeds, block=0):
+def _eb_block(torch, dg, w, t_max, seeds, block=0, delta_scale=1.0):
     """Pass by pass: the GPU's EB step against the oracle's, shadowed; then
-    dg_generate_block_eb from the same start must give the same block."""
+    dg_generate_block_eb from the same start must give the same block.
+    delta_scale widens the shadow deltas (routing and logits) for workloads
+    with many more near-ties than the small ones."""
     m = w.model
     B, N, L = w.batch, m.canvas_len, m.n_layers
     tok0, lk0 = gen.canvas(w)
@@ -239,7 +241,7 @@ def _eb_block(torch, dg, w, t_max, seeds, block=0):
             tr = trace.cpu().numpy()
             st = status.cpu().numpy()
             # the oracle's logits of this pass, the GPU's routing adopted at near-ties
-            sh = om.Shadow(route_idx=[tr[l] for l in range(L)], delta_route=DELTA_REL[m.dtype])
+            sh = om.Shadow(route_idx=[tr[l] for l in range(L)], delta_route=DELTA_REL[m.dtype] * delta_scale)
             x = W.embed_rows(t_o.reshape(-1).astype(np.int64)).copy()
             x = om.forward_hidden(x, W, m, kvf, [w.prompt_len] * B, shadow=sh)
             h = rnd(om.rmsnorm(x, W.norm_final(), m.rms_eps))
@@ -251,7 +253,7 @@ def _eb_block(torch, dg, w, t_max, seeds, block=0):
             herr = float(np.max(np.abs(g_ent - Hs) / (1.0 + Hs)))
             rms = float(np.sqrt(np.mean(lg ** 2)))
             esh = eb.EBShadow(sample=samp.cpu().numpy(), pred=pred.cpu().numpy(), locked_after=locked.cpu().numpy(),
-                              stopped=(st & 4) != 0, dlogit=DELTA_REL[m.dtype] * max(1.0, rms))
+                              stopped=(st & 4) != 0, dlogit=DELTA_REL[m.dtype] * delta_scale * max(1.0, rms))
             t_o, l_o, info = eb.eb_update(lg, t_o, l_o, t, state, seeds, block, t_max, shadow=esh)
             assert not esh.failures, esh.failures[:3]
             for k in ("sample", "pred", "lock", "stop"):
@@ -297,3 +299,19 @@ def test_eb_block_bf16_two_canvases_with_prelocks(torch, dg):
     w = dataclasses.replace(LM_BF16, name="eb-bf16-2", prelock=(0, 12), final_norm_shift=40.0)
     passes = _eb_block(torch, dg, w, 48, [21, 22], block=5)
     assert all(p >= 1 for p in passes)
+
+
+def test_eb_block_max_capacity_batch(torch, dg):
+    # 64 canvases of 64 slots (4096 rows, the most a context takes; 64 canvases
+    # is also the sampler-mode LM head's bound), 128 experts top-8, pre-lock
+    # counts 0..63, every canvas with its own seed
+    m = configs.ModelConfig(n_layers=2, hidden=256, n_heads=4, n_kv_heads=2, head_dim=64, n_experts=128, top_k=8,
+                            expert_ffn=128, vocab=1024, canvas_len=64, window=64, global_layer_mask=0b10,
+                            dtype="bf16")
+    w = dataclasses.replace(C1, name="eb-max-capacity", model=m, batch=64, prompt_len=96, n_steps=4, seed=93,
+                            prelock=tuple(range(64)), final_norm_shift=40.0)
+    # 4096 positions hold far more near-ties than the small workloads: the
+    # shadow deltas are 3% of the logits' RMS here (the bf16 tolerance, 2e-2
+    # of the largest logit, is about 8% of the RMS of Gaussian logits)
+    passes = _eb_block(torch, dg, w, 6, list(range(1000, 1064)), block=2, delta_scale=3.0)
+    assert all(1 <= p <= 6 for p in passes)
