@@ -136,3 +136,16 @@ def test_max_capacity_batch(torch, dg):
     report, worst = shadow_compare(w, tok0, lk0, passes, DELTA_REL["bf16"], TOL["bf16"],
                                    route_delta=TOL["bf16"] * 2.0)
     print(f"max-capacity batch: adopted {report}, worst conf rel err {worst:.3e}")
+    # unshadowed: the oracle's own block from the same start, every decision its
+    # own; the share of final canvas tokens equal to the GPU's
+    W = weights_for(w, cache_layers=True)
+    t_o, l_o = tok0, lk0
+    for t in range(w.n_steps):
+        t_o, l_o, _, _, _ = om.denoise_pass(t_o, l_o, [w.n_steps - t] * w.batch, W, m, prompt_kv_fn(w),
+                                            [w.prompt_len] * w.batch)
+    agree = float(np.mean(t_o == passes[-1]["tokens"]))
+    print(f"max-capacity batch: final canvas tokens equal to the unshadowed oracle's: {agree:.4%}")
+    # measured 96.46%: every routing or argmax near-tie the two sides decide
+    # differently changes that token's later context (random-init logits are
+    # nearly flat); the deterministic GPU path keeps this figure fixed
+    assert agree >= 0.95
