@@ -93,6 +93,13 @@ def c3ctx(torch, dg):
     torch.cuda.empty_cache()
 
 
+@pytest.fixture(scope="module")
+def c3_oracle():
+    # the oracle's float64 layers of the 30-layer workload, generated once for
+    # every test of this module that runs the oracle's whole stack
+    return _oracle_weights(C3, cache_layers=True)
+
+
 def _stack_tolerance():
     """End-to-end tolerance of the 30-layer bf16 stack: four times the
     oracle's own response, after 30 layers, to a half-ulp perturbation of its
@@ -105,13 +112,13 @@ def _stack_tolerance():
         return 4.0 * json.load(f)["rel_diff_max"]
 
 
-def test_c3_first_pass_matches_oracle(torch, c3ctx):
+def test_c3_first_pass_matches_oracle(torch, c3ctx, c3_oracle):
     w = C3
     m = w.model
     M = w.batch * m.canvas_len
     say("C3 first pass")
     tok0, lk0, passes = run_block_stepwise(torch, c3ctx, w, steps=1)
-    W = _oracle_weights(w, cache_layers=True)
+    W = c3_oracle
     kvf = prompt_kv_fn(w)
 
     # layer by layer from the GPU's own input to each layer: every layer meets
@@ -243,7 +250,7 @@ def test_c3_fused_sampler_on_its_own_logits(torch, c3ctx):
     print(f"C3 fused sampler: {int((mine == got).sum())}/{rows.size} sampled rows identical")
 
 
-def test_c3_eb_pass_matches_oracle(torch, c3ctx):
+def test_c3_eb_pass_matches_oracle(torch, c3ctx, c3_oracle):
     # one entropy-bounded pass of the full stack against the oracle, decisions shadowed
     w = C3
     m = w.model
@@ -265,7 +272,7 @@ def test_c3_eb_pass_matches_oracle(torch, c3ctx):
     c3ctx.set_trace(None)
     tol = _stack_tolerance()
     tr = trace.cpu().numpy()
-    W = _oracle_weights(w, cache_layers=True)
+    W = c3_oracle
     kvf = prompt_kv_fn(w)
     sh = om.Shadow(route_idx=[tr[l] for l in range(L)], delta_route=tol)
     x = W.embed_rows(tok0.reshape(-1).astype(np.int64)).copy()
@@ -321,7 +328,40 @@ def test_c3_moe_sampled_tokens(torch, c3ctx):
 
 # ------------------------------------------ 256 canvas, 131072 prompt ----
 
-def test_c3_block_commit_sampled_layers(torch, c3ctx):
+def test_c3_block_final_tokens_unshadowed(torch, c3ctx, c3_oracle):
+    # the whole 8-pass block on the GPU and, from the same start, the oracle's
+    # own block with every decision its own: the share of final canvas tokens
+    # they agree on
+    w = C3
+    say("C3 block")
+    tok0, lk0, passes = run_block_stepwise(torch, c3ctx, w)
+    _check_schedule(w, tok0, lk0, passes)
+    kvf = prompt_kv_fn(w)
+    t_o, l_o = tok0, lk0
+    first = None
+    for t in range(w.n_steps):
+        print(f"[oracle] C3 pass {t}", flush=True)
+        t_o, l_o, pred_o, _, _ = om.denoise_pass(t_o, l_o, [w.n_steps - t] * w.batch, c3_oracle, w.model, kvf,
+                                                 [w.prompt_len] * w.batch)
+        first = pred_o if first is None else first
+    assert l_o.all()
+    agree = float(np.mean(t_o == passes[-1]["tokens"]))
+    agree1 = float(np.mean(first == passes[0]["pred"]))
+    # the oracle against itself with its input moved by half a bf16 ulp
+    # (tests/golden/agreement_c3.json, written by the oracle alone): the
+    # agreement that rounding noise leaves on these nearly flat logits
+    with open(os.path.join(GOLDEN, "agreement_c3.json")) as f:
+        floor = json.load(f)
+    print(f"C3 block: final canvas tokens equal to the unshadowed oracle's: {agree:.2%} "
+          f"(oracle vs half-ulp-perturbed oracle: {floor['final_token_agreement']:.2%}); first-pass argmax "
+          f"{agree1:.2%} ({floor['first_pass_argmax_agreement']:.2%})")
+    # a wrong path would agree on almost nothing (262144 ids); a correct one
+    # sits at the noise floor
+    assert agree >= 0.5 * floor["final_token_agreement"]
+    assert agree1 >= 0.9 * floor["first_pass_argmax_agreement"]
+
+
+def test_c3_block_commit_sampled_layers(torch, c3ctx, c3_oracle):
     # block continuation at full size, last on this context (it grows the
     # caches): the copied part of each cache is bit-exact, the block's K/V
     # meet the one-layer tolerance on layer 0 and the stack's end-to-end
@@ -346,7 +386,7 @@ def test_c3_block_commit_sampled_layers(torch, c3ctx):
     c3ctx.set_trace(None)
     tr = trace.cpu().numpy()
     tol = _stack_tolerance()
-    W = _oracle_weights(w, cache_layers=True)
+    W = c3_oracle
     kvf = prompt_kv_fn(w)
     sh = om.Shadow(route_idx=[tr[l] for l in range(L - 1)] + [None], delta_route=tol)
     blk = om.commit_block(tok0, W, m, kvf, [w.prompt_len], shadow=sh)
