@@ -392,6 +392,65 @@ def _shadow_route(sh: Shadow, layer: int):
     return override
 
 
+def adopt_pred(logits: np.ndarray, pred: np.ndarray, conf: np.ndarray, sh: Shadow) -> None:
+    """Shadowed argmax: where the GPU's token differs from the oracle's, the
+    oracle takes it when its own logit margin for the GPU's token (its best
+    logit minus the GPU token's logit) is at most ``sh.delta_logit``, and then
+    reports that token's probability as the confidence; otherwise the
+    difference is a failure.  ``logits [B, N, V]``; ``pred, conf [B, N]`` are
+    updated in place."""
+    B, N = pred.shape
+    for b in range(B):
+        for i in range(N):
+            gp = int(sh.pred[b, i])
+            if gp == int(pred[b, i]):
+                continue
+            margin = float(logits[b, i, pred[b, i]] - logits[b, i, gp])
+            if margin <= sh.delta_logit:
+                sh.adopted["pred"] += 1
+                sh.max_margin["pred"] = max(sh.max_margin["pred"], margin)
+                pred[b, i] = gp
+                conf[b, i] = 1.0 / np.exp(logits[b, i] - logits[b, i, gp]).sum()
+            else:
+                sh.failures.append(f"pred canvas {b} pos {i}: gpu {gp} oracle "
+                                   f"{int(pred[b, i])} margin {margin:.3e}")
+
+
+def adopt_locks(conf: np.ndarray, pred: np.ndarray, tokens: np.ndarray, locked: np.ndarray,
+                new_tokens: np.ndarray, new_locked: np.ndarray, chosen: Sequence[np.ndarray],
+                sh: Shadow) -> None:
+    """Shadowed lock step: where the GPU locked another set of positions than
+    the oracle's ``chosen``, the oracle takes the GPU's set when it has the
+    same size and the most confident position the GPU left unlocked beats the
+    least confident one it locked by at most ``sh.delta_conf`` (by the oracle's
+    confidences); otherwise the difference is a failure.  ``new_tokens,
+    new_locked`` are updated in place."""
+    B = tokens.shape[0]
+    for b in range(B):
+        gsel = set(np.nonzero((sh.locked_after[b] == 1) & (locked[b] == 0))[0].tolist())
+        osel = set(chosen[b].tolist())
+        if gsel == osel:
+            continue
+        free = np.nonzero(locked[b] == 0)[0]
+        rest = [i for i in free.tolist() if i not in gsel]
+        if gsel:
+            worst_in = float(min(conf[b, list(gsel)]))
+            best_out = float(max(conf[b, rest])) if rest else -np.inf
+            margin = best_out - worst_in
+        else:
+            margin = np.inf
+        if len(gsel) == len(osel) and margin <= sh.delta_conf:
+            sh.adopted["lock"] += 1
+            sh.max_margin["lock"] = max(sh.max_margin["lock"], float(margin))
+            sel = np.array(sorted(gsel), dtype=np.int64)
+            new_tokens[b] = tokens[b]
+            new_locked[b] = locked[b]
+            new_tokens[b, sel] = pred[b, sel]
+            new_locked[b, sel] = 1
+        else:
+            sh.failures.append(f"lock canvas {b}: margin {margin:.3e}")
+
+
 # --------------------------------------------------------------------------
 # one layer, one pass, one block
 # --------------------------------------------------------------------------
@@ -537,46 +596,10 @@ def denoise_pass(tokens: np.ndarray, locked: np.ndarray, steps_left: Sequence[in
     pred = pred.reshape(B, N)
     conf = conf.reshape(B, N)
     if shadow is not None and shadow.pred is not None:
-        lg = logits.reshape(B, N, -1)
-        for b in range(B):
-            for i in range(N):
-                gp = int(shadow.pred[b, i])
-                if gp == int(pred[b, i]):
-                    continue
-                margin = float(lg[b, i, pred[b, i]] - lg[b, i, gp])
-                if margin <= shadow.delta_logit:
-                    shadow.adopted["pred"] += 1
-                    shadow.max_margin["pred"] = max(shadow.max_margin["pred"], margin)
-                    pred[b, i] = gp
-                    conf[b, i] = 1.0 / np.exp(lg[b, i] - lg[b, i, gp]).sum()
-                else:
-                    shadow.failures.append(f"pred canvas {b} pos {i}: gpu {gp} oracle "
-                                           f"{int(pred[b, i])} margin {margin:.3e}")
+        adopt_pred(logits.reshape(B, N, -1), pred, conf, shadow)
     new_tokens, new_locked, chosen = lock_select(conf, pred, tokens, locked, steps_left)
     if shadow is not None and shadow.locked_after is not None:
-        for b in range(B):
-            gsel = set(np.nonzero((shadow.locked_after[b] == 1) & (locked[b] == 0))[0].tolist())
-            osel = set(chosen[b].tolist())
-            if gsel == osel:
-                continue
-            free = np.nonzero(locked[b] == 0)[0]
-            rest = [i for i in free.tolist() if i not in gsel]
-            if gsel:
-                worst_in = float(min(conf[b, list(gsel)]))
-                best_out = float(max(conf[b, rest])) if rest else -np.inf
-                margin = best_out - worst_in
-            else:
-                margin = np.inf
-            if len(gsel) == len(osel) and margin <= shadow.delta_conf:
-                shadow.adopted["lock"] += 1
-                shadow.max_margin["lock"] = max(shadow.max_margin["lock"], float(margin))
-                sel = np.array(sorted(gsel), dtype=np.int64)
-                new_tokens[b] = tokens[b]
-                new_locked[b] = locked[b]
-                new_tokens[b, sel] = pred[b, sel]
-                new_locked[b, sel] = 1
-            else:
-                shadow.failures.append(f"lock canvas {b}: margin {margin:.3e}")
+        adopt_locks(conf, pred, tokens, locked, new_tokens, new_locked, chosen, shadow)
     return new_tokens, new_locked, pred, conf, h
 
 
