@@ -136,6 +136,18 @@ def _ptr(t, dtype=None, name="tensor"):
     return c_void_p(t.data_ptr())
 
 
+def _need(t, n: int, name: str):
+    """Element count check ahead of a C call: a tensor shorter than the call
+    reads or writes would send a kernel or a copy out of bounds.  None
+    passes (optional outputs)."""
+    if t is None:
+        return
+    if not hasattr(t, "numel"):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if int(t.numel()) != int(n):
+        raise ValueError(f"{name}: {int(t.numel())} elements, expected {int(n)}")
+
+
 def _stream(stream):
     import torch
     if stream is None:
@@ -219,18 +231,75 @@ class Context:
     def _c(self, status):
         _check(status, self._h)
 
+    # -- argument sizes (checked before any C call) ------------------------------
+    def _batch(self, B: int) -> int:
+        B = int(B)
+        if not 1 <= B <= self.max_batch:
+            raise ValueError(f"batch {B} outside [1, {self.max_batch}]")
+        return B
+
+    def _canvas(self, tokens, **named):
+        """Batch of ``tokens [B, N]``; every other tensor holds B*N entries."""
+        if tokens is None or not hasattr(tokens, "shape") or tokens.dim() != 2:
+            raise ValueError("tokens: expected a [batch, canvas_len] tensor")
+        N = self.model.canvas_len
+        if int(tokens.shape[1]) != N:
+            raise ValueError(f"tokens: {int(tokens.shape[1])} positions per canvas, expected {N}")
+        B = self._batch(tokens.shape[0])
+        for name, buf in named.items():
+            _need(buf, B * N, name)
+        return B
+
+    def _rows(self, x, width: int, name: str) -> int:
+        """Batch of a row-major ``[B*N, width]`` tensor."""
+        N = self.model.canvas_len
+        n = int(x.numel()) if hasattr(x, "numel") else -1
+        if n <= 0 or n % (N * width):
+            raise ValueError(f"{name}: {n} elements is not a whole number of canvases of {N} x {width}")
+        return self._batch(n // (N * width))
+
+    def _trace_ok(self, B: int):
+        t = self._keep[0] if self._keep else None
+        if t is not None:
+            need = self.model.n_layers * B * self.model.canvas_len * self.model.top_k
+            if int(t.numel()) < need:
+                raise ValueError(f"route trace holds {int(t.numel())} entries, a batch of {B} records {need}")
+
     # -- weights and prompt ----------------------------------------------------
+    def _layer_sizes(self):
+        m = self.model
+        H, F, E = m.hidden, m.expert_ffn, m.n_experts
+        q, kv = m.n_heads * m.head_dim, m.n_kv_heads * m.head_dim
+        return {"wq": H * q, "wk": H * kv, "wv": H * kv, "wo": q * H, "router": H * E,
+                "w_gate": E * H * F, "w_up": E * H * F, "w_down": E * F * H,
+                "sh_gate": H * F, "sh_up": H * F, "sh_down": F * H,
+                "norm_in": H, "norm_pa": H, "norm_pf": H, "norm_pf2": H}
+
+    def _check_layer(self, w: dict):
+        for n, size in self._layer_sizes().items():
+            _need(w[n], size, n)
+
     def set_layer_weights(self, layer: int, w: dict):
+        self._check_layer(w)
         lw = DGLayerWeights()
         for n in LAYER_FIELDS:
             setattr(lw, n, _ptr(w[n], self.wdtype, n))
         self._c(lib().dg_set_layer_weights(self._h, layer, ctypes.byref(lw)))
 
     def set_embedding(self, embed, norm_final):
+        _need(embed, self.model.vocab * self.model.hidden, "embed")
+        _need(norm_final, self.model.hidden, "norm_final")
         self._c(lib().dg_set_embedding(self._h, _ptr(embed, self.wdtype, "embed"),
                                        _ptr(norm_final, self.wdtype, "norm_final")))
 
     def init_weights(self, embed, norm_final, layers: Sequence[dict]):
+        if len(layers) != self.model.n_layers:
+            raise ValueError(f"{len(layers)} layers given, the model has {self.model.n_layers}")
+        if self.model.has_lm_head:
+            _need(embed, self.model.vocab * self.model.hidden, "embed")
+            _need(norm_final, self.model.hidden, "norm_final")
+        for w in layers:
+            self._check_layer(w)
         arr = (DGLayerWeights * len(layers))()
         for i, w in enumerate(layers):
             for n in LAYER_FIELDS:
@@ -239,6 +308,15 @@ class Context:
                                       _ptr(norm_final, self.wdtype, "norm_final"), arr))
 
     def load_prompt_kv(self, slot: int, prompt_len: int, ks: Sequence, vs: Sequence):
+        m = self.model
+        if len(ks) != m.n_layers or len(vs) != m.n_layers:
+            raise ValueError(f"k and v need one tensor per layer ({m.n_layers})")
+        for l in range(m.n_layers):
+            n_l = m.kv_len(l, prompt_len) * m.n_kv_heads * m.head_dim
+            for name, buf in (("k", ks[l]), ("v", vs[l])):
+                if n_l == 0 and (buf is None or buf.numel() == 0):
+                    continue
+                _need(buf, n_l, f"{name}[{l}]")
         n = len(ks)
         karr = (c_void_p * n)(*[_ptr(k, self.wdtype, "k") if k is not None and k.numel() else None for k in ks])
         varr = (c_void_p * n)(*[_ptr(v, self.wdtype, "v") if v is not None and v.numel() else None for v in vs])
@@ -247,7 +325,10 @@ class Context:
     # -- the pass --------------------------------------------------------------
     def denoise_step(self, tokens, locked, steps_left: Sequence[int], conf=None, pred=None):
         import torch
-        B = tokens.shape[0]
+        B = self._canvas(tokens, locked=locked, conf=conf, pred=pred)
+        if len(steps_left) != B:
+            raise ValueError(f"{len(steps_left)} steps_left values for a batch of {B}")
+        self._trace_ok(B)
         sl = (c_int32 * B)(*[int(s) for s in steps_left])
         self._c(lib().dg_denoise_step(self._h, B, _ptr(tokens, torch.int32, "tokens"),
                                       _ptr(locked, torch.uint8, "locked"), sl,
@@ -255,6 +336,7 @@ class Context:
 
     def generate_block(self, tokens, locked, n_steps: int):
         import torch
+        self._trace_ok(self._canvas(tokens, locked=locked))
         self._c(lib().dg_generate_block(self._h, tokens.shape[0], n_steps, _ptr(tokens, torch.int32, "tokens"),
                                         _ptr(locked, torch.uint8, "locked")))
 
@@ -264,7 +346,9 @@ class Context:
         """One EB pass (dg_eb_step); ``prev_pred [B, N]`` and ``status [B]``
         (int32, device) carry the per-canvas state between passes."""
         import torch
-        B = tokens.shape[0]
+        B = self._canvas(tokens, locked=locked, prev_pred=prev_pred, entropy=entropy, sample=sample, pred=pred)
+        _need(status, B, "status")
+        self._trace_ok(B)
         sd = _seeds(seeds, B)
         self._c(lib().dg_eb_step(self._h, B, _ptr(tokens, torch.int32, "tokens"), _ptr(locked, torch.uint8, "locked"),
                                  t, t_max, sd, block, _ptr(prev_pred, torch.int32, "prev_pred"),
@@ -275,7 +359,8 @@ class Context:
         """EB passes until every canvas is done (dg_generate_block_eb); returns
         the number of passes after which each canvas was done."""
         import torch
-        B = tokens.shape[0]
+        B = self._canvas(tokens, locked=locked)
+        self._trace_ok(B)
         sd = _seeds(seeds, B)
         passes = (c_int32 * B)()
         self._c(lib().dg_generate_block_eb(self._h, B, _ptr(tokens, torch.int32, "tokens"),
@@ -286,12 +371,14 @@ class Context:
         """Commit the canvases ``tokens [batch, N]`` (int32, device) to the
         prompt KV caches (dg_commit_block): every slot's prompt_len grows by N."""
         import torch
+        self._trace_ok(self._canvas(tokens))
         self._c(lib().dg_commit_block(self._h, tokens.shape[0], _ptr(tokens, torch.int32, "tokens")))
 
     def commit_tokens(self, tokens, n: int):
         """Commit the first ``n`` tokens of each row of ``tokens [batch, N]``
         (dg_commit_tokens): every slot's prompt_len grows by n."""
         import torch
+        self._trace_ok(self._canvas(tokens))
         self._c(lib().dg_commit_tokens(self._h, tokens.shape[0], _ptr(tokens, torch.int32, "tokens"), int(n)))
 
     def prefill(self, tokens):
@@ -314,6 +401,9 @@ class Context:
 
     def get_prompt_kv(self, slot: int, layer: int, k, v):
         """Copy the slot's cache of one layer into ``k, v [len, Hkv, D]``."""
+        n = self.prompt_kv_len(slot, layer) * self.model.n_kv_heads * self.model.head_dim
+        _need(k, n, "k")
+        _need(v, n, "v")
         self._c(lib().dg_get_prompt_kv(self._h, slot, layer, _ptr(k, self.wdtype, "k"),
                                        _ptr(v, self.wdtype, "v"), None))
 
@@ -321,18 +411,27 @@ class Context:
         """One expert matrix as the GEMMs use it (dg_get_expert_weight): which
         0 gate [H, F], 1 up [H, F], 2 down [F, H]; MXFP4 codes / scales too."""
         import torch
+        m = self.model
+        K, N = (m.expert_ffn, m.hidden) if which == 2 else (m.hidden, m.expert_ffn)
+        _need(values, K * N, "values")
+        _need(codes, K * N, "codes")
+        _need(scales, (K // 32) * N, "scales")
         self._c(lib().dg_get_expert_weight(self._h, layer, expert, which, _ptr(values, self.wdtype, "values"),
                                            _ptr(codes, torch.uint8, "codes"), _ptr(scales, torch.uint8, "scales")))
 
     def forward_hidden(self, x_in, x_out):
         import torch
-        B = x_in.shape[0] // self.model.canvas_len
+        B = self._rows(x_in, self.model.hidden, "x_in")
+        _need(x_out, x_in.numel(), "x_out")
+        self._trace_ok(B)
         self._c(lib().dg_forward_hidden(self._h, B, _ptr(x_in, torch.float32, "x_in"),
                                         _ptr(x_out, torch.float32, "x_out")))
 
     def forward_layers(self, first: int, count: int, x_in, x_out):
         import torch
-        B = x_in.shape[0] // self.model.canvas_len
+        B = self._rows(x_in, self.model.hidden, "x_in")
+        _need(x_out, x_in.numel(), "x_out")
+        self._trace_ok(B)
         self._c(lib().dg_forward_layers(self._h, B, first, count, _ptr(x_in, torch.float32, "x_in"),
                                         _ptr(x_out, torch.float32, "x_out")))
 
@@ -362,32 +461,60 @@ class Context:
 
     # -- single kernels ----------------------------------------------------------
     def k_qkv(self, layer: int, batch: int, a, q, k, v):
+        m = self.model
+        M = self._batch(batch) * m.canvas_len
+        _need(a, M * m.hidden, "a")
+        _need(q, M * m.n_heads * m.head_dim, "q")
+        _need(k, M * m.n_kv_heads * m.head_dim, "k")
+        _need(v, M * m.n_kv_heads * m.head_dim, "v")
         self._c(lib().dg_k_qkv(self._h, layer, batch, _ptr(a, self.wdtype, "a"), _ptr(q, self.wdtype, "q"),
                                _ptr(k, self.wdtype, "k"), _ptr(v, self.wdtype, "v")))
 
     def k_canvas_attn(self, layer: int, batch: int, q, k, v, o, canvas_keys: bool = True):
+        m = self.model
+        M = self._batch(batch) * m.canvas_len
+        _need(q, M * m.n_heads * m.head_dim, "q")
+        _need(k, M * m.n_kv_heads * m.head_dim, "k")
+        _need(v, M * m.n_kv_heads * m.head_dim, "v")
+        _need(o, M * m.n_heads * m.head_dim, "o")
         self._c(lib().dg_k_canvas_attn(self._h, layer, batch, _ptr(q, self.wdtype, "q"),
                                        _ptr(k, self.wdtype, "k"), _ptr(v, self.wdtype, "v"),
                                        _ptr(o, self.wdtype, "o"), int(bool(canvas_keys))))
 
     def k_moe_ffn(self, layer: int, batch: int, f, idx, gates, m):
         import torch
+        M = self._batch(batch) * self.model.canvas_len
+        _need(f, M * self.model.hidden, "f")
+        _need(idx, M * self.model.top_k, "idx")
+        _need(gates, M * self.model.top_k, "gates")
+        _need(m, M * self.model.hidden, "m")
         self._c(lib().dg_k_moe_ffn(self._h, layer, batch, _ptr(f, self.wdtype, "f"),
                                    _ptr(idx, torch.int32, "idx"), _ptr(gates, torch.float32, "gates"),
                                    _ptr(m, torch.float32, "m")))
 
     def k_lm_head(self, batch: int, h, logits):
         import torch
+        M = self._batch(batch) * self.model.canvas_len
+        _need(h, M * self.model.hidden, "h")
+        _need(logits, M * self.model.vocab, "logits")
         self._c(lib().dg_k_lm_head(self._h, batch, _ptr(h, self.wdtype, "h"),
                                    _ptr(logits, torch.float32, "logits")))
 
     def k_lm_argmax(self, batch: int, h, pred, conf):
         import torch
+        M = self._batch(batch) * self.model.canvas_len
+        _need(h, M * self.model.hidden, "h")
+        _need(pred, M, "pred")
+        _need(conf, M, "conf")
         self._c(lib().dg_k_lm_argmax(self._h, batch, _ptr(h, self.wdtype, "h"),
                                      _ptr(pred, torch.int32, "pred"), _ptr(conf, torch.float32, "conf")))
 
     def k_lm_sample(self, batch: int, h, t: int, t_max: int, seeds: Sequence[int], block: int, pred, entropy, sample):
         import torch
+        M = self._batch(batch) * self.model.canvas_len
+        _need(h, M * self.model.hidden, "h")
+        for name, buf in (("pred", pred), ("entropy", entropy), ("sample", sample)):
+            _need(buf, M, name)
         sd = _seeds(seeds, batch)
         self._c(lib().dg_k_lm_sample(self._h, batch, _ptr(h, self.wdtype, "h"), t, t_max, sd, block,
                                      _ptr(pred, torch.int32, "pred"), _ptr(entropy, torch.float32, "entropy"),
@@ -404,6 +531,8 @@ def k_eb_rows(logits, canvas_len: int, t: int, t_max: int, seeds: Sequence[int],
               stream=None):
     import torch
     rows, V = logits.shape
+    for name, buf in (("pred", pred), ("entropy", entropy), ("sample", sample)):
+        _need(buf, rows, name)
     sd = _seeds(seeds, rows // canvas_len)
     _check(lib().dg_k_eb_rows(_ptr(logits, torch.float32, "logits"), rows, V, canvas_len, t, t_max, sd, block,
                               _ptr(pred, torch.int32, "pred"), _ptr(entropy, torch.float32, "entropy"),
@@ -412,6 +541,7 @@ def k_eb_rows(logits, canvas_len: int, t: int, t_max: int, seeds: Sequence[int],
 
 def k_eb_noise(rows: int, vocab: int, canvas_len: int, t: int, seeds: Sequence[int], block: int, noise, stream=None):
     import torch
+    _need(noise, rows * vocab, "noise")
     sd = _seeds(seeds, rows // canvas_len)
     _check(lib().dg_k_eb_noise(rows, vocab, canvas_len, t, sd, block, _ptr(noise, torch.float32, "noise"),
                                _stream(stream)))
@@ -420,6 +550,10 @@ def k_eb_noise(rows: int, vocab: int, canvas_len: int, t: int, seeds: Sequence[i
 def k_eb_select(entropy, sample, pred, tokens, locked, prev_pred, status, t: int, t_max: int, stream=None):
     import torch
     B, N = tokens.shape
+    for name, buf in (("entropy", entropy), ("sample", sample), ("pred", pred), ("locked", locked),
+                    ("prev_pred", prev_pred)):
+        _need(buf, B * N, name)
+    _need(status, B, "status")
     _check(lib().dg_k_eb_select(B, N, _ptr(entropy, torch.float32, "entropy"), _ptr(sample, torch.int32, "sample"),
                                 _ptr(pred, torch.int32, "pred"), _ptr(tokens, torch.int32, "tokens"),
                                 _ptr(locked, torch.uint8, "locked"), _ptr(prev_pred, torch.int32, "prev_pred"),
@@ -429,6 +563,8 @@ def k_eb_select(entropy, sample, pred, tokens, locked, prev_pred, status, t: int
 def k_argmax_conf(logits, pred, conf, stream=None):
     import torch
     rows, V = logits.shape
+    _need(pred, rows, "pred")
+    _need(conf, rows, "conf")
     _check(lib().dg_k_argmax_conf(_ptr(logits, torch.float32, "logits"), rows, V,
                                   _ptr(pred, torch.int32, "pred"), _ptr(conf, torch.float32, "conf"),
                                   _stream(stream)))
@@ -437,6 +573,10 @@ def k_argmax_conf(logits, pred, conf, stream=None):
 def k_lock_select(conf, pred, tokens, locked, steps_left: Sequence[int], stream=None):
     import torch
     B, N = tokens.shape
+    for name, buf in (("conf", conf), ("pred", pred), ("locked", locked)):
+        _need(buf, B * N, name)
+    if len(steps_left) != B:
+        raise ValueError(f"{len(steps_left)} steps_left values for a batch of {B}")
     sl = (c_int32 * max(1, B))(*[int(s) for s in steps_left])
     _check(lib().dg_k_lock_select(B, N, _ptr(conf, torch.float32, "conf"), _ptr(pred, torch.int32, "pred"),
                                   _ptr(tokens, torch.int32, "tokens"), _ptr(locked, torch.uint8, "locked"),
@@ -446,6 +586,11 @@ def k_lock_select(conf, pred, tokens, locked, steps_left: Sequence[int], stream=
 def k_moe_route(logits, top_k: int, idx, gates, counts=None, offsets=None, perm=None, stream=None):
     import torch
     rows, E = logits.shape
+    _need(idx, rows * top_k, "idx")
+    _need(gates, rows * top_k, "gates")
+    _need(counts, E, "counts")
+    _need(offsets, E + 2, "offsets")
+    _need(perm, rows * top_k, "perm")
     _check(lib().dg_k_moe_route(_ptr(logits, torch.float32, "logits"), rows, E, top_k,
                                 _ptr(idx, torch.int32, "idx"), _ptr(gates, torch.float32, "gates"),
                                 _ptr(counts, torch.int32, "counts"), _ptr(offsets, torch.int32, "offsets"),

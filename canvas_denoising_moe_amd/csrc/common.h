@@ -240,8 +240,10 @@ struct NormArgs {
   float* x; const float* delta; const void* w_delta; const void* w_out; void* out;
 };
 hipError_t launch_residual_norm(int is_bf16, const NormArgs& a, hipStream_t s);
-hipError_t launch_embed(int is_bf16, const int32_t* tokens, int rows, int H, int V,
-                        const void* packed_embed, float* x, hipStream_t s);
+// Embedding gather; ids outside [0, V) read as zero rows and, at positions
+// t % N < valid_n, are recorded in *bad (NULL: not recorded), see moe.hip.
+hipError_t launch_embed(int is_bf16, const int32_t* tokens, int rows, int H, int V, int N, int valid_n,
+                        const void* packed_embed, float* x, uint64_t* bad, hipStream_t s);
 hipError_t launch_rope_table(float2* cs, int N, int D, int prompt_len, double theta, hipStream_t s);
 
 // ----------------------------------------------------------------------------

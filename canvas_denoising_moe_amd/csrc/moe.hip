@@ -134,10 +134,13 @@ hipError_t run_residual_norm(const NormArgs& a, hipStream_t s) {
 }
 
 // x[t, h] = E[token_t, h] read from the fragment-packed embedding
-// ([V/16][H/32][64][8]); ids outside [0, V) read as zero rows.
+// ([V/16][H/32][64][8]).  An id outside [0, V) reads as a zero row; when its
+// position i = t % N lies below valid_n, the row and the id are recorded in
+// *bad as ((t + 1) << 32) | id (one 64-bit store per row, by the thread of
+// column 0: any recorded pair is a complete one).
 template <typename T>
-__global__ void k_embed(const int32_t* __restrict__ tokens, int rows, int H, int V,
-                        const T* __restrict__ pe, float* __restrict__ x) {
+__global__ void k_embed(const int32_t* __restrict__ tokens, int rows, int H, int V, int N, int valid_n,
+                        const T* __restrict__ pe, float* __restrict__ x, uint64_t* bad) {
   const long long total = (long long)rows * H;
   const int KB = H >> 5;
   for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < total;
@@ -148,6 +151,8 @@ __global__ void k_embed(const int32_t* __restrict__ tokens, int rows, int H, int
     if (v >= 0 && v < V) {
       const long long o = (((long long)(v >> 4) * KB + (h >> 5)) * 64 + (v & 15) + 16 * ((h & 31) >> 3)) * 8 + (h & 7);
       val = to_f<T>(pe[o]);
+    } else if (h == 0 && bad && (t % N) < valid_n) {
+      *bad = ((uint64_t)(uint32_t)(t + 1) << 32) | (uint32_t)v;
     }
     x[i] = val;
   }
@@ -174,17 +179,18 @@ hipError_t launch_residual_norm(int is_bf16, const NormArgs& a, hipStream_t s) {
   return is_bf16 ? run_residual_norm<bf16_t>(a, s) : run_residual_norm<float>(a, s);
 }
 
-hipError_t launch_embed(int is_bf16, const int32_t* tokens, int rows, int H, int V, const void* pe,
-                        float* x, hipStream_t s) {
+hipError_t launch_embed(int is_bf16, const int32_t* tokens, int rows, int H, int V, int N, int valid_n,
+                        const void* pe, float* x, uint64_t* bad, hipStream_t s) {
   const long long total = (long long)rows * H;
   if (total <= 0) return hipSuccess;
+  if (N <= 0) return hipErrorInvalidValue;
   const unsigned blocks = (unsigned)((total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536);
   if (is_bf16)
-    hipLaunchKernelGGL(k_embed<bf16_t>, dim3(blocks), dim3(256), 0, s, tokens, rows, H, V,
-                       reinterpret_cast<const bf16_t*>(pe), x);
+    hipLaunchKernelGGL(k_embed<bf16_t>, dim3(blocks), dim3(256), 0, s, tokens, rows, H, V, N, valid_n,
+                       reinterpret_cast<const bf16_t*>(pe), x, bad);
   else
-    hipLaunchKernelGGL(k_embed<float>, dim3(blocks), dim3(256), 0, s, tokens, rows, H, V,
-                       reinterpret_cast<const float*>(pe), x);
+    hipLaunchKernelGGL(k_embed<float>, dim3(blocks), dim3(256), 0, s, tokens, rows, H, V, N, valid_n,
+                       reinterpret_cast<const float*>(pe), x, bad);
   return hipGetLastError();
 }
 

@@ -69,6 +69,9 @@ struct dg_ctx {
   float* eb_ent = nullptr;
   int32_t *eb_samp = nullptr, *eb_prev = nullptr, *eb_status = nullptr;
   int32_t* eb_status_host = nullptr;  // pinned
+  // pinned: an out-of-range token id seen by the embedding, ((row + 1) << 32) | id;
+  // the next call on the context reports it
+  uint64_t* bad_id = nullptr;
   bool lm_fused = false;
   long long part_cap = 0;
   int32_t* trace = nullptr;
@@ -248,6 +251,19 @@ dg_status enter(dg_ctx* ctx) {
   HIPX(hipSetDevice(ctx->dev));
   // surface asynchronous faults of earlier work without blocking
   HIPX(hipGetLastError());
+  // an out-of-range token id recorded by an earlier call's embedding (seen
+  // once that work has run): reported once, then cleared
+  if (ctx->bad_id) {
+    const uint64_t b = __atomic_exchange_n(ctx->bad_id, (uint64_t)0, __ATOMIC_ACQ_REL);
+    if (b) {
+      const long long row = (long long)(b >> 32) - 1;
+      const int32_t id = (int32_t)(uint32_t)b;
+      return fail(ctx, DG_EINVAL,
+                  "an earlier call was given token id %d at row %lld (canvas %lld, position %lld), outside "
+                  "[0, %d); that row was embedded as zeros",
+                  id, row, row / ctx->c.canvas_len, row % ctx->c.canvas_len, ctx->c.vocab);
+    }
+  }
   return DG_OK;
 }
 
@@ -295,6 +311,10 @@ dg_status alloc_workspaces(dg_ctx* ctx) {
     void* hp = nullptr;
     HIPX(hipHostMalloc(&hp, (size_t)c.max_batch * 4, hipHostMallocDefault));
     ctx->eb_status_host = static_cast<int32_t*>(hp);
+    void* bp = nullptr;
+    HIPX(hipHostMalloc(&bp, sizeof(uint64_t), hipHostMallocDefault));
+    ctx->bad_id = static_cast<uint64_t*>(bp);
+    *ctx->bad_id = 0;
   }
   TRY(dalloc_t(ctx, &ctx->rope, (size_t)c.max_batch * c.canvas_len * (D / 2) * sizeof(float2)));
   // attention split partials: up to 64 splits of every query row
@@ -597,7 +617,8 @@ dg_status enqueue_head_eb(dg_ctx* ctx, const void* h, int M, const EbArg& eb, in
 dg_status enqueue_trunk(dg_ctx* ctx, int B, const int32_t* tokens) {
   const dg_config& c = ctx->c;
   const int M = B * c.canvas_len, H = c.hidden;
-  HIPX(launch_embed(ctx->bf16, tokens, M, H, c.vocab, ctx->embed, ctx->x, ctx->st));
+  HIPX(launch_embed(ctx->bf16, tokens, M, H, c.vocab, c.canvas_len, c.canvas_len, ctx->embed, ctx->x, ctx->bad_id,
+                    ctx->st));
   NormArgs n0{};
   n0.mode = 2; n0.rows = M; n0.H = H; n0.k = c.top_k; n0.eps = c.rms_eps;
   n0.x = ctx->x; n0.w_out = ctx->L[0].norm[0]; n0.out = ctx->a;
@@ -686,6 +707,7 @@ dg_status dg_destroy(dg_ctx* ctx) {
   for (void* p : ctx->owned)
     if (p) (void)hipFree(p);
   if (ctx->eb_status_host) (void)hipHostFree(ctx->eb_status_host);
+  if (ctx->bad_id) (void)hipHostFree(ctx->bad_id);
   delete ctx;
   return DG_OK;
 }
@@ -878,7 +900,7 @@ dg_status commit_tokens(dg_ctx* ctx, int32_t batch, const int32_t* tokens, int n
       return fail(ctx, DG_EINVAL, "slot %d: prompt_len %d + %d exceeds max_prompt_len %d", b,
                   ctx->slots[b].prompt_len, n, c.max_prompt_len);
   // the block at positions prompt_len + i, causal within the block
-  HIPX(launch_embed(ctx->bf16, tokens, M, H, c.vocab, ctx->embed, ctx->x, ctx->st));
+  HIPX(launch_embed(ctx->bf16, tokens, M, H, c.vocab, N, n, ctx->embed, ctx->x, ctx->bad_id, ctx->st));
   NormArgs n0{};
   n0.mode = 2; n0.rows = M; n0.H = H; n0.k = c.top_k; n0.eps = c.rms_eps;
   n0.x = ctx->x; n0.w_out = ctx->L[0].norm[0]; n0.out = ctx->a;

@@ -37,6 +37,13 @@
  *     returned.  A HIP error reported by the runtime (including an
  *     asynchronous fault of an earlier call) is returned as DG_EHIP.
  *   - dg_last_error() gives a message for the context's last error.
+ *   - Token ids must lie in [0, V) (V = 262144 in the pages' model, [4xFaster]
+ *     "DiffusionGemma's Technical Architecture").  Ids live in device memory,
+ *     so they are checked on the device: the embedding reads an id outside
+ *     that range as a zero row and records it, and the first call on the
+ *     context after that work has run returns DG_EINVAL (naming the id, its
+ *     canvas and position) with nothing enqueued; the record is then cleared.
+ *     Synchronise the stream before that call to see the report there.
  *   - A context is not thread-safe: one host thread at a time.
  *   - bf16 values are raw 16-bit patterns (upper half of an IEEE float32);
  *     "T" below is float for DG_F32 contexts and bf16 for DG_BF16 contexts.

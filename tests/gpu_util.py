@@ -107,3 +107,98 @@ def shadow_compare(w, tok0, lk0, passes, delta_rel, conf_tol, weights=None, rout
         assert np.array_equal(p["locked"], l_o), t
     return report, worst_conf
 
+
+
+# ----------------------------------------- per-pass comparison from a state ---
+
+def rms(a) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    return float(np.sqrt(np.mean(a * a))) if a.size else 0.0
+
+
+def oracle_head_step(x_final, W, m, tokens, locked, steps_left, gpu, logit_delta, conf_delta_rel):
+    """The end of a pass in the oracle from a given final residual stream
+    ``x_final [B*N, H]``: final norm, tied LM head, argmax and confidence,
+    lock step, with the GPU pass's argmax and lock set (``gpu``: its
+    ``pred``, ``locked`` after the pass) adopted at near-ties.  Returns the
+    oracle's new ``tokens, locked``, its ``pred, conf`` and the shadow."""
+    B, N = tokens.shape
+    rnd = om.bf16_round if m.dtype == "bf16" else (lambda z: z)
+    h = rnd(om.rmsnorm(x_final, W.norm_final(), m.rms_eps))
+    logits = om.lm_logits(h, W.embed())
+    pred, conf = om.argmax_conf(logits)
+    pred, conf = pred.reshape(B, N), conf.reshape(B, N)
+    sh = om.Shadow(pred=gpu["pred"], locked_after=gpu["locked"], delta_logit=logit_delta,
+                   delta_conf=conf_delta_rel * rms(gpu["conf"]))
+    om.adopt_pred(logits.reshape(B, N, -1), pred, conf, sh)
+    del logits
+    t_o, l_o, chosen = om.lock_select(conf, pred, tokens, locked, steps_left)
+    om.adopt_locks(conf, pred, tokens, locked, t_o, l_o, chosen, sh)
+    return t_o, l_o, pred, conf, sh
+
+
+def gpu_layer_states(torch, ctx, w, tokens):
+    """The GPU's residual stream before and after every layer of a pass over
+    ``tokens [B, N]``, and the routing of each layer: the embedded canvas
+    (bf16 rows widened exactly) through ``dg_forward_layers`` one layer at a
+    time, which equals the pass's own stack bit for bit."""
+    from synth import gen
+    m = w.model
+    L, M = m.n_layers, tokens.size
+    E = gen.embed(w)[tokens.reshape(-1)]
+    x0 = om.bf16_bits_to_f64(E) if m.dtype == "bf16" else np.asarray(E, dtype=np.float64)
+    xd = torch.from_numpy(x0.astype(np.float32)).cuda()
+    trace = torch.zeros((L, M, m.top_k), dtype=torch.int32, device="cuda")
+    ctx.set_trace(trace)
+    xs = [x0]
+    for l in range(L):
+        xn = torch.empty_like(xd)
+        ctx.forward_layers(l, 1, xd, xn)
+        torch.cuda.synchronize()
+        xs.append(host64(xn))
+        xd = xn
+    ctx.set_trace(None)
+    return xs, trace.cpu().numpy()
+
+
+def anchored_pass_compare(torch, ctx, w, W, kvf, t, tokens, locked, gpu, route_delta, logit_delta,
+                          conf_delta_rel, tag):
+    """Pass ``t`` of a block compared with the oracle layer by layer: every
+    layer of the oracle starts from the GPU's own residual stream at that
+    layer's input (so each layer is held to the one-layer tolerance and its
+    routing to the one-layer decision delta), then the oracle's head and lock
+    step run from the GPU's final residual stream with the GPU's argmax and
+    lock set adopted at near-ties.  The oracle's tokens and locked mask after
+    the pass must equal the GPU's (``gpu``: the pass's ``tokens``,
+    ``locked``, ``pred``, ``conf``).  Returns (worst layer error, conf error,
+    adopted counts)."""
+    m = w.model
+    L = m.n_layers
+    tol = TOL[m.dtype]
+    say(tag, "pass", t, "layer states")
+    xs, tr = gpu_layer_states(torch, ctx, w, tokens)
+    lens = [w.prompt_len] * w.batch
+    worst, adopted = 0.0, {"route": 0, "pred": 0, "lock": 0}
+    for l in range(L):
+        route = [None] * L
+        route[l] = tr[l]
+        sh = om.Shadow(route_idx=route, delta_route=route_delta)
+        ref = om.forward_hidden(xs[l], W, m, kvf, lens, layers=[l], shadow=sh)
+        e = rel_err(xs[l + 1], ref)
+        worst = max(worst, e)
+        assert not sh.failures, (tag, t, l, sh.failures[:5])
+        assert e <= tol, (tag, t, l, e)
+        adopted["route"] += sh.adopted["route"]
+    steps = [w.n_steps - t] * w.batch
+    t_o, l_o, pred_o, conf_o, sh = oracle_head_step(xs[L], W, m, tokens, locked, steps, gpu, logit_delta,
+                                                    conf_delta_rel)
+    assert not sh.failures, (tag, t, sh.failures[:5])
+    ce = rel_err(gpu["conf"], conf_o)
+    assert ce <= tol, (tag, t, ce)
+    assert np.array_equal(gpu["tokens"], t_o), (tag, t)
+    assert np.array_equal(gpu["locked"], l_o), (tag, t)
+    adopted["pred"] += sh.adopted["pred"]
+    adopted["lock"] += sh.adopted["lock"]
+    print(f"{tag} pass {t}: every layer from the GPU's own input within {worst:.3e}; conf rel err "
+          f"{ce:.3e}; adopted {adopted}", flush=True)
+    return worst, ce, adopted

@@ -156,9 +156,11 @@ def _pass_after(torch, ctx, w, W, cache, pos):
     t_o, l_o, pred_o, conf_o, _ = om.denoise_pass(tok0, lk0, [w.n_steps], W, m, lambda l, b: cache[l], [pos],
                                                    shadow=sh)
     assert not sh.failures, sh.failures[:5]
-    ce = float(np.max(np.abs(c_g - conf_o) / conf_o))
-    print(f"{w.name} pass after commits: conf rel err {ce:.3e}, adopted {sh.adopted}")
-    assert ce <= 5 * TOL[m.dtype]
+    ce = rel_err(c_g, conf_o)
+    ce_el = float(np.max(np.abs(c_g - conf_o) / conf_o))
+    print(f"{w.name} pass after commits: conf rel err {ce:.3e} (largest per position {ce_el:.3e}), "
+          f"adopted {sh.adopted}")
+    assert ce <= TOL[m.dtype]
     assert np.array_equal(tokens.cpu().numpy(), t_o)
     assert np.array_equal(locked.cpu().numpy(), l_o)
 

@@ -76,6 +76,53 @@ def test_c1_block_matches_oracle(torch, dg):
     assert report == {"route": 0, "pred": 0, "lock": 0}
 
 
+def test_out_of_range_token_ids_are_reported(torch, dg):
+    # ids outside [0, V) ([4xFaster] "DiffusionGemma's Technical Architecture":
+    # the vocabulary is fixed): the embedding records them on the device and
+    # the next call on the context returns DG_EINVAL naming one of them
+    w = C1
+    m = w.model
+    N, V = m.canvas_len, m.vocab
+    say("C1 out-of-range token ids")
+    with dg.Context(m, max_batch=w.batch, max_prompt_len=w.prompt_len + N) as ctx:
+        upload.load_context(ctx, w)
+        tok0, lk0 = gen.canvas(w)
+        conf = torch.empty((1, N), dtype=torch.float32, device="cuda")
+        pred = torch.empty((1, N), dtype=torch.int32, device="cuda")
+
+        def step(tok):
+            t = torch.from_numpy(tok.copy()).cuda()
+            l = torch.from_numpy(lk0.copy()).cuda()
+            ctx.denoise_step(t, l, [w.n_steps], conf, pred)
+            torch.cuda.synchronize()
+
+        step(tok0)  # valid ids: no report
+        step(tok0)
+        for bad, pos in ((V, 3), (-1, 17), (2 ** 31 - 1, 0)):
+            tok = tok0.copy()
+            tok[0, pos] = bad
+            step(tok)  # enqueued and run: the row reads as zeros
+            with pytest.raises(dg.DGError) as ei:
+                step(tok0)
+            assert ei.value.status == dg.DG_EINVAL
+            msg = str(ei.value)
+            print(f"reported: {msg}")
+            assert f"token id {bad} at row {pos}" in msg and f"outside [0, {V})" in msg
+            step(tok0)  # reported once, then cleared
+        # a commit checks the ids it commits; entries past n are ignored
+        tok = tok0.copy()
+        tok[0, 5:] = V + 7
+        ctx.commit_tokens(torch.from_numpy(tok).cuda(), 5)
+        torch.cuda.synchronize()
+        step(tok0)
+        tok[0, 2] = -3
+        ctx.commit_tokens(torch.from_numpy(tok).cuda(), 5)
+        torch.cuda.synchronize()
+        with pytest.raises(dg.DGError) as ei:
+            step(tok0)
+        assert ei.value.status == dg.DG_EINVAL and "token id -3 at row 2" in str(ei.value)
+
+
 def test_c1_lock_schedule_and_invariants(torch, dg):
     w = C1
     say("C1 schedule")
