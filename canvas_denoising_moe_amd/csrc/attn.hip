@@ -31,6 +31,276 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Flash attention for bf16 with K/V tiles copied straight from global memory
+// into LDS (no register staging), two query sub-tiles per wave.
+//
+//   * Work unit = (canvas b, KV head g, key split s) x q-tile of 128 query
+//     rows; each of the 4 waves holds 32 rows as two 16-row sub-tiles, so
+//     every K or V fragment read from LDS feeds two MFMAs.
+//   * A 64-key tile of K and of V^T is laid out in LDS in MFMA fragment
+//     order (1 KB blocks, lane l's 16 bytes at offset 16 l), written by
+//     direct global->LDS copies in which every lane fetches exactly the 16
+//     bytes it will later read; reads are conflict-free 16-byte loads.  Two
+//     LDS stages: the copy of tile t + 1 runs while tile t is consumed.
+//   * Scores are computed transposed (S^T = K Q^T).  The keys of a K fragment
+//     are permuted (row m of key block kb holds key 32 (kb/2) + 8 (m/4) +
+//     4 (kb%2) + m%4) so that every lane ends up holding 8 consecutive keys
+//     of one query per 32-key step: the B operand of O^T = V^T P^T, whose A
+//     operand (V^T) is then 16 contiguous bytes per lane, copyable as such.
+//   * Online softmax in base 2 with a lazily updated reference maximum: the
+//     running state is rescaled only when a tile's maximum exceeds the
+//     reference by more than 2^8 (P then stays <= 256, exact scaling is
+//     unaffected), which skips almost every rescale.  P is rounded to bf16
+//     for the MFMA and the normaliser is the MFMA sum of the same rounded P
+//     (an all-ones A operand), so a single key gives weight exactly 1.
+// Needs every 8-key group of V^T in one source (key counts multiples of 8).
+template <int D>
+__global__ __launch_bounds__(256, 2) void k_attn_fa(AttnArgs a, int QT, int xcd_map) {
+  constexpr int KT = 64;                 // keys per tile
+  constexpr int KS = D / 32, DB = D / 16;
+  constexpr int NKB = 4 * KS, NVB = 2 * DB;  // 1 KB fragment blocks of a K tile and of a V^T tile
+  static_assert(NKB % 4 == 0 && NVB % 4 == 0, "the four waves copy equal shares of a tile");
+  __shared__ __align__(16) bf16_t K0[NKB * 512];
+  __shared__ __align__(16) bf16_t K1[NKB * 512];
+  __shared__ __align__(16) bf16_t V0[NVB * 512];
+  __shared__ __align__(16) bf16_t V1[NVB * 512];
+
+  int bid = blockIdx.x, unit, qt;
+  if (xcd_map) {
+    const int xcd = bid & 7, slot = bid >> 3;
+    unit = (slot / QT) * 8 + xcd;
+    qt = slot % QT;
+  } else {
+    unit = bid / QT;
+    qt = bid % QT;
+  }
+  int b = 0;
+  while (b + 1 < a.B && a.ubase[b + 1] <= unit) ++b;
+  const int S = a.ns[b], CL = a.cl[b];
+  const int s = (unit - a.ubase[b]) % S, g = (unit - a.ubase[b]) / S;
+  const int group = a.Hq / a.Hkv;
+  const int N = a.N;
+  const int Lw = a.lw[b];
+  const int total = Lw + (a.canvas_keys ? N : 0);
+  const int k0 = s * CL, k1 = min(total, k0 + CL);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lg = lane >> 4, lc = lane & 15;
+  const int grows = group * N;
+  bool qvalid[2];
+  int qh[2], qi[2];
+  long long row_g[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int qrow = qt * 128 + wave * 32 + j * 16 + lc;
+    qvalid[j] = qrow < grows;
+    qh[j] = g * group + (qvalid[j] ? qrow / N : 0);
+    qi[j] = qvalid[j] ? qrow % N : 0;
+    row_g[j] = ((long long)b * a.Hq + qh[j]) * N + qi[j];
+  }
+
+  const bf16_t* kp = reinterpret_cast<const bf16_t*>(a.kp[b]) + (long long)g * Lw * D;
+  const bf16_t* vp = reinterpret_cast<const bf16_t*>(a.vp[b]) + (long long)g * D * Lw;
+  const bf16_t* kc = reinterpret_cast<const bf16_t*>(a.kc) + ((long long)b * a.Hkv + g) * N * D;
+  const bf16_t* vc = reinterpret_cast<const bf16_t*>(a.vc) + ((long long)b * a.Hkv + g) * D * N;
+
+  // Q^T fragments of both sub-tiles (B operand of S^T = K Q^T)
+  uint4 qf[2][KS];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const bf16_t* qp = reinterpret_cast<const bf16_t*>(a.q) + row_g[j] * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[j][ks] = qvalid[j] ? *reinterpret_cast<const uint4*>(qp + ks * 32 + lg * 8) : make_uint4(0, 0, 0, 0);
+  }
+
+  floatx4 oacc[2][DB], lacc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    lacc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < DB; ++i) oacc[j][i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+  float m_ref[2] = {-INFINITY, -INFINITY};  // reference maximum of P (scaled log2 units)
+  const float sc = kLog2e / sqrtf((float)D);
+  const uint4 ones = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);  // bf16 1.0 pairs
+
+  // Direct copies of one tile into a stage: wave w copies K blocks w, w + 4,
+  // ... and V^T blocks w, w + 4, ...  Keys past the split's end are clamped
+  // into it (their scores are masked to -inf, so their P is exactly 0).  The
+  // wave index is made wave-uniform so every LDS destination is a scalar.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int lane_key = 8 * (lc >> 2) + (lc & 3);  // this lane's key within a K block pair
+  auto issue = [&](bf16_t* Kd, bf16_t* Vd, int t0) {
+#pragma unroll
+    for (int i = 0; i < NKB / 4; ++i) {
+      const int q = wv + 4 * i, kb = q / KS, ks = q - kb * KS;
+      const int key = min(t0 + 32 * (kb >> 1) + 4 * (kb & 1) + lane_key, k1 - 1);
+      const bf16_t* src = key < Lw ? kp + key * D : kc + (key - Lw) * D;
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) const void*)(src + ks * 32 + lg * 8),
+                                       (__attribute__((address_space(3))) void*)(Kd + q * 512), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NVB / 4; ++i) {
+      const int q = wv + 4 * i, db = q >> 1, ks2 = q & 1;
+      const int c = min(t0 + ks2 * 32 + lg * 8, k1 - 8);
+      const int d = db * 16 + lc;
+      const bf16_t* src = c < Lw ? vp + d * Lw + c : vc + d * N + (c - Lw);
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) const void*)src,
+                                       (__attribute__((address_space(3))) void*)(Vd + q * 512), 16, 0, 0);
+    }
+  };
+
+  // One 64-key tile from a stage.  `edge`: the tile reaches past the split's
+  // end or holds canvas keys under the causal mask.
+  auto consume = [&](const bf16_t* Ks, const bf16_t* Vs, int t0, bool edge) {
+    floatx4 sacc[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      sacc[0][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      sacc[1][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 kf = *reinterpret_cast<const uint4*>(Ks + (kb * KS + ks) * 512 + lane * 8);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          sacc[j][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, kf),
+                                                                 __builtin_bit_cast(bf16x8_v, qf[j][ks]),
+                                                                 sacc[j][kb], 0, 0, 0);
+      }
+      // at most one key block's fragments live at a time (register budget of two waves per SIMD)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    uint32_t pk[2][2][4];
+    float mt[2];
+    bool need = false;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (edge) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = t0 + 32 * (kb >> 1) + 8 * lg + 4 * (kb & 1) + r;
+            const bool vis = key < k1 && !(a.causal && key - Lw > qi[j]);
+            if (!vis) sacc[j][kb][r] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[j][kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mt[j] = mx * sc;
+      need = need || mt[j] > m_ref[j] + 8.0f;
+    }
+    if (__any(need)) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bool up = mt[j] > m_ref[j] + 8.0f;
+        const float alpha = up ? exp2f(m_ref[j] - mt[j]) : 1.0f;  // m_ref = -inf: alpha 0, state is 0
+        m_ref[j] = up ? mt[j] : m_ref[j];
+        lacc[j] *= alpha;
+#pragma unroll
+        for (int i = 0; i < DB; ++i) oacc[j][i] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float mref = m_ref[j] == -INFINITY ? 0.f : m_ref[j];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+          pk[j][kb >> 1][(kb & 1) * 2 + q] = f2bf2(exp2f(fmaf(sacc[j][kb][2 * q], sc, -mref)),
+                                                   exp2f(fmaf(sacc[j][kb][2 * q + 1], sc, -mref)));
+    }
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const uint4 vf = *reinterpret_cast<const uint4*>(Vs + (db * 2 + ks2) * 512 + lane * 8);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint4 pf = make_uint4(pk[j][ks2][0], pk[j][ks2][1], pk[j][ks2][2], pk[j][ks2][3]);
+          oacc[j][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, vf),
+                                                                 __builtin_bit_cast(bf16x8_v, pf), oacc[j][db], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint4 pf = make_uint4(pk[j][ks2][0], pk[j][ks2][1], pk[j][ks2][2], pk[j][ks2][3]);
+        lacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, ones),
+                                                           __builtin_bit_cast(bf16x8_v, pf), lacc[j], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  const int ntiles = k1 > k0 ? (k1 - k0 + KT - 1) / KT : 0;
+  // tiles that need the mask: past the split's end, or canvas keys (from key
+  // Lw on) under the causal mask
+  auto edge = [&](int t0) { return t0 + KT > k1 || (a.causal && t0 + KT > Lw); };
+  // The copies into a stage are waited for explicitly before the barrier that
+  // publishes it: the compiler's own wait before the barrier is missing on the
+  // loop's back edge (the copy issued in the second half of an iteration is
+  // read in the first half of the next), so without this a wave could pass
+  // the barrier while its part of the tile is still in flight.
+  auto copies_done = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  if (ntiles > 0) issue(K0, V0, k0);
+  for (int it = 0; it < ntiles; it += 2) {
+    copies_done();
+    __syncthreads();  // tile it is in stage 0 (every wave's copies done); stage 1 is free
+    if (it + 1 < ntiles) issue(K1, V1, k0 + (it + 1) * KT);
+    {
+      const int t0 = k0 + it * KT;
+      consume(K0, V0, t0, edge(t0));
+    }
+    if (it + 1 >= ntiles) break;
+    copies_done();
+    __syncthreads();  // tile it + 1 is in stage 1; stage 0 is free
+    if (it + 2 < ntiles) issue(K0, V0, k0 + (it + 2) * KT);
+    {
+      const int t0 = k0 + (it + 1) * KT;
+      consume(K1, V1, t0, edge(t0));
+    }
+  }
+
+  mfma_drain();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (!qvalid[j]) continue;
+    const float l = lacc[j][0];
+    if (S == 1) {
+      // a single split: normalise and store the bf16 output directly (the
+      // same quotient the merge forms from one split)
+      bf16_t* o = reinterpret_cast<bf16_t*>(a.o) + ((long long)b * N + qi[j]) * a.Hq * D + (long long)qh[j] * D;
+      auto nrm = [&](float x) { return f2bf(l > 0.f ? x / l : 0.f); };
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int d = db * 16 + lg * 4;
+        *reinterpret_cast<uint2*>(o + d) =
+            make_uint2((uint32_t)nrm(oacc[j][db][0]) | ((uint32_t)nrm(oacc[j][db][1]) << 16),
+                       (uint32_t)nrm(oacc[j][db][2]) | ((uint32_t)nrm(oacc[j][db][3]) << 16));
+      }
+    } else {
+      const long long rows_all = (long long)a.B * a.Hq * N;
+      const long long pr = (long long)s * rows_all + row_g[j];
+      float* po = a.part_o + pr * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<float4*>(po + db * 16 + lg * 4) =
+            make_float4(oacc[j][db][0], oacc[j][db][1], oacc[j][db][2], oacc[j][db][3]);
+      if (lg == 0) {
+        a.part_m[pr] = m_ref[j];
+        a.part_l[pr] = l;
+      }
+    }
+  }
+}
+
 template <int D, bool ALIGNED>
 __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int QT, int xcd_map) {
   constexpr int KT = 64;            // keys per tile
@@ -415,10 +685,54 @@ static void choose_splits(int total, int Hkv, int QT, int* S_out, int* CL_out) {
   *CL_out = CL;
 }
 
+// Key splits of canvas b for the direct-copy kernel (two workgroups per CU):
+// enough (KV head x split x q-tile) workgroups to fill the chip's slots once,
+// splits of at most 8192 keys, and for long prompts a split count that fills
+// whole rounds of slots; whole 64-key tiles, at most 64 splits.
+static void choose_splits_fa(int total, int base, int* S_out, int* CL_out) {
+  const int slots = 2 * 256;
+  const int smin = (slots + base - 1) / base;
+  int S = max(smin, (total + 8191) / 8192);
+  if (S > smin && slots % base == 0) {
+    const int r = slots / base;
+    S = (S + r - 1) / r * r;
+  }
+  S = min(S, max(1, (total + 63) / 64));
+  S = min(S, 64);
+  int CL = ((total + S - 1) / S + 63) / 64 * 64;
+  if (CL < 64) CL = 64;
+  S = max(1, (total + CL - 1) / CL);
+  *S_out = S;
+  *CL_out = CL;
+}
+
 hipError_t launch_attention(int is_bf16, const AttnArgs& a0, hipStream_t st, KTime t) {
   const long long rows_all = (long long)a0.B * a0.Hq * a0.N;
   if (rows_all == 0) return hipSuccess;
   if (a0.B > DG_MAX_BATCH) return hipErrorInvalidValue;
+  // every 8-key group of V^T in one source, and key counts multiples of 8
+  bool aligned0 = (a0.N & 7) == 0;
+  for (int b = 0; b < a0.B; ++b) aligned0 = aligned0 && (a0.lw[b] & 7) == 0;
+  if (is_bf16 && (a0.D == 128 || a0.D == 64) && aligned0) {
+    AttnArgs a = a0;
+    const int QT = (a.Hq / a.Hkv * a.N + 127) / 128;
+    int smax = 1;
+    a.ubase[0] = 0;
+    for (int b = 0; b < a.B; ++b) {
+      choose_splits_fa(a.lw[b] + (a.canvas_keys ? a.N : 0), a.Hkv * QT, &a.ns[b], &a.cl[b]);
+      smax = max(smax, a.ns[b]);
+      a.ubase[b + 1] = a.ubase[b] + a.Hkv * a.ns[b];
+    }
+    if ((long long)smax * rows_all > a.part_cap_rows) return hipErrorInvalidValue;
+    const long long units = a.ubase[a.B];
+    const int xcd_map = (units % 8) == 0;
+    const dim3 grid((unsigned)(units * QT));
+    hipEvent_t stop1 = smax == 1 ? t.stop : nullptr;
+    hipError_t e = a.D == 128 ? launch_k(k_attn_fa<128>, grid, dim3(256), 0, st, t.start, stop1, a, QT, xcd_map)
+                              : launch_k(k_attn_fa<64>, grid, dim3(256), 0, st, t.start, stop1, a, QT, xcd_map);
+    if (e != hipSuccess || smax == 1) return e;
+    return launch_k(k_attn_merge<bf16_t>, dim3((unsigned)((rows_all + 3) / 4)), dim3(256), 0, st, nullptr, t.stop, a);
+  }
   if (is_bf16 && (a0.D == 128 || a0.D == 64)) {
     AttnArgs a = a0;
     const int QT = (a.Hq / a.Hkv * a.N + 63) / 64;

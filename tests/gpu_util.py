@@ -177,6 +177,12 @@ def anchored_pass_compare(torch, ctx, w, W, kvf, t, tokens, locked, gpu, route_d
     tol = TOL[m.dtype]
     say(tag, "pass", t, "layer states")
     xs, tr = gpu_layer_states(torch, ctx, w, tokens)
+    # the replay is the pass's own stack: same kernels, same inputs, so the
+    # same routing at every layer (every kernel is deterministic)
+    if "trace" in gpu:
+        diff = [l for l in range(L) if not np.array_equal(tr[l], gpu["trace"][l])]
+        assert not diff, (tag, t, f"the layer-by-layer replay routes differently from the pass from layer {diff[0]} "
+                                  f"on ({int((tr[diff[0]] != gpu['trace'][diff[0]]).any(axis=1).sum())} rows)")
     lens = [w.prompt_len] * w.batch
     worst, adopted = 0.0, {"route": 0, "pred": 0, "lock": 0}
     for l in range(L):
