@@ -85,6 +85,7 @@ _SIGS = {
     "dg_k_moe_ffn": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
     "dg_k_lm_head": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p]),
     "dg_k_lm_argmax": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p]),
+    "dg_k_lm_argmax_noalloc": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p]),
     "dg_k_lm_sample": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, POINTER(ctypes.c_uint32),
                                  ctypes.c_uint32, c_void_p, c_void_p, c_void_p]),
     "dg_profile": (c_int32, [c_void_p, c_int32]),
@@ -508,6 +509,17 @@ class Context:
         _need(conf, M, "conf")
         self._c(lib().dg_k_lm_argmax(self._h, batch, _ptr(h, self.wdtype, "h"),
                                      _ptr(pred, torch.int32, "pred"), _ptr(conf, torch.float32, "conf")))
+
+    def k_lm_argmax_noalloc(self, batch: int, h, pred, conf):
+        """dg_k_lm_argmax with its partials in the library's static scratch
+        (allocates nothing; see include/dg.h for the size limit)."""
+        import torch
+        M = self._batch(batch) * self.model.canvas_len
+        _need(h, M * self.model.hidden, "h")
+        _need(pred, M, "pred")
+        _need(conf, M, "conf")
+        self._c(lib().dg_k_lm_argmax_noalloc(self._h, batch, _ptr(h, self.wdtype, "h"),
+                                             _ptr(pred, torch.int32, "pred"), _ptr(conf, torch.float32, "conf")))
 
     def k_lm_sample(self, batch: int, h, t: int, t_max: int, seeds: Sequence[int], block: int, pred, entropy, sample):
         import torch

@@ -6,15 +6,44 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
 #include "common.h"
 #include "dg.h"
 
+// Scratch of dg_k_lm_argmax_noalloc: the fused LM head's (max, sum, argmax)
+// partials, one per (vocabulary tile of 256, row), in an array every device
+// holds from the library's load to the end of the process.  Host code must
+// not use the array's name as a device address: dg_create looks up each
+// device's own copy once (hipGetSymbolAddress with that device current) and
+// the entry point passes that address.
+constexpr long long kNoAllocParts = 1ll << 20;  // (vocabulary tile, row) pairs: 12 MiB
+static __device__ __align__(256) float scratch[3 * kNoAllocParts];
+
 namespace {
 
 std::string g_create_error;
+
+// per device: the address of its copy of `scratch` (null until looked up)
+std::mutex g_scratch_mu;
+void* g_scratch_dev[64] = {nullptr};
+
+// Looks up the current device's copy of `scratch` once; returns it (null on failure).
+void* scratch_addr(int dev) {
+  if (dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_dev[dev] = p;
+  }
+  return g_scratch_dev[dev];
+}
 
 struct LayerW {
   void* qkv = nullptr;   // packed [(Hq+2Hkv)D/16][H/32][64][8]
@@ -681,6 +710,7 @@ dg_status dg_create(const dg_config* cfg, int32_t device, void* hip_stream, dg_c
   if (device < 0 || device >= ndev) return fail(nullptr, DG_EINVAL, "device %d out of range", device);
   he = hipSetDevice(device);
   if (he != hipSuccess) return fail(nullptr, DG_EHIP, "hipSetDevice: %s", hipGetErrorString(he));
+  if (!scratch_addr(device)) return fail(nullptr, DG_EHIP, "device %d: address of the static scratch not found", device);
   dg_ctx* ctx = new dg_ctx();
   ctx->c = *cfg;
   ctx->dev = device;
@@ -1266,6 +1296,33 @@ dg_status dg_k_lm_argmax(dg_ctx* ctx, int32_t batch, const void* h, int32_t* pre
   if (batch < 1 || batch > c.max_batch) return fail(ctx, DG_EINVAL, "batch out of range");
   if (!h || !pred || !conf) return fail(ctx, DG_EINVAL, "h, pred and conf are required");
   return enqueue_head(ctx, h, batch * c.canvas_len, pred, conf);
+}
+
+dg_status dg_k_lm_argmax_noalloc(dg_ctx* ctx, int32_t batch, const void* h, int32_t* pred, float* conf) {
+  TRY(enter(ctx));
+  const dg_config& c = ctx->c;
+  if (batch < 1 || batch > c.max_batch) return fail(ctx, DG_EINVAL, "batch out of range");
+  if (!c.has_lm_head || !ctx->lm_fused)
+    return fail(ctx, DG_EUNSUPPORTED, "the allocation-free LM head needs a bf16 context with the fused LM head");
+  const int M = batch * c.canvas_len;
+  const long long parts = (long long)((c.vocab / 16 + 15) / 16) * M;
+  if (parts > kNoAllocParts)
+    return fail(ctx, DG_EINVAL,
+                "batch %d: %lld (vocabulary tile, row) partials exceed the static scratch of %lld; at most %lld rows "
+                "at this vocabulary",
+                batch, parts, kNoAllocParts, kNoAllocParts / ((c.vocab / 16 + 15) / 16));
+  if (!ctx->embed_set) return fail(ctx, DG_ESTATE, "embedding not loaded");
+  if (!h || !pred || !conf) return fail(ctx, DG_EINVAL, "h, pred and conf are required");
+  float* sp = static_cast<float*>(scratch_addr(ctx->dev));
+  if (!sp) return fail(ctx, DG_EHIP, "address of the static scratch not found");
+  LmArgs la = lm_args(ctx, h, M);
+  la.part_m = sp;
+  la.part_s = sp + kNoAllocParts;
+  la.part_i = reinterpret_cast<int32_t*>(sp + 2 * kNoAllocParts);
+  la.pred = pred;
+  la.conf = conf;
+  HIPX(launch_lm_head(la, LM_ARGMAX, ctx->st));
+  return DG_OK;
 }
 
 dg_status dg_k_lm_sample(dg_ctx* ctx, int32_t batch, const void* h, int32_t t, int32_t t_max,

@@ -373,6 +373,20 @@ dg_status dg_k_lm_head(dg_ctx* ctx, int32_t batch, const void* h, float* logits)
  * are final). */
 dg_status dg_k_lm_argmax(dg_ctx* ctx, int32_t batch, const void* h, int32_t* pred, float* conf);
 
+/* dg_k_lm_argmax without any allocation, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid it): the same kernels, with their per-(vocabulary tile, row)
+ * partials in a static array of the library that each device holds until the
+ * process ends (12 MiB: at most 2^20 (tile of 256 ids, row) pairs, i.e.
+ * batch * N <= 2^20 / ceil(V / 256), 1024 rows at V = 262144; larger batches
+ * return DG_EINVAL with nothing enqueued).  bf16 contexts only
+ * (DG_EUNSUPPORTED otherwise).  Every call on a device shares that array:
+ * calls that overlap in time on one device (other streams or contexts) race
+ * and give undefined results; calls on one stream are ordered and safe.
+ * Nothing needs clearing between calls (every partial is written before it is
+ * read). */
+dg_status dg_k_lm_argmax_noalloc(dg_ctx* ctx, int32_t batch, const void* h, int32_t* pred, float* conf);
+
 /* EB statistics of the tied LM head as an EB pass runs it (bf16 contexts:
  * fused, the logits never reach memory): h T [batch*N, H] -> pred int32,
  * entropy float, sample int32 [batch*N] for pass t of at most t_max with the
