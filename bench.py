@@ -142,6 +142,117 @@ def algorithmic(w, touched):
     return byts, flops, sum(gu_bytes) / len(gu_bytes), gu_flops
 
 
+def trace_touched(ctx, w, tokens, locked, tok0_d, lk0_d):
+    """One whole block with the routing recorded: the number of routed experts
+    that received a token, per pass of the block and per layer."""
+    import numpy as np
+    import torch
+    m = w.model
+    B, T = w.batch, w.n_steps
+    M = B * m.canvas_len
+    trace = torch.empty((m.n_layers, M, m.top_k), dtype=torch.int32, device=tokens.device)
+    tokens.copy_(tok0_d)
+    locked.copy_(lk0_d)
+    ctx.set_trace(trace)
+    out = []
+    for t in range(T):
+        ctx.denoise_step(tokens, locked, [T - t] * B)
+        tr = trace.cpu().numpy()
+        out.append([int(np.unique(tr[l]).size) for l in range(m.n_layers)])
+    ctx.set_trace(None)
+    return out
+
+
+def pass_algorithmic(w, touched_by_pass, passes):
+    """Mean algorithmic bytes and flops of the given passes of the block."""
+    byts = flops = 0.0
+    for s in passes:
+        b, f, _, _ = algorithmic(w, touched_by_pass[s])
+        byts += b
+        flops += f
+    return byts / len(passes), flops / len(passes)
+
+
+def gate_up_bytes(w, touched_by_pass, passes):
+    """Mean algorithmic bytes of one gate|up launch over every layer of the
+    given passes."""
+    return sum(algorithmic(w, touched_by_pass[s])[2] for s in passes) / len(passes)
+
+
+def measure_workload(w, steps, warmup):
+    """Pass time, resolved tokens of one block and the pass roofline of a
+    second workload (its own context), plus its attention launches."""
+    import numpy as np
+    import torch
+
+    import canvas_denoising_moe_amd as dg
+    from canvas_denoising_moe_amd import binding as bd
+    from synth import gen, upload
+
+    m = w.model
+    B, N, T = w.batch, m.canvas_len, w.n_steps
+    M = B * N
+    dev = torch.device("cuda", 0)
+    t0 = time.perf_counter()
+    ctx = dg.Context(m, max_batch=B, max_prompt_len=w.prompt_len, device=0)
+    try:
+        upload.load_context(ctx, w)
+        torch.cuda.synchronize()
+        load_s = time.perf_counter() - t0
+        print(f"[bench] {w.name}: weights and prompt KV loaded in {load_s:.1f} s", file=sys.stderr, flush=True)
+        tok0, lk0 = gen.canvas(w)
+        tok0_d = torch.from_numpy(tok0).to(dev)
+        lk0_d = torch.from_numpy(lk0).to(dev)
+        tokens, locked = tok0_d.clone(), lk0_d.clone()
+        touched_by_pass = trace_touched(ctx, w, tokens, locked, tok0_d, lk0_d)
+
+        def step(i):
+            s = i % T
+            if s == 0:
+                tokens.copy_(tok0_d)
+                locked.copy_(lk0_d)
+            ctx.denoise_step(tokens, locked, [T - s] * B)
+
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        # attention launches (events add dispatch latency: outside the timed region)
+        ctx.profile([bd.PROF_ATTN])
+        for i in range(T):
+            step(steps + i)
+        torch.cuda.synchronize()
+        ctx.profile(())
+        n_at, ms_at = ctx.profile_read(bd.PROF_ATTN)
+        tokens.copy_(tok0_d)
+        locked.copy_(lk0_d)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ctx.generate_block(tokens, locked, T)
+        torch.cuda.synchronize()
+        block_ms = (time.perf_counter() - t0) * 1e3
+        assert bool(locked.all()), "block left unlocked positions"
+    finally:
+        ctx.close()
+        torch.cuda.empty_cache()
+    byts, flops = pass_algorithmic(w, touched_by_pass, [i % T for i in range(steps)])
+    newly = int(M - lk0.sum())
+    n_global = sum(1 for l in range(m.n_layers) if m.is_global(l))
+    return {"workload": w.name, "batch": B, "prompt_len": w.prompt_len, "passes_per_block": T,
+            "ms_per_step": round(ms, 4), "canvas_tok_s": round(M / (ms / 1e3), 1),
+            "block_ms": round(block_ms, 3), "resolved_tok_s": round(newly / (block_ms / 1e3), 1),
+            "pass_roofline": {"bytes": int(byts), "flops": int(flops),
+                              "hbm_frac": round(byts / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                              "mfma_frac": round(flops / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
+            "attention_us_per_layer": round(ms_at / max(n_at, 1) * 1e3, 2),
+            "attention_launches": n_at, "global_layers": n_global,
+            "experts_touched_min": min(min(tp) for tp in touched_by_pass), "load_s": round(load_s, 1)}
+
+
 def cpu_baseline(w):
     """The oracle (float64 numpy) timed on one whole denoise pass of the
     workload: every layer over every canvas position, the LM head, argmax and
@@ -213,13 +324,7 @@ def measure_mxfp4(w0, steps, warmup):
         tok0_d = torch.from_numpy(tok0).to(dev)
         lk0_d = torch.from_numpy(lk0).to(dev)
         tokens, locked = tok0_d.clone(), lk0_d.clone()
-        trace = torch.empty((m.n_layers, M, m.top_k), dtype=torch.int32, device=dev)
-        ctx.set_trace(trace)
-        ctx.denoise_step(tokens, locked, [T] * B)
-        torch.cuda.synchronize()
-        ctx.set_trace(None)
-        tr = trace.cpu().numpy()
-        touched = [int(np.unique(tr[l]).size) for l in range(m.n_layers)]
+        touched_by_pass = trace_touched(ctx, w, tokens, locked, tok0_d, lk0_d)
 
         def step(i):
             s = i % T
@@ -237,6 +342,7 @@ def measure_mxfp4(w0, steps, warmup):
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) * 1e3 / steps
         ctx.profile([bd.PROF_GATE_UP, bd.PROF_DOWN])
+        prof_passes = [(steps + i) % T for i in range(4)]
         for i in range(4):
             step(steps + i)
         torch.cuda.synchronize()
@@ -245,14 +351,14 @@ def measure_mxfp4(w0, steps, warmup):
         n_dn, ms_dn = ctx.profile_read(bd.PROF_DOWN)
     finally:
         ctx.close()
-    _, _, gu_bytes, _ = algorithmic(w, touched)
+    gu_bytes = gate_up_bytes(w, touched_by_pass, prof_passes)
     gu_s = ms_gu / max(n_gu, 1) / 1e3
     ach = gu_bytes / gu_s / 1e9
     return {"workload": w.name, "ms_per_step": round(ms, 4), "canvas_tok_s": round(M / (ms / 1e3), 1),
             "gate_up_us": round(gu_s * 1e6, 2), "down_us": round(ms_dn / max(n_dn, 1) * 1e3, 2),
             "gate_up_roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                  "frac": round(ach / HBM_PEAK_GBS, 4), "bytes_per_launch": int(gu_bytes)},
-            "experts_touched_min": min(touched), "load_s": round(load_s, 1)}
+            "experts_touched_min": min(min(tp) for tp in touched_by_pass), "load_s": round(load_s, 1)}
 
 
 def main():
@@ -269,6 +375,8 @@ def main():
     ap.add_argument("--no-mxfp4", action="store_true",
                     help="skip the variant with MXFP4 expert weights (a second context)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--others", default="C4,C5",
+                    help="further 30-layer workloads measured in their own contexts ('' for none)")
     ap.add_argument("--probe-copy-mib", type=int, default=0,
                     help="only run 4 device copies of this many MiB (calibrates HBM byte counters) and exit")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
@@ -325,14 +433,9 @@ def main():
     tokens = tok0_d.clone()
     locked = lk0_d.clone()
 
-    # routing of one pass: experts that received tokens per layer
-    trace = torch.empty((m.n_layers, M, m.top_k), dtype=torch.int32, device=dev)
-    ctx.set_trace(trace)
-    ctx.denoise_step(tokens, locked, [T] * B)
-    torch.cuda.synchronize()
-    ctx.set_trace(None)
-    tr = trace.cpu().numpy()
-    touched = [int(np.unique(tr[l]).size) for l in range(m.n_layers)]
+    # routing of every pass of one block: experts that received tokens, per
+    # pass of the block and layer (the weights of the others are not read)
+    touched_by_pass = trace_touched(ctx, w, tokens, locked, tok0_d, lk0_d)
 
     def step(i):
         s = i % T
@@ -447,7 +550,12 @@ def main():
         torch.cuda.synchronize()
         commit_ms = (time.perf_counter() - t0) * 1e3
 
-    byts, flops, gu_bytes, gu_flops = algorithmic(w, touched)
+    # the timed region's passes walk the block (pass i % T); the gate|up
+    # launches carry events on every 4th pass
+    timed = [i % T for i in range(args.steps)]
+    byts, flops = pass_algorithmic(w, touched_by_pass, timed)
+    gu_bytes = gate_up_bytes(w, touched_by_pass, [s for i, s in enumerate(timed) if i % 4 == 0])
+    touched = [min(tp[l] for tp in touched_by_pass) for l in range(m.n_layers)]
     gu_avg_s = ms_gu / n_gu / 1e3
     achieved = gu_bytes / gu_avg_s / 1e9
     pass_n, pass_ms = prof[bd.PROF_PASS]
@@ -482,6 +590,7 @@ def main():
                    "top_k": m.top_k, "vocab": m.vocab, "hidden": m.hidden},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "scope": "dominant kernel (the whole pass: pass_roofline)",
                      "kernel": "moe_grouped_gemm gate|up", "bytes_per_launch": int(gu_bytes),
                      "avg_launch_us": round(gu_avg_s * 1e6, 2)},
         "cpu_baseline": cpu,
@@ -502,6 +611,9 @@ def main():
     if not args.no_mxfp4 and m.dtype == "bf16":
         torch.cuda.empty_cache()
         line["mxfp4_experts"] = measure_mxfp4(w, args.steps, args.warmup)
+    for name in [x for x in args.others.split(",") if x and x != args.workload]:
+        torch.cuda.empty_cache()
+        line[name.lower()] = measure_workload(BY_ID[name], args.steps, args.warmup)
     print(json.dumps(line), flush=True)
 
 
