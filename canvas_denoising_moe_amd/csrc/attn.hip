@@ -25,6 +25,8 @@
 //     weight exactly 1.
 // fp32 path and odd head sizes (k_attn_simple): one workgroup per query row,
 // keys in chunks of 256 with the same online-softmax recurrence.
+#include <type_traits>
+
 #include "common.h"
 
 namespace {
@@ -34,36 +36,49 @@ constexpr float kLog2e = 1.4426950408889634f;
 // Flash attention for bf16 with K/V tiles copied straight from global memory
 // into LDS (no register staging), two query sub-tiles per wave.
 //
-//   * Work unit = (canvas b, KV head g, key split s) x q-tile of 128 query
-//     rows; each of the 4 waves holds 32 rows as two 16-row sub-tiles, so
-//     every K or V fragment read from LDS feeds two MFMAs.
+//   * Work unit = (canvas b, KV head g, key split s) x q-tile of 256 query
+//     rows; each of the 8 waves holds 32 rows as two 16-row sub-tiles, so
+//     every K or V fragment read from LDS feeds two MFMAs, and one K/V tile
+//     in LDS feeds all 256 rows.
 //   * A 64-key tile of K and of V^T is laid out in LDS in MFMA fragment
 //     order (1 KB blocks, lane l's 16 bytes at offset 16 l), written by
 //     direct global->LDS copies in which every lane fetches exactly the 16
-//     bytes it will later read; reads are conflict-free 16-byte loads.  Two
-//     LDS stages: the copy of tile t + 1 runs while tile t is consumed.
+//     bytes it will later read; reads are conflict-free 16-byte loads.  Four
+//     LDS stages (128 KB at D = 128): the copies of tiles t + 1 and t + 2 are
+//     in flight while tile t is consumed, and tile t + 3 is issued as soon as
+//     every wave is done with tile t - 1.  A tile in one source (prompt or
+//     canvas keys) is copied from a uniform base plus fixed per-lane offsets;
+//     one that crosses the boundary or the split's end goes through registers.
 //   * Scores are computed transposed (S^T = K Q^T).  The keys of a K fragment
 //     are permuted (row m of key block kb holds key 32 (kb/2) + 8 (m/4) +
 //     4 (kb%2) + m%4) so that every lane ends up holding 8 consecutive keys
 //     of one query per 32-key step: the B operand of O^T = V^T P^T, whose A
 //     operand (V^T) is then 16 contiguous bytes per lane, copyable as such.
+//     K and V^T fragments are read from LDS one block ahead of the MFMAs.
 //   * Online softmax in base 2 with a lazily updated reference maximum: the
 //     running state is rescaled only when a tile's maximum exceeds the
 //     reference by more than 2^8 (P then stays <= 256, exact scaling is
 //     unaffected), which skips almost every rescale.  P is rounded to bf16
 //     for the MFMA and the normaliser is the MFMA sum of the same rounded P
-//     (an all-ones A operand), so a single key gives weight exactly 1.
+//     (an all-ones A operand), so a single key gives weight exactly 1.  The
+//     exponentials use the hardware base-2 exponential directly: arguments
+//     are <= 8, and results below the fp32 normal range only ever meet a
+//     bf16 rounding that keeps them negligible next to the maximum's weight.
 // Needs every 8-key group of V^T in one source (key counts multiples of 8).
 template <int D>
-__global__ __launch_bounds__(256, 2) void k_attn_fa(AttnArgs a, int QT, int xcd_map) {
+__global__ __launch_bounds__(512, 2) void k_attn_fa(AttnArgs a, int QT, int xcd_map) {
   constexpr int KT = 64;                 // keys per tile
+  constexpr int NW = 8;                  // waves per workgroup
   constexpr int KS = D / 32, DB = D / 16;
   constexpr int NKB = 4 * KS, NVB = 2 * DB;  // 1 KB fragment blocks of a K tile and of a V^T tile
-  static_assert(NKB % 4 == 0 && NVB % 4 == 0, "the four waves copy equal shares of a tile");
-  __shared__ __align__(16) bf16_t K0[NKB * 512];
-  __shared__ __align__(16) bf16_t K1[NKB * 512];
-  __shared__ __align__(16) bf16_t V0[NVB * 512];
-  __shared__ __align__(16) bf16_t V1[NVB * 512];
+  constexpr int CKW = NKB / NW, CVW = NVB / NW, CPW = CKW + CVW;  // copies per wave per tile
+  static_assert(NKB % NW == 0 && NVB % NW == 0, "the waves copy equal shares of a tile");
+  // four stages (K blocks, then V^T blocks); one array per stage, so that
+  // reads of a stage are seen to depend only on the copies into it
+  __shared__ __align__(16) bf16_t S0[(NKB + NVB) * 512];
+  __shared__ __align__(16) bf16_t S1[(NKB + NVB) * 512];
+  __shared__ __align__(16) bf16_t S2[(NKB + NVB) * 512];
+  __shared__ __align__(16) bf16_t S3[(NKB + NVB) * 512];
 
   int bid = blockIdx.x, unit, qt;
   if (xcd_map) {
@@ -92,7 +107,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fa(AttnArgs a, int QT, int xcd_
   long long row_g[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int qrow = qt * 128 + wave * 32 + j * 16 + lc;
+    const int qrow = qt * 256 + wave * 32 + j * 16 + lc;
     qvalid[j] = qrow < grows;
     qh[j] = g * group + (qvalid[j] ? qrow / N : 0);
     qi[j] = qvalid[j] ? qrow % N : 0;
@@ -113,6 +128,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_fa(AttnArgs a, int QT, int xcd_
     for (int ks = 0; ks < KS; ++ks)
       qf[j][ks] = qvalid[j] ? *reinterpret_cast<const uint4*>(qp + ks * 32 + lg * 8) : make_uint4(0, 0, 0, 0);
   }
+  // wait for Q here, in a form the compiler sees: otherwise it keeps the
+  // loads pending through the copy pipeline and drains all copies at a use
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
   floatx4 oacc[2][DB], lacc[2];
 #pragma unroll
@@ -131,71 +149,186 @@ __global__ __launch_bounds__(256, 2) void k_attn_fa(AttnArgs a, int QT, int xcd_
   // wave index is made wave-uniform so every LDS destination is a scalar.
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int lane_key = 8 * (lc >> 2) + (lc & 3);  // this lane's key within a K block pair
-  auto issue = [&](bf16_t* Kd, bf16_t* Vd, int t0) {
+  // Byte offsets of this lane's 16 bytes within a tile that lies in one
+  // source: K rows are D elements apart; V^T rows (one per d) are a stride
+  // apart that depends on the source, so only the in-row part is kept.
+  uint32_t koff[CKW], voff[CVW];
+  int vrow[CVW];
 #pragma unroll
-    for (int i = 0; i < NKB / 4; ++i) {
-      const int q = wv + 4 * i, kb = q / KS, ks = q - kb * KS;
+  for (int i = 0; i < CKW; ++i) {
+    const int q = wv + NW * i, kb = q / KS, ks = q - kb * KS;
+    koff[i] = 2u * (uint32_t)((32 * (kb >> 1) + 4 * (kb & 1) + lane_key) * D + ks * 32 + lg * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < CVW; ++i) {
+    const int q = wv + NW * i, db = q >> 1, ks2 = q & 1;
+    vrow[i] = db * 16 + lc;
+    voff[i] = 2u * (uint32_t)(ks2 * 32 + lg * 8);
+  }
+  // One direct copy: every lane moves the 16 bytes at base + voff (byte
+  // offset) to LDS at dst + 16 lane.  Written as asm so that the compiler's
+  // own memory-counter bookkeeping does not see it: it cannot tell the
+  // stages apart and would drain every copy in flight before reading any
+  // stage; the waits before the barriers below cover these copies.  M0
+  // (the LDS destination) is set by the compiler through the constraint;
+  // the s_nop is the one wait state a copy to LDS needs after M0 is written.
+  auto copy16 = [](bf16_t* dst, const char* base, uint32_t voff) {
+    const uint32_t lds = (uint32_t)(size_t)((__attribute__((address_space(3))) bf16_t*)dst);
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
+  };
+  auto issue = [&](bf16_t* Kd, bf16_t* Vd, int t0) {
+    const bool in_p = t0 + KT <= min(k1, Lw), in_c = t0 >= Lw && t0 + KT <= k1;
+    if (in_p || in_c) {
+      // the whole tile in one source: a uniform base plus per-lane offsets
+      const char* kb_ = reinterpret_cast<const char*>(in_p ? kp + (long long)t0 * D : kc + (long long)(t0 - Lw) * D);
+      const char* vb_ = reinterpret_cast<const char*>(in_p ? vp + t0 : vc + (t0 - Lw));
+      const uint32_t vstride = 2u * (uint32_t)(in_p ? Lw : N);
+#pragma unroll
+      for (int i = 0; i < CKW; ++i) copy16(Kd + (wv + NW * i) * 512, kb_, koff[i]);
+#pragma unroll
+      for (int i = 0; i < CVW; ++i) copy16(Vd + (wv + NW * i) * 512, vb_, vstride * (uint32_t)vrow[i] + voff[i]);
+      return;
+    }
+    // A tile that crosses from prompt to canvas keys or past the split's end
+    // (rare): per-lane sources, staged through registers.  Its loads are
+    // waited for before the stores to LDS, and the vector memory counter
+    // drains in order, so every copy issued before it has landed as well.
+    uint4 kr[CKW], vr[CVW];
+#pragma unroll
+    for (int i = 0; i < CKW; ++i) {
+      const int q = wv + NW * i, kb = q / KS, ks = q - kb * KS;
       const int key = min(t0 + 32 * (kb >> 1) + 4 * (kb & 1) + lane_key, k1 - 1);
       const bf16_t* src = key < Lw ? kp + key * D : kc + (key - Lw) * D;
-      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) const void*)(src + ks * 32 + lg * 8),
-                                       (__attribute__((address_space(3))) void*)(Kd + q * 512), 16, 0, 0);
+      kr[i] = *reinterpret_cast<const uint4*>(src + ks * 32 + lg * 8);
     }
 #pragma unroll
-    for (int i = 0; i < NVB / 4; ++i) {
-      const int q = wv + 4 * i, db = q >> 1, ks2 = q & 1;
+    for (int i = 0; i < CVW; ++i) {
+      const int q = wv + NW * i, db = q >> 1, ks2 = q & 1;
       const int c = min(t0 + ks2 * 32 + lg * 8, k1 - 8);
       const int d = db * 16 + lc;
       const bf16_t* src = c < Lw ? vp + d * Lw + c : vc + d * N + (c - Lw);
-      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) const void*)src,
-                                       (__attribute__((address_space(3))) void*)(Vd + q * 512), 16, 0, 0);
+      vr[i] = *reinterpret_cast<const uint4*>(src);
     }
+#pragma unroll
+    for (int i = 0; i < CKW; ++i) *reinterpret_cast<uint4*>(Kd + (wv + NW * i) * 512 + lane * 8) = kr[i];
+#pragma unroll
+    for (int i = 0; i < CVW; ++i) *reinterpret_cast<uint4*>(Vd + (wv + NW * i) * 512 + lane * 8) = vr[i];
   };
 
-  // One 64-key tile from a stage.  `edge`: the tile reaches past the split's
-  // end or holds canvas keys under the causal mask.
-  auto consume = [&](const bf16_t* Ks, const bf16_t* Vs, int t0, bool edge) {
-    floatx4 sacc[2][4];
+  // keys visible to query sub-tile j: below the split's end and, under the
+  // causal mask, canvas keys up to the query's own position
+  int klim[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) klim[j] = a.causal ? min(k1, Lw + qi[j] + 1) : k1;
+  // maximum over the four lanes lc, lc + 16, lc + 32, lc + 48 (one query's
+  // keys): the swaps exchange rows 16 and 32 lanes apart
+  auto max_lg = [](float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    x = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+    const uint32_t w = __float_as_uint(x);
+    const auto s16 = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+    return fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+  };
+
+  // ---- the pieces of one 64-key tile ----
+  typedef floatx4 Sacc[2][4];    // S^T of a tile: [sub-tile j][key block kb]
+  typedef uint32_t Pk[2][2][4];  // P^T as bf16 pairs: [j][32-key step][word]
+  using yes = std::true_type;
+  using no = std::false_type;
+  auto mref_of = [&](int j) { return m_ref[j] == -INFINITY ? 0.f : m_ref[j]; };
+  // two P values of slot pair q of key block kb, rounded to bf16
+  auto p_word = [&](const Sacc& acc, int j, int kb, int q, float mr) {
+    return f2bf2(__builtin_amdgcn_exp2f(fmaf(acc[j][kb][2 * q], sc, -mr)),
+                 __builtin_amdgcn_exp2f(fmaf(acc[j][kb][2 * q + 1], sc, -mr)));
+  };
+  // S^T = K Q^T of the tile in stage Ks, K fragments read one key block
+  // ahead of their MFMAs.  WithP: the P of the previous tile (scores `prev`)
+  // is formed in the same block, its exponentials interleaved with these
+  // MFMAs, so the vector and matrix units work at the same time.
+  auto s_tile = [&](const bf16_t* Ks, Sacc& acc, auto with_p, const Sacc& prev, Pk& pk) {
+    constexpr bool WithP = decltype(with_p)::value;
+    float mr[2] = {0.f, 0.f};
+    if constexpr (WithP) {
+      mr[0] = mref_of(0);
+      mr[1] = mref_of(1);
+    }
+    uint4 kfr[2][KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kfr[0][ks] = *reinterpret_cast<const uint4*>(Ks + ks * 512 + lane * 8);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      sacc[0][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
-      sacc[1][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if (kb + 1 < 4) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint4 kf = *reinterpret_cast<const uint4*>(Ks + (kb * KS + ks) * 512 + lane * 8);
+        for (int ks = 0; ks < KS; ++ks)
+          kfr[(kb + 1) & 1][ks] = *reinterpret_cast<const uint4*>(Ks + ((kb + 1) * KS + ks) * 512 + lane * 8);
+      }
+      acc[0][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      acc[1][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          sacc[j][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, kf),
-                                                                 __builtin_bit_cast(bf16x8_v, qf[j][ks]),
-                                                                 sacc[j][kb], 0, 0, 0);
+          acc[j][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, kfr[kb & 1][ks]),
+                                                               __builtin_bit_cast(bf16x8_v, qf[j][ks]), acc[j][kb],
+                                                               0, 0, 0);
+      if constexpr (WithP) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) pk[j][kb >> 1][(kb & 1) * 2 + q] = p_word(prev, j, kb, q, mr[j]);
       }
-      // at most one key block's fragments live at a time (register budget of two waves per SIMD)
-      __builtin_amdgcn_sched_barrier(0);
+      // schedule: the first block's reads, then per block the next block's
+      // reads ahead of this block's MFMAs (with the P arithmetic between them)
+      if (kb == 0) __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);  // DS read
+      if (kb + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
+      if constexpr (WithP) {
+#pragma unroll
+        for (int m = 0; m < 2 * KS; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+        }
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * KS, 0);
+      }
     }
-    uint32_t pk[2][2][4];
-    float mt[2];
-    bool need = false;
+  };
+  // P of a tile's scores on their own (no MFMAs to hide them behind)
+  auto p_tile = [&](const Sacc& acc, Pk& pk) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float mr = mref_of(j);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int q = 0; q < 2; ++q) pk[j][kb >> 1][(kb & 1) * 2 + q] = p_word(acc, j, kb, q, mr);
+    }
+  };
+  // mask (edge tiles) and per-query maximum of a tile's scores, scaled to log2 units
+  auto tile_max = [&](Sacc& acc, int t0, bool edge, float (&mt)[2]) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       if (edge) {
+        // key t0 + 8 lg + c is visible iff c < rel (c a constant per slot)
+        const int rel = klim[j] - t0 - 8 * lg;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = t0 + 32 * (kb >> 1) + 8 * lg + 4 * (kb & 1) + r;
-            const bool vis = key < k1 && !(a.causal && key - Lw > qi[j]);
-            if (!vis) sacc[j][kb][r] = -INFINITY;
-          }
+          for (int r = 0; r < 4; ++r)
+            acc[j][kb][r] = 32 * (kb >> 1) + 4 * (kb & 1) + r < rel ? acc[j][kb][r] : -INFINITY;
       }
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[j][kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      mt[j] = mx * sc;
-      need = need || mt[j] > m_ref[j] + 8.0f;
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, acc[j][kb][r]);
+      mt[j] = max_lg(mx) * sc;
     }
+  };
+  // raise the reference maximum where a tile's maximum exceeds it by more
+  // than 2^8, rescaling the running state (rare)
+  auto rescale = [&](const float (&mt)[2]) {
+    const bool need = mt[0] > m_ref[0] + 8.0f || mt[1] > m_ref[1] + 8.0f;
     if (__any(need)) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -207,65 +340,157 @@ __global__ __launch_bounds__(256, 2) void k_attn_fa(AttnArgs a, int QT, int xcd_
         for (int i = 0; i < DB; ++i) oacc[j][i] *= alpha;
       }
     }
+  };
+  // O^T += V^T P^T and the row sums (all-ones A operand), V^T fragments read
+  // four at a time one group ahead.  WithMax: the (unmasked) maximum of the
+  // next tile's scores `nxt` is taken in the same block.
+  auto pv_tile = [&](const bf16_t* Vs, const Pk& pk, auto with_max, Sacc& nxt, float (&mt)[2]) {
+    constexpr bool WithMax = decltype(with_max)::value;
+    constexpr int NG = 2 * DB / 4;  // groups of 4 fragments: (ks2, 4 d blocks)
+    uint4 vfr[2][4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const float mref = m_ref[j] == -INFINITY ? 0.f : m_ref[j];
+    for (int i = 0; i < 4; ++i) vfr[0][i] = *reinterpret_cast<const uint4*>(Vs + i * 2 * 512 + lane * 8);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+    for (int gi = 0; gi < NG; ++gi) {
+      const int ks2 = gi / (DB / 4), db0 = (gi % (DB / 4)) * 4;
+      if (gi + 1 < NG) {
+        const int ks2n = (gi + 1) / (DB / 4), db0n = ((gi + 1) % (DB / 4)) * 4;
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
-          pk[j][kb >> 1][(kb & 1) * 2 + q] = f2bf2(exp2f(fmaf(sacc[j][kb][2 * q], sc, -mref)),
-                                                   exp2f(fmaf(sacc[j][kb][2 * q + 1], sc, -mref)));
-    }
+        for (int i = 0; i < 4; ++i)
+          vfr[(gi + 1) & 1][i] = *reinterpret_cast<const uint4*>(Vs + ((db0n + i) * 2 + ks2n) * 512 + lane * 8);
+      }
 #pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const uint4 vf = *reinterpret_cast<const uint4*>(Vs + (db * 2 + ks2) * 512 + lane * 8);
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const uint4 pf = make_uint4(pk[j][ks2][0], pk[j][ks2][1], pk[j][ks2][2], pk[j][ks2][3]);
-          oacc[j][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, vf),
-                                                                 __builtin_bit_cast(bf16x8_v, pf), oacc[j][db], 0, 0, 0);
+          oacc[j][db0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, vfr[gi & 1][i]),
+                                                                      __builtin_bit_cast(bf16x8_v, pf),
+                                                                      oacc[j][db0 + i], 0, 0, 0);
+        }
+      if (db0 + 4 == DB) {  // last d group of this key step: the row sums
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint4 pf = make_uint4(pk[j][ks2][0], pk[j][ks2][1], pk[j][ks2][2], pk[j][ks2][3]);
+          lacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, ones),
+                                                             __builtin_bit_cast(bf16x8_v, pf), lacc[j], 0, 0, 0);
         }
       }
+      if (gi == 0) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS read
+      if (gi + 1 < NG) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      const int nm = db0 + 4 == DB ? 10 : 8;
+      if constexpr (WithMax) {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+        }
+        if (nm == 10) __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      } else {
+        if (nm == 10)
+          __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);  // MFMA (with the row sums)
+        else
+          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      }
+    }
+    if constexpr (WithMax) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const uint4 pf = make_uint4(pk[j][ks2][0], pk[j][ks2][1], pk[j][ks2][2], pk[j][ks2][3]);
-        lacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, ones),
-                                                           __builtin_bit_cast(bf16x8_v, pf), lacc[j], 0, 0, 0);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, nxt[j][kb][r]);
+        mt[j] = max_lg(mx) * sc;
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   const int ntiles = k1 > k0 ? (k1 - k0 + KT - 1) / KT : 0;
   // tiles that need the mask: past the split's end, or canvas keys (from key
-  // Lw on) under the causal mask
+  // Lw on) under the causal mask; they all come after the ones that do not
   auto edge = [&](int t0) { return t0 + KT > k1 || (a.causal && t0 + KT > Lw); };
-  // The copies into a stage are waited for explicitly before the barrier that
-  // publishes it: the compiler's own wait before the barrier is missing on the
-  // loop's back edge (the copy issued in the second half of an iteration is
-  // read in the first half of the next), so without this a wave could pass
-  // the barrier while its part of the tile is still in flight.
-  auto copies_done = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
-  if (ntiles > 0) issue(K0, V0, k0);
-  for (int it = 0; it < ntiles; it += 2) {
-    copies_done();
-    __syncthreads();  // tile it is in stage 0 (every wave's copies done); stage 1 is free
-    if (it + 1 < ntiles) issue(K1, V1, k0 + (it + 1) * KT);
-    {
-      const int t0 = k0 + it * KT;
-      consume(K0, V0, t0, edge(t0));
-    }
-    if (it + 1 >= ntiles) break;
-    copies_done();
-    __syncthreads();  // tile it + 1 is in stage 1; stage 0 is free
-    if (it + 2 < ntiles) issue(K0, V0, k0 + (it + 2) * KT);
-    {
-      const int t0 = k0 + (it + 1) * KT;
-      consume(K1, V1, t0, edge(t0));
-    }
+  const int klast = a.causal ? min(k1, Lw) : k1;
+  const int n_main = klast > k0 ? min(ntiles, (klast - k0) / KT) : 0;  // leading unmasked tiles
+
+  // Tile i lives in stage i % 4.  A step waits for the copies of a tile and
+  // then passes a barrier; each wave waits until its own copies of that tile
+  // have landed, and as the vector memory counter drains in issue order it is
+  // enough to allow the copies of the later tiles issued so far (at most
+  // two) to remain outstanding.  A tile staged through registers leaves
+  // nothing outstanding and has already drained the copies before it, so the
+  // counts never wait too little.  The wait and the barrier sit in one asm
+  // statement (a __syncthreads() would add a release fence, which drains
+  // every copy); lgkmcnt(0) publishes register-staged stores to LDS.
+  auto sync_tile = [&](int i, int issued) {
+    const int later = issued - 1 - i;
+    if (later >= 2)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * CPW) : "memory");
+    else if (later == 1)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(CPW) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  constexpr int VB = NKB * 512;  // V^T blocks of a stage
+  // a stage chosen at run time (the masked tail only: reads through such a
+  // pointer are not known to avoid the copies in flight, so they wait for all)
+  auto stage = [&](int i) -> bf16_t* {
+    const int r = i & 3;
+    return r == 0 ? S0 : r == 1 ? S1 : r == 2 ? S2 : S3;
+  };
+
+  // Software pipeline over the unmasked tiles: step t waits for tile t + 1,
+  // refills the stage of tile t - 1 with tile t + 3, then computes S(t + 1)
+  // while forming P(t), and O += P(t) V(t) while taking the maximum of
+  // S(t + 1).
+  Sacc cur, nxt;
+  Pk pk;
+  float mt[2] = {-INFINITY, -INFINITY};
+  if (ntiles > 0) issue(S0, S0 + VB, k0);
+  if (ntiles > 1) issue(S1, S1 + VB, k0 + KT);
+  if (ntiles > 2) issue(S2, S2 + VB, k0 + 2 * KT);
+  if (ntiles > 0) sync_tile(0, min(3, ntiles));
+  if (n_main > 0) {
+    s_tile(S0, cur, no{}, cur, pk);
+    tile_max(cur, k0, false, mt);
+  }
+  auto pipe_step = [&](const bf16_t* Vt, const bf16_t* Kn, bf16_t* Is, int t) {
+    sync_tile(t + 1, min(t + 3, ntiles));
+    if (t + 3 < ntiles) issue(Is, Is + VB, k0 + (t + 3) * KT);
+    rescale(mt);
+    s_tile(Kn, nxt, yes{}, cur, pk);
+    pv_tile(Vt, pk, yes{}, nxt, mt);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) cur[j][kb] = nxt[j][kb];
+  };
+  for (int t = 0; t + 1 < n_main; t += 4) {
+    pipe_step(S0 + VB, S1, S3, t);
+    if (t + 2 >= n_main) break;
+    pipe_step(S1 + VB, S2, S0, t + 1);
+    if (t + 3 >= n_main) break;
+    pipe_step(S2 + VB, S3, S1, t + 2);
+    if (t + 4 >= n_main) break;
+    pipe_step(S3 + VB, S0, S2, t + 3);
+  }
+  if (n_main > 0) {  // the last unmasked tile: its scores are in `cur`
+    const int t = n_main - 1;
+    sync_tile(t + 1, min(t + 3, ntiles));
+    if (t + 3 < ntiles) issue(stage(t + 3), stage(t + 3) + VB, k0 + (t + 3) * KT);
+    rescale(mt);
+    p_tile(cur, pk);
+    pv_tile(stage(t) + VB, pk, no{}, nxt, mt);
+  }
+  for (int t = n_main; t < ntiles; ++t) {  // masked tiles, one at a time
+    sync_tile(t + 1, min(t + 3, ntiles));
+    if (t + 3 < ntiles) issue(stage(t + 3), stage(t + 3) + VB, k0 + (t + 3) * KT);
+    const int t0 = k0 + t * KT;
+    s_tile(stage(t), cur, no{}, cur, pk);
+    tile_max(cur, t0, edge(t0), mt);
+    rescale(mt);
+    p_tile(cur, pk);
+    pv_tile(stage(t) + VB, pk, no{}, nxt, mt);
   }
 
   mfma_drain();
@@ -685,18 +910,13 @@ static void choose_splits(int total, int Hkv, int QT, int* S_out, int* CL_out) {
   *CL_out = CL;
 }
 
-// Key splits of canvas b for the direct-copy kernel (two workgroups per CU):
+// Key splits of canvas b for the direct-copy kernel (one workgroup per CU):
 // enough (KV head x split x q-tile) workgroups to fill the chip's slots once,
-// splits of at most 8192 keys, and for long prompts a split count that fills
-// whole rounds of slots; whole 64-key tiles, at most 64 splits.
+// whole 64-key tiles, at most 64 splits.  The choice depends on the canvas
+// alone, so a canvas's result does not depend on the batch it runs in.
 static void choose_splits_fa(int total, int base, int* S_out, int* CL_out) {
-  const int slots = 2 * 256;
-  const int smin = (slots + base - 1) / base;
-  int S = max(smin, (total + 8191) / 8192);
-  if (S > smin && slots % base == 0) {
-    const int r = slots / base;
-    S = (S + r - 1) / r * r;
-  }
+  const int slots = 256;
+  int S = (slots + base - 1) / base;
   S = min(S, max(1, (total + 63) / 64));
   S = min(S, 64);
   int CL = ((total + S - 1) / S + 63) / 64 * 64;
@@ -715,7 +935,7 @@ hipError_t launch_attention(int is_bf16, const AttnArgs& a0, hipStream_t st, KTi
   for (int b = 0; b < a0.B; ++b) aligned0 = aligned0 && (a0.lw[b] & 7) == 0;
   if (is_bf16 && (a0.D == 128 || a0.D == 64) && aligned0) {
     AttnArgs a = a0;
-    const int QT = (a.Hq / a.Hkv * a.N + 127) / 128;
+    const int QT = (a.Hq / a.Hkv * a.N + 255) / 256;
     int smax = 1;
     a.ubase[0] = 0;
     for (int b = 0; b < a.B; ++b) {
@@ -728,8 +948,8 @@ hipError_t launch_attention(int is_bf16, const AttnArgs& a0, hipStream_t st, KTi
     const int xcd_map = (units % 8) == 0;
     const dim3 grid((unsigned)(units * QT));
     hipEvent_t stop1 = smax == 1 ? t.stop : nullptr;
-    hipError_t e = a.D == 128 ? launch_k(k_attn_fa<128>, grid, dim3(256), 0, st, t.start, stop1, a, QT, xcd_map)
-                              : launch_k(k_attn_fa<64>, grid, dim3(256), 0, st, t.start, stop1, a, QT, xcd_map);
+    hipError_t e = a.D == 128 ? launch_k(k_attn_fa<128>, grid, dim3(512), 0, st, t.start, stop1, a, QT, xcd_map)
+                              : launch_k(k_attn_fa<64>, grid, dim3(512), 0, st, t.start, stop1, a, QT, xcd_map);
     if (e != hipSuccess || smax == 1) return e;
     return launch_k(k_attn_merge<bf16_t>, dim3((unsigned)((rows_all + 3) / 4)), dim3(256), 0, st, nullptr, t.stop, a);
   }

@@ -201,27 +201,31 @@ MHA_MODEL = configs.ModelConfig(
 MHA_W = configs.Workload(name="attn-mha-test", model=MHA_MODEL, batch=2, prompt_len=100, n_steps=1, seed=17)
 
 
-def test_canvas_attention_single_split(torch, dg):
-    # 32 KV heads x 8 query tiles of 64 rows (2 query heads x 256 slots) fill
-    # the chip from one canvas without key splits, so the attention kernel
-    # normalises and stores its output itself (grouped heads, head size 64)
+@pytest.mark.parametrize("lens,ck", [
+    ([100, 37], True),   # prompt lengths not multiples of 8: the general kernel, whose 32 KV
+                         # heads x 8 query tiles fill the chip without key splits
+    ([64, 40], False),   # the direct-copy kernel with one 64-key tile per canvas
+])
+def test_canvas_attention_single_split(torch, dg, lens, ck):
+    # one key split per canvas: the attention kernel normalises and stores its
+    # output itself (grouped heads, head size 64); no merge runs
     m = MHA_MODEL
-    say("attention single split")
-    with dg.Context(m, max_batch=2, max_prompt_len=128) as ctx:
+    say("attention single split", lens, ck)
+    B, N = len(lens), m.canvas_len
+    with dg.Context(m, max_batch=B, max_prompt_len=128) as ctx:
         ctx.set_layer_weights(0, upload.layer_to_device(MHA_W, 0))
-        kv = _load_prompts(torch, ctx, MHA_W, [100, 37])
-        B, N = 2, m.canvas_len
+        kv = _load_prompts(torch, ctx, MHA_W, lens)
         qb = gen.activations(18, 3, (B, N, m.n_heads, m.head_dim), std=1.0, dtype="bf16")
         kb = gen.activations(18, 4, (B, N, m.n_kv_heads, m.head_dim), std=1.0, dtype="bf16")
         vb = gen.activations(18, 5, (B, N, m.n_kv_heads, m.head_dim), std=1.0, dtype="bf16")
         o = torch.empty((B, N, m.n_heads * m.head_dim), dtype=torch.bfloat16, device="cuda")
         ctx.k_canvas_attn(0, B, upload.to_device(qb, "bf16"), upload.to_device(kb, "bf16"),
-                          upload.to_device(vb, "bf16"), o)
+                          upload.to_device(vb, "bf16"), o, canvas_keys=ck)
         torch.cuda.synchronize()
     ref = om.canvas_attention(om.bf16_bits_to_f64(qb), om.bf16_bits_to_f64(kb), om.bf16_bits_to_f64(vb),
-                              [kv[b][0] for b in range(B)], om.bf16_round)
+                              [kv[b][0] for b in range(B)], om.bf16_round, canvas_keys=ck)
     e = rel_err(host64(o).reshape(B * N, -1), ref)
-    print(f"attention single split: rel err {e:.3e}")
+    print(f"attention single split {lens} canvas keys {ck}: rel err {e:.3e}")
     assert e <= TOL["bf16"]
 
 
