@@ -778,10 +778,21 @@ hipError_t run_stream_mt(const StreamArgs& g, const EpiArgs& e, hipStream_t s, K
   return hipErrorInvalidValue;
 }
 
+// dense fp32-output projections over many rows (several canvases): row
+// entries of 64 rows, so fewer entries re-read each weight tile from L2; the
+// caller keeps the grid at about one workgroup per CU, each staging its A
+// rows in 128 KB chunks
+template <typename T, int MT>
+hipError_t run_stream_wide_rows(const StreamArgs& g, const EpiArgs& e, hipStream_t s, KTime t) {
+  if (g.qb || g.ent_off || g.ksplit > 1 || e.kind != EPI_STORE_F32) return hipErrorInvalidValue;
+  return run_stream<T, MT, 2, EPI_STORE_F32, 8, kStreamLdsWideKB>(g, e, s, t);
+}
+
 template <typename T>
 hipError_t run_stream_t(const StreamArgs& g, const EpiArgs& e, hipStream_t s, KTime t) {
   if (g.mt == 1) return run_stream_mt<T, 1>(g, e, s, t);
   if (g.mt == 2) return run_stream_mt<T, 2>(g, e, s, t);
+  if (g.mt == 4) return run_stream_wide_rows<T, 4>(g, e, s, t);
   return hipErrorInvalidValue;
 }
 
