@@ -48,9 +48,23 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src)[:-4] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+# Debug build of the host side under AddressSanitizer (device code unchanged):
+# the runtime's argument checks and error paths run instrumented in a host
+# process, on any machine with hipcc and no GPU.  The library lands outside the
+# package, under _build/asan/, and is loaded only by the test that asks for it.
+ASAN_HOST_FLAGS = [
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+    "-Xarch_host", "-g",
+]
+ASAN_LIB = os.path.join(BUILD_DIR, "asan", "libdg.so")
+
+
+def _compile(src: str, verbose: bool, asan: bool = False) -> str:
+    out_dir = os.path.join(BUILD_DIR, "asan") if asan else BUILD_DIR
+    obj = os.path.join(out_dir, os.path.basename(src)[:-4] + ".o")
+    flags = HIPCC_FLAGS + (ASAN_HOST_FLAGS if asan else [])
+    cmd = [hipcc(), *flags, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -62,22 +76,27 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source for gfx950 and link ``libdg.so``; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    os.makedirs(LIB_DIR, exist_ok=True)
+def build(verbose: bool = False, asan: bool = False) -> str:
+    """Compile every HIP source for gfx950 and link ``libdg.so``; returns its path.
+
+    ``asan``: the AddressSanitizer debug build of the host side instead
+    (``ASAN_LIB``); the product library is left alone."""
+    out = ASAN_LIB if asan else LIB
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    os.makedirs(os.path.join(BUILD_DIR, "asan") if asan else BUILD_DIR, exist_ok=True)
     srcs = sources()
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
+        objs = list(ex.map(lambda s: _compile(s, verbose, asan), srcs))
+    tmp = out + ".tmp"
+    link_flags = ["-Xarch_host", "-fsanitize=address"] if asan else []
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *link_flags, "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
