@@ -161,6 +161,89 @@ def gpu_layer_states(torch, ctx, w, tokens):
     return xs, trace.cpu().numpy()
 
 
+class _KeptExperts:
+    """One expert stack of a layer whose matrices, once widened to float64,
+    are kept for the other passes compared with that layer."""
+
+    def __init__(self, stack):
+        self.stack, self.shape, self.kept = stack, stack.shape, {}
+
+    def __getitem__(self, e):
+        if e not in self.kept:
+            self.kept[e] = self.stack[e]
+        return self.kept[e]
+
+
+class _OneLayer:
+    """Layer ``l`` of oracle weights with its expert matrices kept once
+    widened (the oracle widens each used expert on every call, most of its
+    time at the full sizes); the same float64 values as ``W.layer(l)``."""
+
+    def __init__(self, W, l):
+        self.l = l
+        self.d = {k: (_KeptExperts(v) if isinstance(v, om._ExpertStack) else v) for k, v in W.layer(l).items()}
+
+    def layer(self, l):
+        assert l == self.l
+        return self.d
+
+
+def anchored_passes_compare(torch, ctx, w, W, kvf, t0, t1, tokens, locked, passes, route_delta, logit_delta,
+                            conf_delta_rel, tag):
+    """Passes ``t0 .. t1 - 1`` of a block (``passes[t]``: the GPU pass's
+    ``tokens``, ``locked``, ``pred``, ``conf``, ``trace``; ``tokens``,
+    ``locked``: the canvas before pass ``t0``), each checked exactly as
+    :func:`anchored_pass_compare` checks one pass, with the oracle run layer
+    by layer across the passes so that a layer's expert matrices are widened
+    once for all of them.  Returns the per-pass (worst layer error, conf
+    error, adopted counts)."""
+    m = w.model
+    L = m.n_layers
+    tol = TOL[m.dtype]
+    runs = []
+    for t in range(t0, t1):
+        gpu = passes[t]
+        say(tag, "pass", t, "layer states")
+        xs, tr = gpu_layer_states(torch, ctx, w, tokens)
+        diff = [l for l in range(L) if not np.array_equal(tr[l], gpu["trace"][l])]
+        assert not diff, (tag, t, f"the layer-by-layer replay routes differently from the pass from layer {diff[0]} "
+                                  f"on ({int((tr[diff[0]] != gpu['trace'][diff[0]]).any(axis=1).sum())} rows)")
+        runs.append({"t": t, "tokens": tokens, "locked": locked, "xs": xs, "tr": tr, "gpu": gpu, "worst": 0.0,
+                     "adopted": {"route": 0, "pred": 0, "lock": 0}})
+        tokens, locked = gpu["tokens"], gpu["locked"]
+    lens = [w.prompt_len] * w.batch
+    for l in range(L):
+        Wl = _OneLayer(W, l)
+        for r in runs:
+            route = [None] * L
+            route[l] = r["tr"][l]
+            sh = om.Shadow(route_idx=route, delta_route=route_delta)
+            ref = om.forward_hidden(r["xs"][l], Wl, m, kvf, lens, layers=[l], shadow=sh)
+            e = rel_err(r["xs"][l + 1], ref)
+            r["worst"] = max(r["worst"], e)
+            assert not sh.failures, (tag, r["t"], l, sh.failures[:5])
+            assert e <= tol, (tag, r["t"], l, e)
+            r["adopted"]["route"] += sh.adopted["route"]
+        del Wl
+    out = []
+    for r in runs:
+        t, gpu = r["t"], r["gpu"]
+        steps = [w.n_steps - t] * w.batch
+        t_o, l_o, pred_o, conf_o, sh = oracle_head_step(r["xs"][L], W, m, r["tokens"], r["locked"], steps, gpu,
+                                                        logit_delta, conf_delta_rel)
+        assert not sh.failures, (tag, t, sh.failures[:5])
+        ce = rel_err(gpu["conf"], conf_o)
+        assert ce <= tol, (tag, t, ce)
+        assert np.array_equal(gpu["tokens"], t_o), (tag, t)
+        assert np.array_equal(gpu["locked"], l_o), (tag, t)
+        r["adopted"]["pred"] += sh.adopted["pred"]
+        r["adopted"]["lock"] += sh.adopted["lock"]
+        print(f"{tag} pass {t}: every layer from the GPU's own input within {r['worst']:.3e}; conf rel err "
+              f"{ce:.3e}; adopted {r['adopted']}", flush=True)
+        out.append((r["worst"], ce, r["adopted"]))
+    return out
+
+
 def anchored_pass_compare(torch, ctx, w, W, kvf, t, tokens, locked, gpu, route_delta, logit_delta,
                           conf_delta_rel, tag):
     """Pass ``t`` of a block compared with the oracle layer by layer: every

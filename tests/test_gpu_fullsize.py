@@ -29,8 +29,8 @@ import os
 import numpy as np
 import pytest
 
-from gpu_util import (DELTA_REL, TOL, anchored_pass_compare, host64, needs_gpu, oracle_head_step, rel_err, rms,
-                      run_block_stepwise, say)
+from gpu_util import (DELTA_REL, TOL, anchored_pass_compare, anchored_passes_compare, host64, needs_gpu,
+                      oracle_head_step, rel_err, rms, run_block_stepwise, say)
 from oracle import eb
 from oracle import model as om
 from oracle.inputs import prompt_kv_fn, weights_for
@@ -192,12 +192,9 @@ def _route_delta(w):
 def _anchored_block(torch, ctx, w, W, tok0, lk0, passes, t0, t1, route_delta):
     kvf = prompt_kv_fn(w)
     tokens, locked = (tok0, lk0) if t0 == 0 else (passes[t0 - 1]["tokens"], passes[t0 - 1]["locked"])
-    out = []
-    for t in range(t0, t1):
-        p = passes[t]
-        out.append(anchored_pass_compare(torch, ctx, w, W, kvf, t, tokens, locked, p, route_delta,
-                                         DELTA_REL["bf16"], DELTA_REL["bf16"], w.name))
-        tokens, locked = p["tokens"], p["locked"]
+    out = anchored_passes_compare(torch, ctx, w, W, kvf, t0, t1, tokens, locked, passes, route_delta,
+                                  DELTA_REL["bf16"], DELTA_REL["bf16"], w.name)
+    torch.cuda.empty_cache()
     return out
 
 
