@@ -9,10 +9,10 @@
 // 8 row tiles of 16 rows and 4 column blocks of 16 (128 fp32 accumulators per
 // lane).  The embedding (the packed B operand, 1 GB at V = 262144) streams
 // through a 4-deep register ring of fragments, 32 MFMAs per k-step per wave;
-// h rows are staged through LDS in double-buffered chunks of 4 k-steps, each
-// wave loading one k-step of the next chunk into registers while the current
-// chunk is consumed, so no load latency sits between chunks.  The whole state
-// fits 256 VGPRs (accumulators included), so two workgroups share a CU.  Units
+// h rows go through LDS in double-buffered chunks of 4 k-steps, copied
+// straight from global memory one chunk ahead, so no load latency sits
+// between chunks and no registers hold them in flight.  The whole state fits
+// 256 VGPRs (accumulators included), so two workgroups share a CU.  Units
 // (vocabulary tile, row group) are sliced contiguously per XCD, so the row
 // groups of one vocabulary tile run side by side on one XCD and read its
 // embedding fragments from HBM once, through that XCD's L2.
@@ -39,9 +39,7 @@ constexpr int kLmRT = 8;   // row tiles of 16 per workgroup
 constexpr int kLmRows = 16 * kLmRT;
 constexpr int kLmKC = 4;   // k-steps per staged A chunk
 constexpr int kLmR = 4;    // W ring depth in k-steps
-constexpr int kLmKS = kLmKC / 4;  // k-steps of a chunk staged by each wave
 static_assert(kLmKC % kLmR == 0, "ring slot == k-step within the chunk mod R");
-static_assert(kLmKC % 4 == 0, "the four waves stage equal shares of a chunk");
 constexpr int kLmLds = 2 * kLmKC * kLmRT * 512 * 2;  // two chunks, bf16
 
 struct Part { float m; int i; float s; };
@@ -88,33 +86,39 @@ __global__ __launch_bounds__(256) void k_lm_head(LmArgs a) {
     for (int cc = 0; cc < 4; ++cc)
       b[i][cc] = *reinterpret_cast<const v4u*>(bp[cc] + (long long)min(i, KB - 1) * 512);
 
-  // A staging: wave w owns k-steps w*KS .. w*KS + KS-1 of every chunk, all
-  // row tiles; lane j carries row (j & 15) of a tile, k-group j >> 4 (fragment
-  // order).  Rows past M repeat the last row (their results are never used).
-  // One lane pointer plus a wave-uniform offset per row tile: a tile past M
-  // repeats the last full tile (M is a multiple of 16).
-  const bf16_t* __restrict__ H = reinterpret_cast<const bf16_t*>(a.h);
-  const bf16_t* hbase = H + (long long)(lane & 15) * a.K + wave * kLmKS * 32 + (lane >> 4) * 8;
-  long long hoff[kLmRT];
+  // A staging: chunks of KC k-steps copied straight from global memory into
+  // LDS in fragment order [KC][RT][64][8], one chunk ahead.  Wave w copies row
+  // tiles w and w + 4 of every k-step of a chunk (8 blocks of 1 KB); lane j
+  // moves row (j & 15) of its tile at k offset 8 (j >> 4).  A tile past M
+  // repeats the last full tile (M is a multiple of 16; those rows' results are
+  // never used).  The copies are asm, out of the compiler's sight: its own
+  // wait bookkeeping cannot tell the two buffers apart and would drain the
+  // weight ring before every LDS read.  The wait before each chunk's barrier
+  // covers them: the vector memory counter drains in order, and only the
+  // chunk's 4 KC weight refills are issued after them.
+  static_assert(kLmRT == 8 && kLmKC * kLmRT == 32, "four waves copy two row tiles of every k-step");
+  constexpr int kRefills = 4 * kLmKC;  // vector memory ops issued after a chunk's copies
+  const char* hbase = reinterpret_cast<const char*>(reinterpret_cast<const bf16_t*>(a.h) + (long long)rbase * a.K);
+  uint32_t hoff[2];
 #pragma unroll
-  for (int i = 0; i < kLmRT; ++i) hoff[i] = (long long)min(rbase + i * 16, a.M - 16) * a.K;
-  v4u st[kLmKS][kLmRT];  // the next chunk's share of this wave, in flight
-#define LM_LOAD_CHUNK(c)                                                                     \
-  _Pragma("unroll") for (int j = 0; j < kLmKS; ++j)                                          \
-    _Pragma("unroll") for (int i = 0; i < kLmRT; ++i)                                        \
-      st[j][i] = *reinterpret_cast<const v4u*>(hbase + hoff[i] + ((c) * kLmKC + j) * 32);
-#define LM_STORE_CHUNK(c)                                                                    \
-  {                                                                                          \
-    bf16_t* dst = As + (((c) & 1) * kLmKC + wave * kLmKS) * kLmRT * 512 + lane * 8;          \
-    _Pragma("unroll") for (int j = 0; j < kLmKS; ++j)                                        \
-      _Pragma("unroll") for (int i = 0; i < kLmRT; ++i)                                      \
-        *reinterpret_cast<v4u*>(dst + (j * kLmRT + i) * 512) = st[j][i];                     \
+  for (int h = 0; h < 2; ++h) {
+    const int row = min(rbase + (wave + 4 * h) * 16, a.M - 16) - rbase + (lane & 15);
+    hoff[h] = (uint32_t)(((long long)row * a.K + (lane >> 4) * 8) * 2);
   }
+  auto copy_chunk = [&](int c) {
+    bf16_t* dst = As + (c & 1) * kLmKC * kLmRT * 512;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int kl = i >> 1, rt = wave + 4 * (i & 1);
+      const uint32_t lds = (uint32_t)(size_t)((__attribute__((address_space(3))) bf16_t*)(dst + (kl * kLmRT + rt) * 512));
+      const uint32_t voff = hoff[i & 1] + (uint32_t)((c * kLmKC + kl) * 64);
+      // the s_nop is the wait state a copy to LDS needs after M0 is written
+      asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(hbase), "{m0}"(lds) : "memory");
+    }
+  };
   const int NC = KB / kLmKC;
-  LM_LOAD_CHUNK(0)
-  LM_STORE_CHUNK(0)
-  LM_LOAD_CHUNK(min(1, NC - 1))
-  __syncthreads();
+  copy_chunk(0);
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   floatx4 acc[kLmRT][4];
 #pragma unroll
@@ -123,15 +127,18 @@ __global__ __launch_bounds__(256) void k_lm_head(LmArgs a) {
     for (int cc = 0; cc < 4; ++cc) acc[rt][cc] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   for (int c = 0; c < NC; ++c) {
+    // its buffer was last read in chunk c - 1, before the barrier that ended it
+    if (c + 1 < NC) copy_chunk(c + 1);
     const bf16_t* Ab = As + (c & 1) * kLmKC * kLmRT * 512 + lane * 8;
 #pragma unroll
     for (int kl = 0; kl < kLmKC; ++kl) {
+      v4u af[kLmRT];  // the k-step's A fragments, all read before its MFMAs
 #pragma unroll
-      for (int rt = 0; rt < kLmRT; ++rt) {
-        const v4u af = *reinterpret_cast<const v4u*>(Ab + (kl * kLmRT + rt) * 512);
+      for (int rt = 0; rt < kLmRT; ++rt) af[rt] = *reinterpret_cast<const v4u*>(Ab + (kl * kLmRT + rt) * 512);
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) mma_bf16(acc[rt][cc], af, b[kl % kLmR][cc]);
-      }
+      for (int rt = 0; rt < kLmRT; ++rt)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) mma_bf16(acc[rt][cc], af[rt], b[kl % kLmR][cc]);
       const int kn = min(c * kLmKC + kl + kLmR, KB - 1);
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc)
@@ -140,14 +147,9 @@ __global__ __launch_bounds__(256) void k_lm_head(LmArgs a) {
       // sink them to the end of the chunk and drain the ring
       __builtin_amdgcn_sched_barrier(0);
     }
-    // unconditional, so the compiler's load counters stay exact: past the last
-    // chunk this rewrites a buffer nobody reads again
-    LM_STORE_CHUNK(c + 1)  // its buffer was last read in chunk c - 1, before the barrier
-    LM_LOAD_CHUNK(min(c + 2, NC - 1))
-    __syncthreads();
+    // this chunk's LDS reads done and the next chunk landed, in every wave
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kRefills) : "memory");
   }
-#undef LM_LOAD_CHUNK
-#undef LM_STORE_CHUNK
   mfma_drain();
 
   const int col_in = lane & 15, rq = (lane >> 4) * 4;
