@@ -912,15 +912,20 @@ static void choose_splits(int total, int Hkv, int QT, int* S_out, int* CL_out) {
 
 // Key splits of canvas b for the direct-copy kernel (one workgroup per CU):
 // enough (KV head x split x q-tile) workgroups to fill the chip's slots once,
-// whole 64-key tiles, at most 64 splits.  The choice depends on the canvas
-// alone, so a canvas's result does not depend on the batch it runs in.
+// whole 64-key tiles, at least 256 keys per split, at most 64 splits.  The
+// choice depends on the canvas alone, so a canvas's result does not depend on
+// the batch it runs in.  The 256-key floor only moves the 1280-key
+// sliding-window layers (10 splits of 128 -> 5 of 256): on one canvas it is
+// neutral (attention + merge 26.6 -> 26.3 us per layer), on four it halves
+// the fp32 partials the merge reads (112.3 -> 99.5 us per layer; a 512-key
+// floor gave 89.4 there but 31.1 on one canvas).
 static void choose_splits_fa(int total, int base, int* S_out, int* CL_out) {
   const int slots = 256;
   int S = (slots + base - 1) / base;
   S = min(S, max(1, (total + 63) / 64));
   S = min(S, 64);
   int CL = ((total + S - 1) / S + 63) / 64 * 64;
-  if (CL < 64) CL = 64;
+  if (CL < 256) CL = 256;
   S = max(1, (total + CL - 1) / CL);
   *S_out = S;
   *CL_out = CL;

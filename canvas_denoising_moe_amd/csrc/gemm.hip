@@ -788,13 +788,16 @@ hipError_t run_stream_wide_rows(const StreamArgs& g, const EpiArgs& e, hipStream
   return run_stream<T, MT, 2, EPI_STORE_F32, 8, kStreamLdsWideKB>(g, e, s, t);
 }
 
-// bf16 expert GEMMs over 64-row entries: gate|up in the 32-row entries' shape;
-// down with 64 KB of LDS, which its fp32 output tiles need at 64 rows
+// bf16 GEMMs over 64-row entries with a fused epilogue: expert gate|up in the
+// 32-row entries' shape; down with 64 KB of LDS, which its fp32 output tiles
+// need at 64 rows; the q/k/v projection of several canvases in 64 KB A chunks
+// (two workgroups per CU)
 template <typename T>
-hipError_t run_stream_experts_wide(const StreamArgs& g, const EpiArgs& e, hipStream_t s, KTime t) {
+hipError_t run_stream_wide_epi(const StreamArgs& g, const EpiArgs& e, hipStream_t s, KTime t) {
   if constexpr (sizeof(T) == 2) {
     if (!g.qb && e.kind == EPI_GEGLU) return run_stream<T, 4, 2, EPI_GEGLU, 8, kStreamLdsKB>(g, e, s, t);
     if (!g.qb && e.kind == EPI_DOWN) return run_stream<T, 4, 4, EPI_DOWN, 2, 64>(g, e, s, t);
+    if (!g.qb && e.kind == EPI_QKV) return run_stream<T, 4, 2, EPI_QKV, 8, 64>(g, e, s, t);
   }
   return hipErrorInvalidValue;
 }
@@ -803,7 +806,7 @@ template <typename T>
 hipError_t run_stream_t(const StreamArgs& g, const EpiArgs& e, hipStream_t s, KTime t) {
   if (g.mt == 1) return run_stream_mt<T, 1>(g, e, s, t);
   if (g.mt == 2) return run_stream_mt<T, 2>(g, e, s, t);
-  if (g.mt == 4 && e.kind != EPI_STORE_F32) return run_stream_experts_wide<T>(g, e, s, t);
+  if (g.mt == 4 && e.kind != EPI_STORE_F32) return run_stream_wide_epi<T>(g, e, s, t);
   if (g.mt == 4) return run_stream_wide_rows<T, 4>(g, e, s, t);
   return hipErrorInvalidValue;
 }

@@ -209,15 +209,15 @@ bool is_global(const dg_config& c, int l) { return (c.global_layer_mask >> l) & 
 constexpr int kStreamMT = 2;
 constexpr int kEntryRows = 16 * kStreamMT;
 
-// Row tiles per entry of a dense fp32-output projection with NB n-blocks (8
-// per workgroup tile) over M rows: starting from mt, doubled up to 4 while
-// the grid keeps at least one workgroup per CU, so that with many rows each
+// Row tiles per entry of a dense projection with NB n-blocks (8 per
+// workgroup tile) over M rows: starting from mt, doubled up to 4 while the
+// grid keeps at least one workgroup per CU, so that with many rows each
 // weight tile is read from L2 by fewer entries (measured on four canvases:
-// output projection 26.0 -> 22.6 us with 64-row entries; 128-row entries
-// made the q/k/v projection slower, 53.1 against 51.3 us, as its A rows are
-// then staged in four synchronous chunks).  The choice does not change any
-// row's result (an MFMA row depends only on its own A row, and the k order is
-// the same).
+// output projection 26.0 -> 22.6 us and q/k/v projection 51.7 -> 41.3 us with
+// 64-row entries; 128-row entries made the q/k/v projection slower, 53.1
+// against 51.3 us, as its A rows are then staged in four synchronous chunks).
+// The choice does not change any row's result (an MFMA row depends only on its
+// own A row, and the k order is the same).
 int dense_mt(int NB, int M, int mt) {
   const long long tiles = (NB + 7) / 8;
   while (mt < 4 && tiles * ((M + 32 * mt - 1) / (32 * mt)) >= 256) mt *= 2;
@@ -410,7 +410,9 @@ dg_status enqueue_qkv(dg_ctx* ctx, int l, int B, const void* a, void* q, void* k
   StreamArgs g{};
   g.A = a; g.lda = H; g.B = ctx->L[l].qkv; g.K = H;
   g.NB = (c.n_heads + 2 * c.n_kv_heads) * D / 16;
-  g.mt = kStreamMT; g.n_dense = (M + kEntryRows - 1) / kEntryRows; g.dense_rows = M;
+  // 64-row entries once that still fills the chip (several canvases), bf16 only
+  g.mt = ctx->bf16 ? dense_mt(g.NB, M, kStreamMT) : kStreamMT;
+  g.n_dense = (M + 16 * g.mt - 1) / (16 * g.mt); g.dense_rows = M;
   EpiArgs e{};
   e.kind = EPI_QKV;
   e.q = q; e.k = k; e.v = v;

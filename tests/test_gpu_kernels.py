@@ -139,11 +139,13 @@ def _load_prompts(torch, ctx, w, lens):
     return kv
 
 
-def test_qkv_rope_matches_oracle(torch, actx):
+@pytest.mark.parametrize("B", [1, 2])
+def test_qkv_rope_matches_oracle(torch, actx, B):
+    # one canvas: 32-row entries; two canvases fill the chip with 64-row entries
     m = ATTN_MODEL
-    lens = [1024, 4000]
+    lens = [1024, 4000][:B]
     _load_prompts(torch, actx, ATTN_W, lens)
-    B, N = 2, m.canvas_len
+    N = m.canvas_len
     a_bits = gen.activations(12, 2, (B * N, m.hidden), std=1.0, dtype="bf16")
     a = upload.to_device(a_bits, "bf16")
     for l in range(m.n_layers):
