@@ -549,23 +549,64 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs g, EpiArgs e) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) arow[m] = A + (long long)s_rows[m * 16 + (lane & 15)] * g.lda + (lane >> 4) * 8;
   }
-  for (int kc0 = 0; kc0 < KB; kc0 += KC) {
-    const int nk = min(KC, KB - kc0);  // k-steps in this chunk (< KC only in the last one)
-    __syncthreads();                   // row indices written / previous chunk consumed
-    if constexpr (sizeof(T) == 2) {
-      // direct global->LDS copies: one 1 KB fragment block (k-step, row tile) per
-      // wave instruction, all of the chunk in flight at once and no registers
-      // held; the wait before the barrier below covers them
-      for (int q = wave; q < nk * MT; q += 4) {
-        const int kl = q / MT, m = q - kl * MT;
-        const T* src = arow[0];
+  // bf16 A: the rows of a chunk are copied straight from global memory into
+  // LDS in fragment order, one 1 KB fragment block (k-step, row tile) per wave
+  // instruction, all in flight at once and no registers held.  When K needs
+  // more than one chunk, the LDS budget holds two chunks of KC / 2 k-steps and
+  // chunk c + 1 is copied while chunk c is consumed.  The copies are asm, out
+  // of the compiler's sight: its wait bookkeeping cannot tell the buffers
+  // apart and put a full drain of the vector memory counter before every
+  // chunk, emptying the weight ring.  The explicit wait closing a chunk covers
+  // them instead: the counter drains in issue order, and only the chunk's
+  // NREF weight refills are issued after its successor's copies.  (The
+  // compiler's own waits for the ring count those copies as ops it does not
+  // know of, so right after them such a wait is stricter than it needs to be
+  // by up to the chunk's copies: a small cost against the drain.)  Measured:
+  // one canvas gate|up 95.6 -> 94.9 us, MXFP4 gate|up 44.5 -> 42.6 us; four
+  // canvases (64-row entries) gate|up 168.3 -> 163.5 us, the pass 16.20 ->
+  // 15.92 ms.
+  constexpr bool DBUF = sizeof(T) == 2;
+  constexpr int KCH = DBUF ? KC / 2 : KC;  // k-steps per chunk when double-buffered
+  static_assert(!DBUF || (QB ? KCH % (4 * R) == 0 : KCH % R == 0), "a half chunk must hold whole rounds of the ring");
+  constexpr int NREF_ALL = QB ? (KCH / 4) * WN * 2 : KCH * WN;  // refills of one full chunk
+  constexpr int NREF = NREF_ALL < 63 ? NREF_ALL : 63;             // fewer is stricter, never wrong
+  const bool dbuf = DBUF && KB > KC;
+  const int CK = dbuf ? KCH : KC;  // k-steps per chunk
+  // fragment block q = (k-step kl, row tile m) sits at q = kl * MT + m; wave w
+  // copies the blocks q = w (mod 4), i.e. row tile w % MT of the k-steps
+  // kl = w / MT (mod 4 / MT), so each wave needs one source row pointer
+  static_assert(4 % MT == 0, "four waves share a chunk's row tiles evenly");
+  const T* crow = nullptr;
+  if constexpr (sizeof(T) == 2) {
+    crow = arow[0];
 #pragma unroll
-        for (int mm = 1; mm < MT; ++mm)
-          if (m == mm) src = arow[mm];
-        __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) const void*)(src + (kc0 + kl) * 32),
-                                         (__attribute__((address_space(3))) void*)(As + q * 512), 16, 0, 0);
+    for (int mm = 1; mm < MT; ++mm)
+      if (wave % MT == mm) crow = arow[mm];
+  }
+  auto copy_chunk = [=](int buf, int k0, int nk) {
+    if constexpr (sizeof(T) == 2) {
+      T* dst = As + buf * KCH * MT * 512 + (wave % MT) * 512;
+      for (int kl = wave / MT; kl < nk; kl += 4 / MT) {
+        const T* src = crow + (k0 + kl) * 32;
+        const uint32_t lds = (uint32_t)(size_t)((__attribute__((address_space(3))) T*)(dst + kl * MT * 512));
+        // the s_nop is the wait state a copy to LDS needs after M0 is written
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
       }
+    }
+  };
+  if constexpr (sizeof(T) == 2) {
+    copy_chunk(0, 0, min(CK, KB));
+    // the first chunk and the ring's first loads (issued before it) both land here
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+  for (int kc0 = 0, c = 0; kc0 < KB; kc0 += CK, ++c) {
+    const int nk = min(CK, KB - kc0);  // k-steps in this chunk (< CK only in the last one)
+    if constexpr (sizeof(T) == 2) {
+      // (one chunk when !dbuf, copied above) its buffer was last read in chunk
+      // c - 1, before the barrier that closed it
+      if (dbuf && kc0 + CK < KB) copy_chunk((c + 1) & 1, kc0 + CK, min(CK, KB - kc0 - CK));
     } else {
+      __syncthreads();  // row indices written / previous chunk consumed
       const int k8s = nk * 4;          // 8-element groups per row within the chunk
       const int groups8 = ROWS * k8s;
       constexpr int U = 4;  // fp32: loads in flight, bounded by the ring's registers
@@ -584,14 +625,14 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs g, EpiArgs e) {
           st_frag<T>(As + (((k8 >> 2) * MT + (r >> 4)) * 64 + (r & 15) + 16 * (k8 & 3)) * 8, v[u]);
         }
       }
+      __syncthreads();
     }
-    __syncthreads();
     // One branch-free loop over this chunk in groups of R k-steps.  Keeping the
     // accumulators in one loop with no peeled tail also keeps them in place: a
     // peeled tail made the register allocator copy them out of the accumulator
     // registers right behind the last MFMA, and those reads returned values
     // the MFMA had not yet written.
-    const T* Ap = As + lane * 8;
+    const T* Ap = As + (dbuf ? (c & 1) * KCH * MT * 512 : 0) + lane * 8;
     if constexpr (QB == 0) {
       for (int kb0 = kc0; kb0 < kc0 + nk; kb0 += R) {
 #pragma unroll
@@ -646,6 +687,10 @@ __global__ __launch_bounds__(256) void k_stream(StreamArgs g, EpiArgs e) {
         }
       }
     }
+    // bf16, more than one chunk: this chunk's LDS reads done and the next
+    // chunk landed, in every wave
+    if constexpr (sizeof(T) == 2)
+      if (dbuf) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NREF) : "memory");
   }
   mfma_drain();
   if constexpr (EPI == EPI_DOWN && sizeof(T) == 2) {
@@ -788,14 +833,15 @@ hipError_t run_stream_wide_rows(const StreamArgs& g, const EpiArgs& e, hipStream
   return run_stream<T, MT, 2, EPI_STORE_F32, 8, kStreamLdsWideKB>(g, e, s, t);
 }
 
-// bf16 GEMMs over 64-row entries with a fused epilogue: expert gate|up in the
-// 32-row entries' shape; down with 64 KB of LDS, which its fp32 output tiles
-// need at 64 rows; the q/k/v projection of several canvases in 64 KB A chunks
-// (two workgroups per CU)
+// bf16 GEMMs over 64-row entries with a fused epilogue, each with 64 KB of
+// LDS (two workgroups per CU), so that a half chunk holds whole rounds of the
+// ring: expert gate|up in the 32-row entries' shape, down (whose fp32 output
+// tiles need that much at 64 rows), and the q/k/v projection of several
+// canvases
 template <typename T>
 hipError_t run_stream_wide_epi(const StreamArgs& g, const EpiArgs& e, hipStream_t s, KTime t) {
   if constexpr (sizeof(T) == 2) {
-    if (!g.qb && e.kind == EPI_GEGLU) return run_stream<T, 4, 2, EPI_GEGLU, 8, kStreamLdsKB>(g, e, s, t);
+    if (!g.qb && e.kind == EPI_GEGLU) return run_stream<T, 4, 2, EPI_GEGLU, 8, 64>(g, e, s, t);
     if (!g.qb && e.kind == EPI_DOWN) return run_stream<T, 4, 4, EPI_DOWN, 2, 64>(g, e, s, t);
     if (!g.qb && e.kind == EPI_QKV) return run_stream<T, 4, 2, EPI_QKV, 8, 64>(g, e, s, t);
   }
