@@ -346,21 +346,22 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs g, EpiArgs e) {
 // K.  The ring's first loads go out before anything else, so the weight
 // stream is under way while A is staged.  The entry's A rows are staged into
 // LDS in MFMA A-fragment order, [k-step][row tile][64 lanes][8] (every lane
-// reads its own 16 contiguous bytes), in chunks of LK KB copied straight from
-// global memory into LDS (bf16); the ring runs on across chunk boundaries
-// (weights do not depend on A).  Loads in the
-// k loop are unconditional so the compiler's wait counts stay exact; k-steps
-// past the end use a zero A fragment and clamped refills.
+// reads its own 16 contiguous bytes) within an LDS budget of LK KB, copied
+// straight from global memory into LDS (bf16; double-buffered half chunks
+// when K needs more than one chunk); the ring runs on across chunk boundaries
+// (weights do not depend on A).  Loads in the k loop are unconditional so the
+// compiler's wait counts stay exact; k-steps past the end use a zero A
+// fragment and clamped refills.
 //
 // Entries come either from a dense row range or from the router's work list
 // (expert, first row, end row), in which heavy experts are split into several
 // entries that run in parallel.  Blocks are ordered tile-major over (tile,
 // entry) and every XCD (blockIdx & 7) takes a contiguous slice, so the entries
 // of one expert run back to back on one XCD and share that expert's W tile
-// through its L2.  Wider entries (MT = 2) halve the weight reads of dense
-// GEMMs and of experts with more than 16 rows.
+// through its L2.  Wider entries (MT = 2, or 4 with many rows) cut the weight
+// reads of dense GEMMs and of experts with more rows than one tile.
 // ----------------------------------------------------------------------------
-// LDS budget of one A chunk, in KB: 32 keeps three 32-row workgroups per CU;
+// LDS budget of the A staging, in KB: 32 keeps three 32-row workgroups per CU;
 // a grid of at most one workgroup per CU (the dense projections of one canvas)
 // takes 128 and stages the whole K range of its rows at once.
 constexpr int kStreamLdsKB = 32, kStreamLdsWideKB = 128;
