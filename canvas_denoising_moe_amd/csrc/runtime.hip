@@ -224,8 +224,9 @@ int dense_mt(int NB, int M, int mt) {
   return mt;
 }
 
-// capacity of the expert work list for M tokens: every routed expert adds at
-// most one partial entry beyond M*k/kEntryRows, the shared expert M/kEntryRows
+// capacity of the expert work list for M tokens in entries of er rows: every
+// routed expert adds at most one partial entry beyond M*k/er, the shared
+// expert M/er (the workspace is sized for the smallest entries, 32 rows)
 int work_cap(const dg_config& c, int M, int er = kEntryRows) {
   return c.n_experts + (M * c.top_k + er - 1) / er + (M + er - 1) / er;
 }
