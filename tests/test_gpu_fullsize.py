@@ -219,6 +219,22 @@ def test_c3_block_anchored_passes_4_to_7(torch, c3ctx, c3_oracle, c3_block):
           f"when its input moves by half a bf16 ulp (tests/golden/agreement_c3.json)")
 
 
+def test_c3_passes_repeat_bit_for_bit(torch, c3ctx, c3_block):
+    """Run twice, compare bits: the block's first two passes run again from
+    the same canvas on the same context give the same routing at every
+    layer, confidence, argmax, tokens and lock mask, bit for bit (no float
+    atomics anywhere; every sum runs in a fixed order)."""
+    w = C3
+    tok0, lk0, passes = c3_block
+    t0, l0, again = run_block_stepwise(torch, c3ctx, w, steps=2)
+    assert np.array_equal(t0, tok0) and np.array_equal(l0, lk0)
+    for t, p in enumerate(again):
+        for key in ("trace", "conf", "pred", "tokens", "locked"):
+            assert np.array_equal(p[key], passes[t][key]), (t, key)
+    print(f"{w.name}: passes 0 and 1 run again from the same canvas equal the first run bit for bit "
+          f"(routing of all {w.model.n_layers} layers, confidence, argmax, tokens, lock mask)")
+
+
 def test_c3_lm_head_sampled_rows(torch, c3ctx):
     w = C3
     m = w.model
