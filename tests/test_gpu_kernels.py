@@ -78,9 +78,14 @@ def _expected_scatter(idx, E):
     return counts, offsets, np.array(perm)
 
 
+# the last three: the largest expert count at the scatter's bitmap bound
+# (256 experts x 2048 rows = 16384 words), an expert count that leaves part
+# of every lane's last logit group empty with a ragged row count, and k = 1
 @pytest.mark.parametrize("rows,E,k,std,integer", [(256, 128, 8, 1.0, False), (1024, 128, 8, 2.0, False),
                                                   (256, 128, 8, 1.0, True), (4096, 128, 8, 1.0, False),
-                                                  (32, 16, 2, 1.0, True), (1, 16, 2, 1.0, False)])
+                                                  (32, 16, 2, 1.0, True), (1, 16, 2, 1.0, False),
+                                                  (2048, 256, 8, 1.0, True), (77, 100, 3, 1.0, False),
+                                                  (64, 200, 1, 2.0, True)])
 def test_moe_route_bit_exact(torch, dg, rows, E, k, std, integer):
     say("moe_route", rows, E, k, integer)
     r = gen.router_logits(5 + rows, rows, E, std)
