@@ -265,14 +265,37 @@ def c2ctx(torch, dg):
     ctx.close()
 
 
-def test_moe_ffn_matches_oracle(torch, c2ctx):
+def _concentrated_routing(M, E, k, pattern):
+    """Routing that piles rows onto few experts.  "same8": every token picks
+    experts 0..7 in its own order (each gets all M rows, split over several
+    work entries; the other experts stay empty).  "hot127": slot 0 of every
+    token is expert 127, the other slots distinct random experts.  Gates are
+    a softmax over random logits of the k picks."""
+    rng = np.random.default_rng([31, M, E, k, len(pattern)])
+    idx = np.empty((M, k), dtype=np.int64)
+    for t in range(M):
+        if pattern == "same8":
+            idx[t] = rng.permutation(k)
+        else:
+            idx[t, 0] = E - 1
+            idx[t, 1:] = rng.choice(E - 1, size=k - 1, replace=False)
+    z = rng.standard_normal((M, k))
+    g = np.exp(z - z.max(axis=1, keepdims=True))
+    return idx, g / g.sum(axis=1, keepdims=True)
+
+
+@pytest.mark.parametrize("pattern", ["router", "same8", "hot127"])
+def test_moe_ffn_matches_oracle(torch, c2ctx, pattern):
     from synth import C2
     m = C2.model
-    say("moe_ffn C2 layer 0")
+    say("moe_ffn C2 layer 0, routing", pattern)
     M = C2.batch * m.canvas_len
     f_bits = gen.activations(15, 6, (M, m.hidden), std=1.0, dtype="bf16")
-    r = gen.router_logits(16, M, m.n_experts, 1.0).astype(np.float64)
-    idx, gates = om.route(r, m.top_k)
+    if pattern == "router":
+        r = gen.router_logits(16, M, m.n_experts, 1.0).astype(np.float64)
+        idx, gates = om.route(r, m.top_k)
+    else:
+        idx, gates = _concentrated_routing(M, m.n_experts, m.top_k, pattern)
     out = torch.empty((M, m.hidden), dtype=torch.float32, device="cuda")
     c2ctx.k_moe_ffn(0, C2.batch, upload.to_device(f_bits, "bf16"),
                     torch.from_numpy(idx.astype(np.int32)).cuda(),
@@ -283,7 +306,7 @@ def test_moe_ffn_matches_oracle(torch, c2ctx):
     m_ref, *_ = om.moe_block(om.bf16_bits_to_f64(f_bits), lw, m.top_k, om.bf16_round,
                              route_override=lambda rr, i, g: (idx, g32))
     e = rel_err(host64(out), m_ref)
-    print(f"moe_ffn rel err {e:.3e}")
+    print(f"moe_ffn ({pattern} routing) rel err {e:.3e}")
     assert e <= TOL["bf16"]
 
 
