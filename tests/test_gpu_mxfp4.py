@@ -72,19 +72,26 @@ def test_quantised_experts_match_oracle(torch, dg, w):
         print(f"{w.name}: codes, scales and dequantised values identical to the oracle")
 
 
-def test_moe_ffn_mxfp4(torch, dg):
+# "random": distinct random experts per token; "same2": four canvases whose
+# every token picks experts 3 and 9 (in its own order), so each of the two
+# takes all 128 rows over several work entries and the other 14 stay empty
+@pytest.mark.parametrize("batch,pattern", [(1, "random"), (4, "same2")])
+def test_moe_ffn_mxfp4(torch, dg, batch, pattern):
     w = TINY_Q
     m = w.model
-    M = m.canvas_len
-    rng = np.random.default_rng(3)
+    M = batch * m.canvas_len
+    rng = np.random.default_rng(3 if pattern == "random" else 4)
     f_bits = gen.activations(7, 2, (M, m.hidden), std=1.0, dtype="bf16")
-    idx = np.stack([rng.choice(m.n_experts, m.top_k, replace=False) for _ in range(M)]).astype(np.int32)
+    if pattern == "random":
+        idx = np.stack([rng.choice(m.n_experts, m.top_k, replace=False) for _ in range(M)]).astype(np.int32)
+    else:
+        idx = np.stack([rng.permutation(np.array([3, 9])) for _ in range(M)]).astype(np.int32)
     gates = rng.dirichlet(np.ones(m.top_k), size=M).astype(np.float32)
-    with dg.Context(m, max_batch=1, max_prompt_len=w.prompt_len) as ctx:
+    with dg.Context(m, max_batch=batch, max_prompt_len=w.prompt_len) as ctx:
         upload.load_context(ctx, w, layers=[0, 1])
         out = torch.empty((M, m.hidden), dtype=torch.float32, device="cuda")
-        say("mxfp4 moe")
-        ctx.k_moe_ffn(0, 1, upload.to_device(f_bits, "bf16"), torch.from_numpy(idx).cuda(),
+        say("mxfp4 moe", pattern, "batch", batch)
+        ctx.k_moe_ffn(0, batch, upload.to_device(f_bits, "bf16"), torch.from_numpy(idx).cuda(),
                       torch.from_numpy(gates).cuda(), out)
         torch.cuda.synchronize()
         got = host64(out)
@@ -98,7 +105,7 @@ def test_moe_ffn_mxfp4(torch, dg):
                                                   om.bf16_round)[0]
         ref[t] += om.expert_ffn(f[t:t + 1], lw["sh_gate"], lw["sh_up"], lw["sh_down"], om.bf16_round)[0]
     e = rel_err(got, ref)
-    print(f"mxfp4 routed MoE: rel err {e:.3e}")
+    print(f"mxfp4 routed MoE ({pattern}, {M} rows): rel err {e:.3e}")
     assert e <= TOL["bf16"]
 
 
