@@ -51,13 +51,23 @@ def test_argmax_conf_bit_exact(torch, dg, rows, V):
 
 # ------------------------------------------------------------- lock select --
 
-@pytest.mark.parametrize("B,N,steps", [(4, 256, [1, 2, 5, 12]), (1, 4096, [3]), (2, 16, [7, 1]),
-                                       (64, 32, [4] * 64)])
-def test_lock_select_bit_exact(torch, dg, B, N, steps):
-    say("lock_select", B, N)
+# the last case: canvas 0 already fully locked (nothing to lock, nothing may
+# change), canvas 1 with nothing locked and every confidence equal (the
+# lowest positions win), canvas 2 with one free slot on its last pass
+@pytest.mark.parametrize("B,N,steps,edge", [(4, 256, [1, 2, 5, 12], False), (1, 4096, [3], False),
+                                            (2, 16, [7, 1], False), (64, 32, [4] * 64, False),
+                                            (3, 256, [2, 2, 1], True)])
+def test_lock_select_bit_exact(torch, dg, B, N, steps, edge):
+    say("lock_select", B, N, "edge" if edge else "")
     rng = np.random.default_rng([41, B, N])
     conf = (rng.integers(0, 40, size=(B, N)) / 40.0).astype(np.float32)  # many exact ties
     locked = (rng.random((B, N)) < 0.3).astype(np.uint8)
+    if edge:
+        locked[0] = 1
+        locked[1] = 0
+        conf[1] = 0.5
+        locked[2] = 1
+        locked[2, 77] = 0
     tokens = rng.integers(0, 1000, size=(B, N)).astype(np.int32)
     pred = rng.integers(1000, 2000, size=(B, N)).astype(np.int32)
     t_ref, l_ref, _ = om.lock_select(conf.astype(np.float64), pred, tokens, locked, steps)
@@ -66,6 +76,10 @@ def test_lock_select_bit_exact(torch, dg, B, N, steps):
     torch.cuda.synchronize()
     assert np.array_equal(tt.cpu().numpy(), t_ref)
     assert np.array_equal(lt.cpu().numpy(), l_ref)
+    if edge:
+        assert np.array_equal(t_ref[0], tokens[0])  # a full canvas is left alone
+        assert np.array_equal(np.nonzero(l_ref[1])[0], np.arange(128))  # ceil(256 / 2), lowest first
+        assert l_ref[2].all() and t_ref[2, 77] == pred[2, 77]
 
 
 # ----------------------------------------------------------------- routing --
