@@ -388,7 +388,7 @@ def main():
         summarize_counters(*args.summarize_counters, args.copy_mib)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the library has no "
               "multi-GPU path: independent canvases shard with no exchange, see the design notes.",
               file=sys.stderr)
         sys.exit(2)

@@ -65,7 +65,7 @@ typedef enum dg_status {
   DG_ENOMEM = -2,       /* device allocation failed */
   DG_EHIP = -3,         /* HIP runtime error */
   DG_ESTATE = -4,       /* call not valid in the context's state */
-  DG_EUNSUPPORTED = -5  /* shape or dtype this build does not handle */
+  DG_EUNSUPPORTED = -5  /* shape or dtype the library does not handle */
 } dg_status;
 
 typedef enum dg_dtype { DG_F32 = 0, DG_BF16 = 1 } dg_dtype;
